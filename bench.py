@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 NVFP4 block-scaled GEMM, C = alpha * (A . B^T).
+
+One "step" is one call of the whole path, nvfp4_gemm, on packed operands
+already resident in HBM (decode, MFMA contraction, split-K reduction where the
+plan uses it, alpha and bf16 epilogue).  Timing follows the protocol of
+"Peeling the Kernel Onion", section "The Benchmark Design" (warm-up calls,
+then timed calls bracketed by device synchronisation), with HIP events
+recorded on the stream the kernels are launched on.
+
+The headline line is the decode attention projection, M=1, N=768, K=6144,
+alpha=0.5 (the pages' batch-1 point, 0.30 TFLOPS on their GPU); the other
+workloads are reported under "per_shape".  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HEADLINE = 2            # decode attention projection 1 x 768 x 6144
+PAGES_TFLOPS = {2: 0.30, 3: 161.0, 4: 437.0}  # same shapes, measured on the pages' GPU
+# MI355X published peaks
+HBM_GBPS = 8000.0
+MFMA_F16_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=HEADLINE, help="1..5")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="skip the per-shape lines for the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time with operand copies rotated beyond the last-level cache")
+    return ap.parse_args()
+
+
+def roofline_for(cfg, seconds_per_call):
+    b = synth.algorithmic_bytes(cfg.M, cfg.N, cfg.K)
+    f = synth.flops(cfg.M, cfg.N, cfg.K)
+    ai = f / b
+    ridge = MFMA_F16_TFLOPS * 1e12 / (HBM_GBPS * 1e9)
+    if ai < ridge:
+        ach = b / seconds_per_call / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
+                "frac": ach / HBM_GBPS, "traffic": None,
+                "algorithmic_bytes_per_launch": b}
+    ach = f / seconds_per_call / 1e12
+    return {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / MFMA_F16_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": f}
+
+
+def time_workload(nv, torch, cfg, steps, warmup, cold=False):
+    ops = synth.make_inputs(cfg)
+    a = nv.to_device(ops.a_codes, ops.a_scales, "cuda")
+    b = nv.to_device(ops.b_codes, ops.b_scales, "cuda")
+    out = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
+    sets = [(a, b, out)]
+    if cold:
+        # distinct operand copies whose total exceeds the 256 MB last-level cache twice
+        per = a.codes.numel() + a.scales.numel() + b.codes.numel() + b.scales.numel()
+        n = max(2, min(4096, int(2 * 256e6 // per) + 1))
+        sets = []
+        for _ in range(n):
+            sets.append((nv.PackedOperand(a.codes.clone(), a.scales.clone(), a.rows, a.K),
+                         nv.PackedOperand(b.codes.clone(), b.scales.clone(), b.rows, b.K),
+                         torch.empty_like(out)))
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        x, y, o = sets[i % len(sets)]
+        nv.gemm(x, y, cfg.alpha, out=o, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        x, y, o = sets[i % len(sets)]
+        nv.gemm(x, y, cfg.alpha, out=o, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    plan = nv.plan(cfg.M, cfg.N, cfg.K)
+    del sets
+    return ms, wall, plan, ops
+
+
+def cpu_baseline(cfg, ops, budget_s):
+    from oracle import oracle as orc
+    o = orc.load()
+    # one call first to size the sample
+    t0 = time.perf_counter()
+    o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, cfg.alpha, want_exact=False)
+    one = time.perf_counter() - t0
+    reps = max(1, int(budget_s / max(one, 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, cfg.alpha, want_exact=False)
+    el = time.perf_counter() - t0
+    tflops = synth.flops(cfg.M, cfg.N, cfg.K) * reps / el / 1e12
+    return {"value": tflops, "unit": "TFLOPS", "cores": o.threads, "kind": "oracle",
+            "sample": f"the full {cfg.M}x{cfg.N}x{cfg.K} GEMM repeated {reps} times "
+                      f"({el:.1f} s, fp64 C oracle, OpenMP over rows)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM's "
+              "multi-GPU sharding is described in the design notes but not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_scaled_fp4_04_amd as nv
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    nv.init(torch.cuda.current_device())
+
+    cfg = synth.config(args.workload)
+    ms, wall, plan, ops = time_workload(nv, torch, cfg, args.steps, args.warmup)
+    tflops = synth.flops(cfg.M, cfg.N, cfg.K) / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "NVFP4 GEMM TFLOPS (2MNK/s) per shape + % of HBM/MFMA roofline, 1 MI355X",
+        "value": tflops, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (tflops / PAGES_TFLOPS[cfg.index]) if PAGES_TFLOPS.get(cfg.index) else None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} M={cfg.M} N={cfg.N} K={cfg.K} alpha={cfg.alpha}",
+                   "M": cfg.M, "N": cfg.N, "K": cfg.K, "alpha": cfg.alpha,
+                   "path": "skinny" if plan["path"] == nv.PATH_SKINNY else "tile",
+                   "split_k": plan["split_k"], "tile": [plan["tile_m"], plan["tile_n"]],
+                   "operands": "E2M1 codes + E4M3 per-16 scales (packed), bf16 out, "
+                               "fp16 MFMA with fp32 accumulation",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline_for(cfg, ms * 1e-3),
+        "wall_s_timed_region": wall,
+    }
+    if args.cold:
+        cms, _, _, _ = time_workload(nv, torch, cfg, args.steps, args.warmup, cold=True)
+        line["cold"] = {"ms_per_step": cms,
+                        "tflops": synth.flops(cfg.M, cfg.N, cfg.K) / (cms * 1e-3) / 1e12,
+                        "roofline": roofline_for(cfg, cms * 1e-3)}
+    if not args.only_headline:
+        per = {}
+        for c in synth.CONFIGS:
+            if c.index == cfg.index:
+                continue
+            cms, _, cplan, _ = time_workload(nv, torch, c, args.steps, args.warmup)
+            ctf = synth.flops(c.M, c.N, c.K) / (cms * 1e-3) / 1e12
+            per[c.name] = {"M": c.M, "N": c.N, "K": c.K, "ms": cms, "tflops": ctf,
+                           "roofline": roofline_for(c, cms * 1e-3),
+                           "path": "skinny" if cplan["path"] == nv.PATH_SKINNY else "tile",
+                           "split_k": cplan["split_k"],
+                           "pages_tflops_other_gpu": PAGES_TFLOPS.get(c.index)}
+        line["per_shape"] = per
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, ops, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+"""Python binding of the gfx950 NVFP4 block-scaled GEMM library (libnvfp4.so).
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels
+behind the C ABI of ``include/nvfp4.h``; PyTorch supplies device memory and
+the current stream.  There is no fallback: if the library is missing, every
+call raises.
+
+    C = alpha * (A . B^T)
+A is M x K and B is N x K, both E2M1 codes packed two per byte with one
+E4M3 scale per 16 elements, alpha is FP32 and C is bfloat16 M x N ("Peeling
+the Kernel Onion", sections "The Benchmark Design" and "The Chain of
+Reasoning").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+OK = 0
+ERR_INVALID_VALUE = 1
+ERR_MISALIGNED = 2
+ERR_UNSUPPORTED = 3
+ERR_HIP = 4
+ERR_ALLOC = 5
+
+PATH_AUTO = 0
+PATH_TILE = 1
+PATH_SKINNY = 2
+
+EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_pack",
+           "nvfp4_unpack", "nvfp4_init", "nvfp4_shutdown", "nvfp4_gemm",
+           "nvfp4_gemm_with_path", "nvfp4_plan"]
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_lib: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -m block_scaled_fp4_04_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        L.nvfp4_status_string.argtypes = [ctypes.c_int]
+        L.nvfp4_version.restype = ctypes.c_int
+        L.nvfp4_packed_size.restype = ctypes.c_int
+        L.nvfp4_packed_size.argtypes = [_i64, _i64, ctypes.POINTER(ctypes.c_size_t),
+                                        ctypes.POINTER(ctypes.c_size_t)]
+        L.nvfp4_pack.restype = ctypes.c_int
+        L.nvfp4_pack.argtypes = [_u8p, _u8p, _i64, _i64, _u8p, _u8p]
+        L.nvfp4_unpack.restype = ctypes.c_int
+        L.nvfp4_unpack.argtypes = [_u8p, _u8p, _i64, _i64, _u8p, _u8p]
+        L.nvfp4_init.restype = ctypes.c_int
+        L.nvfp4_init.argtypes = [ctypes.c_int]
+        L.nvfp4_shutdown.restype = None
+        L.nvfp4_gemm.restype = ctypes.c_int
+        L.nvfp4_gemm.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i64, _vp]
+        L.nvfp4_gemm_with_path.restype = ctypes.c_int
+        L.nvfp4_gemm_with_path.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
+                                           _i64, ctypes.c_int, ctypes.c_int, _vp]
+        ip = ctypes.POINTER(ctypes.c_int)
+        L.nvfp4_plan.restype = ctypes.c_int
+        L.nvfp4_plan.argtypes = [_i64, _i64, _i64, ip, ip, ip, ip]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().nvfp4_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().nvfp4_version())
+
+
+def packed_size(rows: int, K: int) -> tuple[int, int]:
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    st = lib().nvfp4_packed_size(rows, K, ctypes.byref(cb), ctypes.byref(sb))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_packed_size(rows={rows}, K={K})")
+    return cb.value, sb.value
+
+
+def _check_canonical(codes: np.ndarray, scales: np.ndarray) -> tuple[int, int]:
+    if codes.dtype != np.uint8 or scales.dtype != np.uint8 or codes.ndim != 2 or scales.ndim != 2:
+        raise ValueError("codes and scales must be 2-D uint8 arrays")
+    rows, kh = codes.shape
+    K = 2 * kh
+    if scales.shape != (rows, K // 16) or K % 16:
+        raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape} "
+                         "(one scale per 16 elements, K % 16 == 0)")
+    return rows, K
+
+
+def pack(codes: np.ndarray, scales: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Canonical host arrays -> packed host arrays (nvfp4_pack)."""
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    rows, K = _check_canonical(codes, scales)
+    cb, sb = packed_size(rows, K)
+    pc = np.empty(cb, np.uint8)
+    ps = np.empty(sb, np.uint8)
+    st = lib().nvfp4_pack(codes.ctypes.data_as(_u8p), scales.ctypes.data_as(_u8p), rows, K,
+                          pc.ctypes.data_as(_u8p), ps.ctypes.data_as(_u8p))
+    if st:
+        raise Nvfp4Error(st, "nvfp4_pack")
+    return pc, ps
+
+
+def unpack(packed_codes: np.ndarray, packed_scales: np.ndarray, rows: int, K: int):
+    """Packed host arrays -> canonical (codes [rows, K/2], scales [rows, K/16])."""
+    packed_codes = np.ascontiguousarray(packed_codes, dtype=np.uint8)
+    packed_scales = np.ascontiguousarray(packed_scales, dtype=np.uint8)
+    cb, sb = packed_size(rows, K)
+    if packed_codes.size != cb or packed_scales.size != sb:
+        raise ValueError("packed buffers have the wrong size")
+    codes = np.empty((rows, K // 2), np.uint8)
+    scales = np.empty((rows, K // 16), np.uint8)
+    st = lib().nvfp4_unpack(packed_codes.ctypes.data_as(_u8p), packed_scales.ctypes.data_as(_u8p),
+                            rows, K, codes.ctypes.data_as(_u8p), scales.ctypes.data_as(_u8p))
+    if st:
+        raise Nvfp4Error(st, "nvfp4_unpack")
+    return codes, scales
+
+
+def plan(M: int, N: int, K: int) -> dict:
+    p, s, tm, tn = (ctypes.c_int() for _ in range(4))
+    st = lib().nvfp4_plan(M, N, K, ctypes.byref(p), ctypes.byref(s), ctypes.byref(tm),
+                          ctypes.byref(tn))
+    if st:
+        raise Nvfp4Error(st, "nvfp4_plan")
+    return {"path": p.value, "split_k": s.value, "tile_m": tm.value, "tile_n": tn.value}
+
+
+def init(device: int = 0) -> None:
+    st = lib().nvfp4_init(device)
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_init({device})")
+
+
+def shutdown() -> None:
+    lib().nvfp4_shutdown()
+
+
+@dataclass
+class PackedOperand:
+    """One GEMM operand in the packed layout, resident on a device.
+    ``codes``/``scales`` are uint8 torch tensors; ``rows`` x ``K`` is the
+    logical shape."""
+    codes: "object"
+    scales: "object"
+    rows: int
+    K: int
+
+
+def to_device(codes: np.ndarray, scales: np.ndarray, device="cuda") -> PackedOperand:
+    """Pack canonical host arrays and copy them to ``device``."""
+    import torch
+    rows, K = _check_canonical(codes, scales)
+    pc, ps = pack(codes, scales)
+    return PackedOperand(torch.from_numpy(pc).to(device), torch.from_numpy(ps).to(device), rows, K)
+
+
+def _stream_handle(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def gemm(a: PackedOperand, b: PackedOperand, alpha: float = 1.0, out=None,
+         path: int = PATH_AUTO, split_k: int = 0, stream=None):
+    """C = alpha * (A . B^T) as an M x N bfloat16 tensor on A's device.
+    Raises ValueError when A and B do not share K (a mismatch is an error,
+    not a silent result)."""
+    import torch
+    if a.K != b.K:
+        raise ValueError(f"K dimension mismatch: A has K={a.K}, B has K={b.K}")
+    M, N, K = a.rows, b.rows, a.K
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
+    for name, t, need in (("a.codes", a.codes, packed_size(M, K)[0]),
+                          ("a.scales", a.scales, packed_size(M, K)[1]),
+                          ("b.codes", b.codes, packed_size(N, K)[0]),
+                          ("b.scales", b.scales, packed_size(N, K)[1])):
+        if t.dtype != torch.uint8 or t.numel() != need or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 tensor of {need} bytes")
+    st = lib().nvfp4_gemm_with_path(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+                                    b.scales.data_ptr(), float(alpha), out.data_ptr(), M, N, K,
+                                    int(path), int(split_k), _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_gemm(M={M}, N={N}, K={K})")
+    return out
+
+
+def gemm_raw(a_codes: int, a_scales: int, b_codes: int, b_scales: int, alpha: float, out: int,
+             M: int, N: int, K: int, stream: int | None = None) -> int:
+    """Direct call of nvfp4_gemm with raw device addresses; returns the status."""
+    return int(lib().nvfp4_gemm(a_codes, a_scales, b_codes, b_scales, float(alpha), out, M, N, K,
+                                stream))

@@ -1,0 +1,58 @@
+// nvfp4_internal.h -- launch arguments shared by the host library and the
+// gfx950 kernels of the NVFP4 block-scaled GEMM (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Packed operand geometry (see include/nvfp4.h, "Packed layout").
+constexpr int kPanelK = 64;        // elements per panel
+constexpr int kPanelCodeBytes = 32;  // bytes of codes per row per panel
+constexpr int kPanelScaleBytes = 4;  // scale bytes per row per panel
+constexpr int kRowPad = 16;
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct GemmArgs {
+    const uint8_t* a_codes;   // [P][Mp][32]
+    const uint8_t* a_scales;  // [P][Mp][4]
+    const uint8_t* b_codes;   // [P][Np][32]
+    const uint8_t* b_scales;  // [P][Np][4]
+    uint16_t* out;            // [M][N] bfloat16 bits
+    float* partials;          // split-K partial sums (workspace), or null
+    uint32_t* counters;       // split-K arrival counters (workspace), or null
+    float alpha;
+    int M, N;                 // logical output size
+    int Mp, Np;               // padded row counts of the packed operands
+    int P;                    // number of 64-element K panels
+    int split_k;              // number of K slices (>= 1)
+    int tiles_m, tiles_n;     // output tiles along M and N (tile kernel)
+};
+
+// Tile configurations of the large-M kernel.
+enum TileConfig { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x64 = 2 };
+
+struct TileShape { int bm, bn; };
+inline TileShape tile_shape(int cfg) {
+    switch (cfg) {
+        case TILE_256x256: return {256, 256};
+        case TILE_128x128: return {128, 128};
+        default: return {64, 64};
+    }
+}
+
+// Number of 128-element K steps (two panels each) of the tile kernel and of
+// the skinny kernel.
+inline int k_steps(int P) { return (P + 1) / 2; }
+
+// Workspace needs (bytes of partials, number of counters) of a launch.
+size_t tile_partial_floats(int cfg, const GemmArgs& a);
+size_t tile_counters(int cfg, const GemmArgs& a);
+size_t skinny_partial_floats(const GemmArgs& a);
+size_t skinny_counters(const GemmArgs& a);
+
+hipError_t launch_tile(int cfg, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace nvfp4

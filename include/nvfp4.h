@@ -1,0 +1,135 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled GEMM library.
+ *
+ * The operation is C = alpha * (A . B^T):
+ *   - A is M x K and B is N x K, both held as FP4 E2M1 codes packed two per
+ *     byte, with one FP8 E4M3 scale per 16-element block along K ("Peeling
+ *     the Kernel Onion", section "The Benchmark Design": packed uint8 data,
+ *     FP8 scale factors, one per 16 elements; "The SM120 FP4 Kernel
+ *     Disaster", section "Input Knowledge Required", item 3);
+ *   - alpha is an FP32 scalar and C is a caller-provided M x N bfloat16
+ *     output ("Peeling the Kernel Onion", section "The Chain of Reasoning":
+ *     the GEMM takes alpha and an output tensor);
+ *   - K must be a positive multiple of the 16-element block size (and so of
+ *     the packing factor 2): "The SM120 FP4 Kernel Disaster", section "The
+ *     Bash Command".
+ *
+ * Element formats (OCP Microscaling Formats v1.0): E2M1 codes are
+ * sign(bit 3) | exponent(bits 2:1, bias 1) | mantissa(bit 0), values
+ * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}; E4M3 scales are the "FN" variant (bias 7,
+ * subnormals, 0x7F/0xFF NaN, no infinity, max 448).
+ *
+ * Canonical layout (what callers produce; row-major, K contiguous):
+ *   codes  [rows][K/2]  byte j of a row holds element 2j in bits 3:0 and
+ *                       element 2j+1 in bits 7:4;
+ *   scales [rows][K/16] byte b scales elements 16b .. 16b+15.
+ * Packed layout (what nvfp4_gemm consumes; produced by nvfp4_pack): rows are
+ * padded to Rp = roundup(rows, 16) and K to Kp = roundup(K, 64) with zero
+ * codes and zero scales; the data is split into Kp/64 panels of 64 elements:
+ *   packed codes  [Kp/64][Rp][32]  (32 bytes = 64 codes of one row, same
+ *                                   byte/nibble order as canonical)
+ *   packed scales [Kp/64][Rp][4]   (the row's four scale bytes of the panel)
+ * Padding contributes exact zeros, so results are unaffected.
+ *
+ * Status codes: every entry point returns an nvfp4_status (0 = success) and
+ * never aborts, throws or prints.  Argument errors are detected on the host
+ * before any device work is enqueued.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_ERR_INVALID_VALUE = 1, /* bad size, null pointer, K % 16 != 0, ... */
+    NVFP4_ERR_MISALIGNED = 2,    /* a device pointer is not 16-byte aligned */
+    NVFP4_ERR_UNSUPPORTED = 3,   /* no gfx950 device / forced path cannot run */
+    NVFP4_ERR_HIP = 4,           /* a HIP runtime call failed */
+    NVFP4_ERR_ALLOC = 5          /* workspace allocation failed */
+} nvfp4_status;
+
+/* Kernel paths for nvfp4_gemm_with_path. */
+enum {
+    NVFP4_PATH_AUTO = 0,   /* library's choice from M, N, K */
+    NVFP4_PATH_TILE = 1,   /* large-M MFMA tile kernel (LDS double buffer) */
+    NVFP4_PATH_SKINNY = 2  /* M <= 16: split-K MFMA kernel for decode shapes */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* nvfp4_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int nvfp4_version(void);
+
+/* Byte sizes of the packed code and scale buffers for an operand of `rows`
+ * rows and K elements per row (see "Packed layout" above).
+ * rows >= 1, K >= 16, K % 16 == 0, else NVFP4_ERR_INVALID_VALUE.  Output
+ * pointers must be non-null. */
+int nvfp4_packed_size(int64_t rows, int64_t K, size_t* code_bytes, size_t* scale_bytes);
+
+/* Host-side layout transform, canonical -> packed (a pure byte permutation
+ * plus zero padding; no arithmetic).  All pointers are HOST memory owned by
+ * the caller; packed buffers must hold nvfp4_packed_size() bytes.  Used for
+ * both A (rows = M) and B (rows = N).  Same size rules as nvfp4_packed_size. */
+int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+               uint8_t* packed_codes, uint8_t* packed_scales);
+
+/* Inverse of nvfp4_pack (drops the padding). HOST memory, caller-owned. */
+int nvfp4_unpack(const uint8_t* packed_codes, const uint8_t* packed_scales, int64_t rows,
+                 int64_t K, uint8_t* codes, uint8_t* scales);
+
+/* Optional set-up for `device`: checks that it is a gfx950 GPU and creates
+ * the split-K workspace of the calling stream lazily afterwards.  nvfp4_gemm
+ * calls it implicitly for the current device.  Returns NVFP4_ERR_UNSUPPORTED
+ * for a non-gfx950 device, NVFP4_ERR_HIP if the device cannot be queried. */
+int nvfp4_init(int device);
+
+/* Frees every workspace the library allocated.  The caller must make sure no
+ * nvfp4 kernel is still running; later calls re-create what they need. */
+void nvfp4_shutdown(void);
+
+/* C = alpha * (A . B^T), bfloat16 output, round-to-nearest-even.
+ *   a_packed, a_scales : DEVICE pointers, A packed by nvfp4_pack (rows = M)
+ *   b_packed, b_scales : DEVICE pointers, B packed by nvfp4_pack (rows = N)
+ *   alpha              : FP32 scale applied once to the FP32 accumulator
+ *   out                : DEVICE pointer, M x N bfloat16, row-major (ld = N);
+ *                        overwritten (no beta); must not alias the inputs
+ *   M, N, K            : logical sizes (M, N >= 1; K >= 16, K % 16 == 0)
+ *   stream             : hipStream_t to enqueue on (NULL = default stream)
+ * All device buffers are caller-owned and must be 16-byte aligned (else
+ * NVFP4_ERR_MISALIGNED).  The call is asynchronous: it returns after the
+ * kernels are enqueued; device-side faults surface at the caller's next
+ * synchronisation.  Split-K paths use a library-owned workspace per
+ * (device, stream) pair, allocated on the first call that needs it (the
+ * only allocation the library makes); calls on one stream are ordered, calls
+ * on different streams use different workspaces.  Launch failures return
+ * NVFP4_ERR_HIP. */
+int nvfp4_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
+               const void* b_scales, float alpha, void* out, int64_t M, int64_t N, int64_t K,
+               void* stream);
+
+/* nvfp4_gemm with an explicit kernel path (NVFP4_PATH_*) and split-K factor
+ * (0 = library's choice, else the number of K slices, clamped to the number
+ * of K steps).  Same contract as nvfp4_gemm; NVFP4_ERR_UNSUPPORTED if the
+ * forced path cannot run the shape (skinny needs M <= 16). */
+int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void* b_packed,
+                         const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
+                         int64_t K, int path, int split_k, void* stream);
+
+/* The path (NVFP4_PATH_TILE / NVFP4_PATH_SKINNY) and split-K factor that
+ * nvfp4_gemm would use for a shape; also the tile sizes.  Any output pointer
+ * may be NULL.  Host-only, no device work. */
+int nvfp4_plan(int64_t M, int64_t N, int64_t K, int* path, int* split_k, int* tile_m,
+               int* tile_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -20,6 +20,7 @@ saturates to +-6; the code keeps the sign of x.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -56,11 +57,33 @@ def e4m3_value(byte: np.ndarray) -> np.ndarray:
     return _E4M3_POS[np.asarray(byte, dtype=np.int64)]
 
 
-def quantize_nvfp4(x: np.ndarray):
-    """fp32 [rows, K] -> (codes uint8 [rows, K/2], scales uint8 [rows, K/16])."""
+def quantize_nvfp4(x: np.ndarray, workers: int | None = None):
+    """fp32 [rows, K] -> (codes uint8 [rows, K/2], scales uint8 [rows, K/16]).
+    Large inputs are processed in row chunks on a thread pool (the result
+    does not depend on the chunking)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     rows, K = x.shape
     assert K % 16 == 0
+    chunk = max(1, (1 << 22) // K)
+    if rows <= chunk:
+        return _quantize_rows(x)
+    from concurrent.futures import ThreadPoolExecutor
+    codes = np.empty((rows, K // 2), np.uint8)
+    scales = np.empty((rows, K // 16), np.uint8)
+
+    def work(r0):
+        c, s = _quantize_rows(x[r0:r0 + chunk])
+        codes[r0:r0 + chunk] = c
+        scales[r0:r0 + chunk] = s
+
+    n = workers or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(work, range(0, rows, chunk)))
+    return codes, scales
+
+
+def _quantize_rows(x: np.ndarray):
+    rows, K = x.shape
     blocks = x.reshape(rows, K // 16, 16)
     amax = np.max(np.abs(blocks), axis=2)
     scale_f32 = (amax / np.float32(6.0)).astype(np.float32)

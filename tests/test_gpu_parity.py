@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every comparison is element by element on the same seeded inputs.  The
+bound is |gpu - oracle| <= 1 bf16 ulp + 1e-5 * |alpha| * sum_k |a'_k b'_k|;
+because the kernels decode exactly and accumulate exact products in FP32,
+the results are also expected to be bit-identical to the oracle on (almost)
+every element, and the tests report that fraction.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import oracle as orc
+from parity import compare
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_04_amd as nv  # noqa: E402
+
+DEV = "cuda"
+
+
+def say(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return orc.load()
+
+
+def run_gpu(ops: synth.Operands, path=nv.PATH_AUTO, split_k=0, stream=None, label=""):
+    say(f"{label} M={ops.M} N={ops.N} K={ops.K} alpha={ops.alpha} path={path} split_k={split_k}")
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    out = nv.gemm(a, b, ops.alpha, path=path, split_k=split_k, stream=stream)
+    torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy().astype(np.uint16)
+
+
+def check_full(o, ops, gpu_bits, label, min_exact=0.999):
+    bits, exact, mag = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha)
+    r = compare(gpu_bits, bits, exact, mag, ops.alpha)
+    say(f"{label}: {r}")
+    assert r["over"] == 0, r
+    assert r["bit_exact_frac"] >= min_exact, r
+    return r
+
+
+# ------------------------------------------------------------ decode and layout
+
+@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_SKINNY])
+def test_decode_exhaustive(o, path):
+    """Every E4M3 scale byte times every E2M1 code, through the GEMM: one
+    operand has a single 1.0 at k=0 with scale s in row s, the other has code
+    c at k=0 with scale 1.0 in row c, so C holds every product exactly."""
+    K = 64
+    sc_rows = np.zeros((256, K // 2), np.uint8)
+    sc_rows[:, 0] = 0x02                                   # code 1.0 at k = 0
+    sc_scales = np.full((256, K // 16), 0x38, np.uint8)
+    sc_scales[:, 0] = np.arange(256, dtype=np.uint8)       # scale byte s in row s
+    cd_rows = np.zeros((16, K // 2), np.uint8)
+    cd_rows[:, 0] = np.arange(16, dtype=np.uint8)          # code c at k = 0 in row c
+    cd_scales = np.full((16, K // 16), 0x38, np.uint8)
+    if path == nv.PATH_TILE:
+        ops = synth.Operands(sc_rows, sc_scales, cd_rows, cd_scales, 1.0, 256, 16, K)
+    else:   # skinny: M <= 16, so the code rows are A
+        ops = synth.Operands(cd_rows, cd_scales, sc_rows, sc_scales, 1.0, 16, 256, K)
+    g = run_gpu(ops, path=path, label="decode")
+    bits, exact, mag = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, 1.0)
+    nan_o = ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
+    nan_g = ((g & 0x7F80) == 0x7F80) & ((g & 0x7F) != 0)
+    assert np.array_equal(nan_o, nan_g)
+    ok = ~nan_o
+    same = (g[ok] == bits[ok]) | (((g[ok] & 0x7FFF) == 0) & ((bits[ok] & 0x7FFF) == 0))
+    assert np.all(same), np.argwhere(~same)[:10]
+
+
+@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_SKINNY])
+def test_onehot_positions(o, path):
+    """One non-zero product at a time, at positions across tile, panel and
+    scale-block boundaries: pins nibble order, K slots, scale blocks, the
+    packer and the MFMA operand/result layouts."""
+    M = 16 if path == nv.PATH_SKINNY else 300
+    N, K = 290, 320
+    g = np.random.Generator(np.random.PCG64(77))
+    for t in range(6):
+        m, n, k = int(g.integers(M)), int(g.integers(N)), int(g.integers(K))
+        if t == 0:
+            m, n, k = M - 1, N - 1, K - 1
+        ac = np.zeros((M, K // 2), np.uint8)
+        bc = np.zeros((N, K // 2), np.uint8)
+        ac[m, k // 2] = 0x5 << (4 * (k % 2))          # 3.0
+        bc[n, k // 2] = 0xB << (4 * (k % 2))          # -1.5
+        as_ = np.full((M, K // 16), 0x38, np.uint8)
+        bs = np.full((N, K // 16), 0x38, np.uint8)
+        as_[m, k // 16] = 0x3B                        # 1.375
+        bs[n, k // 16] = 0x06                         # subnormal 6 * 2^-9
+        ops = synth.Operands(ac, as_, bc, bs, 1.0, M, N, K)
+        gb = run_gpu(ops, path=path, label=f"onehot m={m} n={n} k={k}")
+        want = np.zeros((M, N), np.uint16)
+        bits, _, _ = o.gemm(ac, as_, bc, bs, 1.0)
+        assert bits[m, n] != 0 and int(np.count_nonzero(bits & 0x7FFF)) == 1
+        nz = np.argwhere(gb & 0x7FFF)
+        assert nz.tolist() == [[m, n]], (m, n, k, nz[:5])
+        assert gb[m, n] == bits[m, n]
+        del want
+
+
+# ------------------------------------------------------------ the workloads
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_parity_workload(o, i):
+    cfg = synth.config(i)
+    ops = synth.make_inputs(cfg)
+    g = run_gpu(ops, label=f"workload {i} {cfg.name}")
+    r = check_full(o, ops, g, f"workload {i}")
+    assert not r["all_zero"]
+
+
+def test_parity_saturation_sampled(o):
+    """16384 x 8192 x 8192 in the launch configuration the benchmark times;
+    checked at sampled elements (full rows, full columns and random ones)."""
+    cfg = synth.config(5)
+    ops = synth.make_inputs(cfg)
+    g = run_gpu(ops, label="workload 5 saturation")
+    rng = np.random.Generator(np.random.PCG64(5))
+    rows = [0, 255, 256, cfg.M - 1]
+    cols = [0, 255, 256, cfg.N - 1]
+    ms = np.concatenate([np.repeat(rows, 512), np.tile(rng.integers(0, cfg.M, 512), 1)])
+    ns = np.concatenate([np.tile(rng.integers(0, cfg.N, 512), len(rows)),
+                         rng.integers(0, cfg.N, 512)])
+    ms = np.concatenate([ms, rng.integers(0, cfg.M, 512)])
+    ns = np.concatenate([ns, np.repeat(cols, 128)])
+    pb, pe, pm = o.gemm_points(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha,
+                               ms, ns)
+    r = compare(g[ms, ns], pb, pe, pm, ops.alpha)
+    say(f"workload 5 sampled: {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
+    # property at every element: finite, and not all zero
+    gf = orc.bf16_bits_to_float(g)
+    assert np.all(np.isfinite(gf)) and np.count_nonzero(g & 0x7FFF) > 0.99 * g.size
+
+
+# ------------------------------------------------------------ edges
+
+EDGE_SHAPES = [(1, 1, 16), (1, 17, 32), (2, 33, 48), (15, 16, 80), (16, 255, 6160),
+               (17, 16, 16), (63, 65, 208), (64, 64, 64), (65, 31, 128), (257, 130, 336),
+               (300, 513, 1040)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
+def test_edge_shapes(o, M, N, K):
+    ops = synth.random_operands(1000 * M + N + K, M, N, K, alpha=0.75)
+    paths = [nv.PATH_AUTO, nv.PATH_TILE] + ([nv.PATH_SKINNY] if M <= 16 else [])
+    for path in paths:
+        g = run_gpu(ops, path=path, label="edge")
+        check_full(o, ops, g, f"edge {M}x{N}x{K} path {path}")
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 5, 16])
+def test_split_k_variants(o, split_k):
+    ops = synth.quantized_operands(91, 200, 160, 2048, alpha=1.25)
+    g = run_gpu(ops, path=nv.PATH_TILE, split_k=split_k, label="split-k tile")
+    check_full(o, ops, g, f"tile split {split_k}")
+    ops16 = synth.quantized_operands(92, 9, 300, 2048, alpha=-0.5)
+    g = run_gpu(ops16, path=nv.PATH_SKINNY, split_k=split_k, label="split-k skinny")
+    check_full(o, ops16, g, f"skinny split {split_k}")
+
+
+def test_wide_scale_range(o):
+    """Scale bytes across the whole finite range (negative, subnormal, 448)."""
+    g0 = np.random.Generator(np.random.PCG64(123))
+    M, N, K = 96, 80, 256
+    fin = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    ops = synth.Operands(g0.integers(0, 256, (M, K // 2), dtype=np.uint8),
+                         g0.choice(fin, (M, K // 16)).astype(np.uint8),
+                         g0.integers(0, 256, (N, K // 2), dtype=np.uint8),
+                         g0.choice(fin, (N, K // 16)).astype(np.uint8), 1.0, M, N, K)
+    for path in (nv.PATH_TILE,):
+        g = run_gpu(ops, path=path, label="wide scales")
+        check_full(o, ops, g, "wide scales", min_exact=0.99)
+
+
+# ------------------------------------------------------------ properties
+
+def test_determinism_and_symmetry(o):
+    ops = synth.quantized_operands(5, 64, 96, 1024)
+    g1 = run_gpu(ops, split_k=4, path=nv.PATH_TILE, label="determinism 1")
+    g2 = run_gpu(ops, split_k=4, path=nv.PATH_TILE, label="determinism 2")
+    assert np.array_equal(g1, g2)
+    t = synth.Operands(ops.b_codes, ops.b_scales, ops.a_codes, ops.a_scales, 1.0, 96, 64, 1024)
+    gt = run_gpu(t, path=nv.PATH_TILE, label="transpose")
+    assert np.array_equal(gt, g1.T)
+    s1 = synth.make_inputs(synth.config(1))
+    a1 = run_gpu(s1, label="determinism skinny 1")
+    a2 = run_gpu(s1, label="determinism skinny 2")
+    assert np.array_equal(a1, a2)
+
+
+def test_out_guard_and_stream(o):
+    """The kernels write exactly M x N elements (guard words around the
+    output stay intact) and run on a caller's stream."""
+    ops = synth.random_operands(8, 33, 70, 192)
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    for path in (nv.PATH_TILE, nv.PATH_SKINNY) if ops.M <= 16 else (nv.PATH_TILE,):
+        say(f"guard path={path}")
+        buf = torch.full((33 * 70 + 2 * 64,), -12345, dtype=torch.int16, device=DEV)
+        out = buf[64:64 + 33 * 70].view(torch.bfloat16).view(33, 70)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            nv.gemm(a, b, 1.0, out=out, path=path, stream=s)
+        s.synchronize()
+        host = buf.cpu().numpy()
+        assert np.all(host[:64] == -12345) and np.all(host[64 + 33 * 70:] == -12345)
+        g = host[64:64 + 33 * 70].astype(np.uint16).reshape(33, 70)
+        check_full(o, ops, g, "guard")
