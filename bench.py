@@ -65,40 +65,71 @@ def roofline_for(cfg, seconds_per_call):
             "frac": ach / MFMA_F16_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": f}
 
 
-def time_workload(nv, torch, cfg, steps, warmup, cold=False):
-    ops = synth.make_inputs(cfg)
+def _operand_sets(nv, torch, cfg, ops, cold):
     a = nv.to_device(ops.a_codes, ops.a_scales, "cuda")
     b = nv.to_device(ops.b_codes, ops.b_scales, "cuda")
     out = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
-    sets = [(a, b, out)]
-    if cold:
-        # distinct operand copies whose total exceeds the 256 MB last-level cache twice
-        per = a.codes.numel() + a.scales.numel() + b.codes.numel() + b.scales.numel()
-        n = max(2, min(4096, int(2 * 256e6 // per) + 1))
-        sets = []
-        for _ in range(n):
-            sets.append((nv.PackedOperand(a.codes.clone(), a.scales.clone(), a.rows, a.K),
-                         nv.PackedOperand(b.codes.clone(), b.scales.clone(), b.rows, b.K),
-                         torch.empty_like(out)))
-    stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        x, y, o = sets[i % len(sets)]
-        nv.gemm(x, y, cfg.alpha, out=o, stream=stream)
-    torch.cuda.synchronize()
+    if not cold:
+        return [(a, b, out)]
+    # distinct operand copies whose total exceeds the 256 MB last-level cache twice
+    per = a.codes.numel() + a.scales.numel() + b.codes.numel() + b.scales.numel()
+    n = max(2, min(2048, int(2 * 256e6 // per) + 1))
+    return [(nv.PackedOperand(a.codes.clone(), a.scales.clone(), a.rows, a.K),
+             nv.PackedOperand(b.codes.clone(), b.scales.clone(), b.rows, b.K),
+             torch.empty_like(out)) for _ in range(n)]
+
+
+def time_workload(nv, torch, cfg, steps, warmup, cold=False, ops=None):
+    """Per-call time of nvfp4_gemm on resident operands.
+
+    'graph': the `steps` calls are captured once into a HIP graph (no memset
+    or allocation inside: the split-K workspace exists after the warm-up) and
+    the graph is replayed between two events, so the figure is the device
+    time per call without host launch overhead.  'eager': the same calls
+    issued one by one from Python between two events (host overhead
+    included when the host is slower than the device)."""
+    if ops is None:
+        ops = synth.make_inputs(cfg)
+    sets = _operand_sets(nv, torch, cfg, ops, cold)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(max(1, warmup)):
+            x, y, o = sets[i % len(sets)]
+            nv.gemm(x, y, cfg.alpha, out=o, stream=stream)
+    stream.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    # eager
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for i in range(steps):
+            x, y, o = sets[i % len(sets)]
+            nv.gemm(x, y, cfg.alpha, out=o, stream=stream)
+        stop.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(stop) / steps
+    # graph
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        cap = torch.cuda.current_stream()
+        for i in range(steps):
+            x, y, o = sets[i % len(sets)]
+            nv.gemm(x, y, cfg.alpha, out=o, stream=cap)
+    with torch.cuda.stream(stream):
+        g.replay()                       # warm replay
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
-        x, y, o = sets[i % len(sets)]
-        nv.gemm(x, y, cfg.alpha, out=o, stream=stream)
-    stop.record(stream)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        g.replay()
+        stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / steps
+    graph_ms = start.elapsed_time(stop) / steps
     plan = nv.plan(cfg.M, cfg.N, cfg.K)
-    del sets
-    return ms, wall, plan, ops
+    del g, sets
+    return {"graph_ms": graph_ms, "eager_ms": eager_ms, "wall_s": wall, "plan": plan, "ops": ops}
 
 
 def cpu_baseline(cfg, ops, budget_s):
@@ -114,7 +145,8 @@ def cpu_baseline(cfg, ops, budget_s):
         o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, cfg.alpha, want_exact=False)
     el = time.perf_counter() - t0
     tflops = synth.flops(cfg.M, cfg.N, cfg.K) * reps / el / 1e12
-    return {"value": tflops, "unit": "TFLOPS", "cores": o.threads, "kind": "oracle",
+    # the oracle parallelises over output rows, so it uses at most M threads
+    return {"value": tflops, "unit": "TFLOPS", "cores": min(o.threads, cfg.M), "kind": "oracle",
             "sample": f"the full {cfg.M}x{cfg.N}x{cfg.K} GEMM repeated {reps} times "
                       f"({el:.1f} s, fp64 C oracle, OpenMP over rows)"}
 
@@ -134,7 +166,8 @@ def main():
     nv.init(torch.cuda.current_device())
 
     cfg = synth.config(args.workload)
-    ms, wall, plan, ops = time_workload(nv, torch, cfg, args.steps, args.warmup)
+    r = time_workload(nv, torch, cfg, args.steps, args.warmup)
+    ms, plan, ops = r["graph_ms"], r["plan"], r["ops"]
     tflops = synth.flops(cfg.M, cfg.N, cfg.K) / (ms * 1e-3) / 1e12
     line = {
         "metric": "NVFP4 GEMM TFLOPS (2MNK/s) per shape + % of HBM/MFMA roofline, 1 MI355X",
@@ -149,26 +182,30 @@ def main():
                    "split_k": plan["split_k"], "tile": [plan["tile_m"], plan["tile_n"]],
                    "operands": "E2M1 codes + E4M3 per-16 scales (packed), bf16 out, "
                                "fp16 MFMA with fp32 accumulation",
+                   "timing": "HIP graph of the timed calls replayed between HIP events",
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline_for(cfg, ms * 1e-3),
-        "wall_s_timed_region": wall,
+        "eager_ms_per_step": r["eager_ms"],
+        "wall_s_timed_region": r["wall_s"],
     }
     if args.cold:
-        cms, _, _, _ = time_workload(nv, torch, cfg, args.steps, args.warmup, cold=True)
-        line["cold"] = {"ms_per_step": cms,
-                        "tflops": synth.flops(cfg.M, cfg.N, cfg.K) / (cms * 1e-3) / 1e12,
-                        "roofline": roofline_for(cfg, cms * 1e-3)}
+        c = time_workload(nv, torch, cfg, args.steps, args.warmup, cold=True, ops=ops)
+        line["cold"] = {"ms_per_step": c["graph_ms"],
+                        "tflops": synth.flops(cfg.M, cfg.N, cfg.K) / (c["graph_ms"] * 1e-3) / 1e12,
+                        "roofline": roofline_for(cfg, c["graph_ms"] * 1e-3)}
     if not args.only_headline:
         per = {}
         for c in synth.CONFIGS:
             if c.index == cfg.index:
                 continue
-            cms, _, cplan, _ = time_workload(nv, torch, c, args.steps, args.warmup)
+            cr = time_workload(nv, torch, c, args.steps, args.warmup)
+            cms = cr["graph_ms"]
             ctf = synth.flops(c.M, c.N, c.K) / (cms * 1e-3) / 1e12
             per[c.name] = {"M": c.M, "N": c.N, "K": c.K, "ms": cms, "tflops": ctf,
+                           "eager_ms": cr["eager_ms"],
                            "roofline": roofline_for(c, cms * 1e-3),
-                           "path": "skinny" if cplan["path"] == nv.PATH_SKINNY else "tile",
-                           "split_k": cplan["split_k"],
+                           "path": "skinny" if cr["plan"]["path"] == nv.PATH_SKINNY else "tile",
+                           "split_k": cr["plan"]["split_k"],
                            "pages_tflops_other_gpu": PAGES_TFLOPS.get(c.index)}
         line["per_shape"] = per
     if not args.no_cpu_baseline:

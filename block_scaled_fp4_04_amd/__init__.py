@@ -170,6 +170,13 @@ class PackedOperand:
     rows: int
     K: int
 
+    def check(self, name: str) -> None:
+        import torch
+        need_c, need_s = packed_size(self.rows, self.K)
+        for what, t, need in ((".codes", self.codes, need_c), (".scales", self.scales, need_s)):
+            if t.dtype != torch.uint8 or t.numel() != need or not t.is_contiguous():
+                raise ValueError(f"{name}{what} must be a contiguous uint8 tensor of {need} bytes")
+
 
 def to_device(codes: np.ndarray, scales: np.ndarray, device="cuda") -> PackedOperand:
     """Pack canonical host arrays and copy them to ``device``."""
@@ -199,12 +206,8 @@ def gemm(a: PackedOperand, b: PackedOperand, alpha: float = 1.0, out=None,
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
-    for name, t, need in (("a.codes", a.codes, packed_size(M, K)[0]),
-                          ("a.scales", a.scales, packed_size(M, K)[1]),
-                          ("b.codes", b.codes, packed_size(N, K)[0]),
-                          ("b.scales", b.scales, packed_size(N, K)[1])):
-        if t.dtype != torch.uint8 or t.numel() != need or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous uint8 tensor of {need} bytes")
+    a.check("a")
+    b.check("b")
     st = lib().nvfp4_gemm_with_path(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
                                     b.scales.data_ptr(), float(alpha), out.data_ptr(), M, N, K,
                                     int(path), int(split_k), _stream_handle(stream))

@@ -10,6 +10,7 @@
 // SM120 FP4 Kernel Disaster", section "The Bash Command").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -104,19 +105,22 @@ constexpr int kCUs = 256;
 
 Plan make_plan(int64_t M, int64_t N, int64_t K, int path, int split_req) {
     Plan p{};
-    const int64_t P = round_up(K, kPanelK) / kPanelK;
-    const int steps = (int)((P + 1) / 2);
+    const int64_t P = num_panels(K);
+    const int steps = (int)(P / 2);
     if (path == NVFP4_PATH_AUTO) path = (M <= 16) ? NVFP4_PATH_SKINNY : NVFP4_PATH_TILE;
     p.path = path;
     if (path == NVFP4_PATH_SKINNY) {
+        // One workgroup of kSkinnyWaves waves per 16 output columns covers the
+        // whole K range: the split-K hand-off costs more than it saves once
+        // there are 8 or more column groups (measured at 1x768x6144 and
+        // 16x256x6144).  Fewer groups split K (each wave keeps at least one
+        // 128-element work unit).
         const int64_t groups = round_up(N, kRowPad) / 16;
         int s = split_req;
         if (s <= 0) {
-            // Aim for about 4 work units per workgroup (one per wave) and at
-            // least two workgroups per CU in flight.
-            s = (int)((steps + 3) / 4);
-            while (s > 1 && groups * s > 8 * kCUs) --s;
-            if (s < 1) s = 1;
+            s = (int)((8 + groups - 1) / groups);
+            const int cap = steps / kSkinnyWaves;
+            if (s > cap) s = cap;
         }
         if (s > steps) s = steps;
         p.split_k = s < 1 ? 1 : s;
@@ -167,6 +171,14 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     if (dst != NVFP4_OK) return dst;
 
     const Plan plan = make_plan(M, N, K, path, split_k);
+    if (plan.path == NVFP4_PATH_TILE) {
+        // the tile kernel addresses each packed operand with 32-bit offsets
+        const int64_t P = num_panels(K);
+        const int64_t limit = (int64_t)1 << 31;
+        if (P * round_up(M, kRowPad) * kPanelCodeBytes >= limit ||
+            P * round_up(N, kRowPad) * kPanelCodeBytes >= limit)
+            return NVFP4_ERR_UNSUPPORTED;
+    }
     GemmArgs a{};
     a.a_codes = static_cast<const uint8_t*>(a_packed);
     a.a_scales = static_cast<const uint8_t*>(a_scales);
@@ -178,7 +190,7 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     a.N = (int)N;
     a.Mp = (int)round_up(M, kRowPad);
     a.Np = (int)round_up(N, kRowPad);
-    a.P = (int)(round_up(K, kPanelK) / kPanelK);
+    a.P = (int)(num_panels(K));
     a.split_k = plan.split_k;
     a.tiles_m = plan.tiles_m;
     a.tiles_n = plan.tiles_n;
@@ -221,7 +233,7 @@ int nvfp4_version(void) { return 100; }
 int nvfp4_packed_size(int64_t rows, int64_t K, size_t* code_bytes, size_t* scale_bytes) {
     if (!code_bytes || !scale_bytes || !valid_rows_k(rows, K)) return NVFP4_ERR_INVALID_VALUE;
     const int64_t Rp = round_up(rows, kRowPad);
-    const int64_t P = round_up(K, kPanelK) / kPanelK;
+    const int64_t P = num_panels(K);
     *code_bytes = (size_t)(P * Rp * kPanelCodeBytes);
     *scale_bytes = (size_t)(P * Rp * kPanelScaleBytes);
     return NVFP4_OK;
@@ -232,7 +244,7 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_
     if (!codes || !scales || !packed_codes || !packed_scales || !valid_rows_k(rows, K))
         return NVFP4_ERR_INVALID_VALUE;
     const int64_t Rp = round_up(rows, kRowPad);
-    const int64_t P = round_up(K, kPanelK) / kPanelK;
+    const int64_t P = num_panels(K);
     const int64_t rb = K / 2, rs = K / 16;  // canonical row strides
     for (int64_t p = 0; p < P; ++p) {
         for (int64_t r = 0; r < Rp; ++r) {
@@ -244,11 +256,13 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_
                 std::memset(ds, 0, kPanelScaleBytes);
                 continue;
             }
-            const int64_t nc = std::min<int64_t>(kPanelCodeBytes, rb - j0);
-            const int64_t ns = std::min<int64_t>(kPanelScaleBytes, rs - b0);
-            std::memcpy(dc, codes + r * rb + j0, (size_t)nc);
+            // bytes of this panel that exist in the canonical row (0 in the
+            // zero panels that round K up to whole steps)
+            const int64_t nc = std::max<int64_t>(0, std::min<int64_t>(kPanelCodeBytes, rb - j0));
+            const int64_t ns = std::max<int64_t>(0, std::min<int64_t>(kPanelScaleBytes, rs - b0));
+            if (nc > 0) std::memcpy(dc, codes + r * rb + j0, (size_t)nc);
             if (nc < kPanelCodeBytes) std::memset(dc + nc, 0, (size_t)(kPanelCodeBytes - nc));
-            std::memcpy(ds, scales + r * rs + b0, (size_t)ns);
+            if (ns > 0) std::memcpy(ds, scales + r * rs + b0, (size_t)ns);
             if (ns < kPanelScaleBytes) std::memset(ds + ns, 0, (size_t)(kPanelScaleBytes - ns));
         }
     }
@@ -260,16 +274,16 @@ int nvfp4_unpack(const uint8_t* packed_codes, const uint8_t* packed_scales, int6
     if (!codes || !scales || !packed_codes || !packed_scales || !valid_rows_k(rows, K))
         return NVFP4_ERR_INVALID_VALUE;
     const int64_t Rp = round_up(rows, kRowPad);
-    const int64_t P = round_up(K, kPanelK) / kPanelK;
+    const int64_t P = num_panels(K);
     const int64_t rb = K / 2, rs = K / 16;
     for (int64_t p = 0; p < P; ++p) {
         for (int64_t r = 0; r < rows; ++r) {
             const uint8_t* sc = packed_codes + (p * Rp + r) * kPanelCodeBytes;
             const uint8_t* ss = packed_scales + (p * Rp + r) * kPanelScaleBytes;
             const int64_t j0 = p * kPanelCodeBytes, b0 = p * kPanelScaleBytes;
-            const int64_t nc = std::min<int64_t>(kPanelCodeBytes, rb - j0);
-            const int64_t ns = std::min<int64_t>(kPanelScaleBytes, rs - b0);
-            std::memcpy(codes + r * rb + j0, sc, (size_t)nc);
+            const int64_t nc = std::max<int64_t>(0, std::min<int64_t>(kPanelCodeBytes, rb - j0));
+            const int64_t ns = std::max<int64_t>(0, std::min<int64_t>(kPanelScaleBytes, rs - b0));
+            if (nc > 0) std::memcpy(codes + r * rb + j0, sc, (size_t)nc);
             if (ns > 0) std::memcpy(scales + r * rs + b0, ss, (size_t)ns);
         }
     }

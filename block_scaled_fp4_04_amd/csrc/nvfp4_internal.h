@@ -8,11 +8,15 @@ namespace nvfp4 {
 
 // Packed operand geometry (see include/nvfp4.h, "Packed layout").
 constexpr int kPanelK = 64;        // elements per panel
+constexpr int kStepK = 128;        // K is padded to whole steps of two panels
 constexpr int kPanelCodeBytes = 32;  // bytes of codes per row per panel
 constexpr int kPanelScaleBytes = 4;  // scale bytes per row per panel
 constexpr int kRowPad = 16;
+constexpr int kSkinnyWaves = 16;    // waves per workgroup of the skinny kernel
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+// Number of 64-element panels of a packed operand (always even).
+inline int64_t num_panels(int64_t K) { return round_up(K, kStepK) / kPanelK; }
 
 struct GemmArgs {
     const uint8_t* a_codes;   // [P][Mp][32]
@@ -25,7 +29,7 @@ struct GemmArgs {
     float alpha;
     int M, N;                 // logical output size
     int Mp, Np;               // padded row counts of the packed operands
-    int P;                    // number of 64-element K panels
+    int P;                    // number of 64-element K panels (even)
     int split_k;              // number of K slices (>= 1)
     int tiles_m, tiles_n;     // output tiles along M and N (tile kernel)
 };
@@ -42,9 +46,6 @@ inline TileShape tile_shape(int cfg) {
     }
 }
 
-// Number of 128-element K steps (two panels each) of the tile kernel and of
-// the skinny kernel.
-inline int k_steps(int P) { return (P + 1) / 2; }
 
 // Workspace needs (bytes of partials, number of counters) of a launch.
 size_t tile_partial_floats(int cfg, const GemmArgs& a);

@@ -59,48 +59,128 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int s) {
 }
 
 // ---------------------------------------------------------------------------
+// Split-K hand-off between workgroups.
+//
+// Partial sums are written and read with relaxed device-scope atomic stores
+// and loads (on gfx950 these are plain stores/loads with the device-coherence
+// bit, so no cache-wide write-back or invalidate is needed); the writer waits
+// for its stores to complete before it increments the tile's arrival counter,
+// and the last arrival reads the partials only after its increment returned.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void publish(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Increments the counter once all earlier stores of the calling wave have
+// completed; returns the counter's previous value.
+__device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
+    __builtin_amdgcn_s_waitcnt(0);
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(uint32_t* counter) {
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until at most N vector-memory instructions of this wave are in flight
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+typedef __attribute__((address_space(3))) uint8_t* lds_u8;
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(lds_u8)(p);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Direct HBM -> LDS copies (buffer_load ... lds): every lane fetches 16 (or
+// 4) bytes at voff + soff inside the buffer and the wave's 1024 (or 256)
+// bytes land contiguously at LDS address `lds` (wave-uniform, through M0).
+// Issued as inline assembly so that the compiler neither reorders LDS reads
+// around them nor inserts its own conservative wait for every LDS read; the
+// kernel waits for them explicitly with wait_vmcnt and orders LDS reuse with
+// barriers.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                     uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
+}
+// Workgroup barrier that is also a compiler barrier for memory operations
+// (it adds no wait for outstanding loads: those are waited for explicitly).
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
 // Large-M tile kernel.
 //
 // Workgroup: 256 threads = 4 waves in a 2 x 2 grid; workgroup tile BM x BN,
 // wave tile (BM/2) x (BN/2) made of 32 x 32 MFMA blocks
 // (v_mfma_f32_32x32x16_f16).  K advances in steps of two 64-element panels.
-// Each step's packed codes (4 bits/element) and scales are copied from HBM
-// to LDS with 16-byte loads; the scales are widened to fp16 on the way.
-// LDS holds two such steps (double buffer): the next step's loads are in
-// flight while the current one is decoded and multiplied.
+//
+// HBM -> LDS: each step's packed codes (4 bits/element) and raw E4M3 scale
+// bytes are copied with direct-to-LDS loads (16 and 4 bytes per lane) into a
+// ring of NS stage buffers, NS-1 steps ahead of the step being multiplied, so
+// several steps of loads are always in flight and no VGPRs are spent on
+// staging.
 //
 // LDS code layout of one operand and panel: rows in groups of 32; within a
-// group, first the low 16 bytes of the 32 rows, then the high 16 bytes:
+// group, first the low 16 bytes of the 32 rows, then the high 16 bytes
+// (one 1 KB direct load per group):
 //   offset(row, half) = (row / 32) * 1024 + half * 512 + (row % 32) * 16.
-// MFMA lane l reads row l % 32, half l / 32 as one 16-byte read, so the 16
-// lanes of each LDS phase touch 256 consecutive bytes.
-// LDS scale layout: fp16 [panel][row][4 blocks].
+// MFMA lane l reads row l % 32, half l / 32 as one 16-byte read, so the lanes
+// of each LDS phase touch consecutive bytes.  Scales: [panel][row][4 bytes].
+//
+// Decode and MFMA are software-pipelined: the operands of sub-step s+1 are
+// decoded while the 16 MFMAs of sub-step s run, with the instruction
+// scheduler told to alternate one MFMA and a few VALU instructions.
+//
+// Rows past the padded operand are clamped to its last row (their results
+// are never stored).  The packed K is a whole number of steps (the packer
+// pads with zeros), so every step holds two panels.
 //
 // Split-K (split_k > 1): the K steps are divided into split_k contiguous
-// ranges; each workgroup stores its FP32 tile to the workspace, and the last
-// of a tile's workgroups to arrive (atomic counter) adds the partial tiles in
-// split order (deterministic) and runs the epilogue.
+// ranges; each workgroup publishes its FP32 tile to the workspace, and the
+// last of a tile's workgroups to arrive adds the partial tiles in split order
+// (deterministic) and runs the epilogue.
 // ---------------------------------------------------------------------------
-template <int BM, int BN>
+template <int BM, int BN, int NS, bool SPLIT>
 __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     constexpr int MI = BM / 64;  // 32-row blocks per wave
     constexpr int NI = BN / 64;  // 32-column blocks per wave
     constexpr int A_CODE = 2 * BM * 32;
     constexpr int B_CODE = 2 * BN * 32;
-    constexpr int A_SC = 2 * BM * 8;
-    constexpr int B_SC = 2 * BN * 8;
-    constexpr int BUF = A_CODE + B_CODE + A_SC + B_SC;
-    constexpr int CODE_CHUNKS = 4 * (BM + BN);  // 16-byte chunks per step
-    constexpr int CPT = CODE_CHUNKS / 256;      // per thread
-    constexpr int A_CPT = (4 * BM) / 256;       // first A_CPT chunks are A
-    constexpr int SC_CHUNKS = (BM + BN) / 2;    // 16-byte scale chunks per step
-    static_assert(CODE_CHUNKS % 256 == 0 && SC_CHUNKS <= 256, "tile shape");
+    constexpr int A_SC = 2 * BM * 4;
+    constexpr int B_SC = 2 * BN * 4;
+    constexpr int OFF_B = A_CODE;
+    constexpr int OFF_SA = A_CODE + B_CODE;
+    constexpr int OFF_SB = OFF_SA + A_SC;
+    constexpr int STAGE = OFF_SB + B_SC;
+    constexpr int A_CCH = 2 * BM / 32;           // 1 KB code chunks of A per step
+    constexpr int CCH = A_CCH + 2 * BN / 32;
+    constexpr int A_SCH = 2 * BM / 64;           // 256 B scale chunks of A per step
+    constexpr int SCH = A_SCH + 2 * BN / 64;
+    static_assert(CCH % 4 == 0 && SCH % 4 == 0, "chunks must split evenly over 4 waves");
+    constexpr int LPS = CCH / 4 + SCH / 4;       // direct loads per wave per step
+    static_assert(NS >= 3 && NS <= 4 && (NS - 2) * LPS < 64, "pipeline depth");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int q = lane & 31, h = lane >> 5;
 
@@ -110,7 +190,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     int bid = blockIdx.x;
     const int total = gridDim.x;
     if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int S = a.split_k;
+    const int S = SPLIT ? a.split_k : 1;
     const int z = bid % S;
     const int t = bid / S;
     constexpr int GROUP_M = 8;
@@ -121,78 +201,65 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     const int tn = (t % in_group) / gsize;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    const int nst = (a.P + 1) / 2;
+    const int nst = a.P / 2;
     const int st0 = (int)((int64_t)z * nst / S);
     const int st1 = (int)((int64_t)(z + 1) * nst / S);
 
-    // Per-thread copy plan (constant over K steps).
-    int c_row[CPT], c_half[CPT], c_pl[CPT], c_lds[CPT];
+    const uint32_t lds0 = lds_addr(lds);
+
+    // Direct-load plan of this wave (constant over K steps): for each of its
+    // code and scale chunks, the lane's byte offset inside a panel and the
+    // chunk's place in the stage buffer.
+    const __amdgpu_buffer_rsrc_t rac = make_rsrc(a.a_codes, (uint32_t)a.P * a.Mp * 32u);
+    const __amdgpu_buffer_rsrc_t rbc = make_rsrc(a.b_codes, (uint32_t)a.P * a.Np * 32u);
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(a.a_scales, (uint32_t)a.P * a.Mp * 4u);
+    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(a.b_scales, (uint32_t)a.P * a.Np * 4u);
+    uint32_t c_voff[CCH / 4], s_voff[SCH / 4];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c = tid + 256 * j;
-        const bool isA = j < A_CPT;
+    for (int i = 0; i < CCH / 4; ++i) {
+        const int k = wave + 4 * i;
+        const bool isA = k < A_CCH;
         const int R = isA ? BM : BN;
-        const int cc = isA ? c : c - 4 * BM;
-        c_pl[j] = cc / (2 * R);
-        const int rem = cc % (2 * R);
-        c_row[j] = rem >> 1;
-        c_half[j] = rem & 1;
-        c_lds[j] = (isA ? 0 : A_CODE) + c_pl[j] * R * 32 + (c_row[j] >> 5) * 1024 +
-                   c_half[j] * 512 + (c_row[j] & 31) * 16;
+        const int grp = (isA ? k : k - A_CCH) % (R / 32);
+        const int row = min((isA ? m0 : n0) + grp * 32 + q, (isA ? a.Mp : a.Np) - 1);
+        c_voff[i] = (uint32_t)row * 32u + (uint32_t)h * 16u;
     }
-    const bool sc_active = tid < SC_CHUNKS;
-    const bool sc_isA = tid < BM / 2;
-    const int sc_c = sc_isA ? tid : tid - BM / 2;
-    const int sc_R = sc_isA ? BM : BN;
-    const int sc_pl = sc_c / (sc_R / 4);
-    const int sc_row = 4 * (sc_c % (sc_R / 4));
-    const int sc_lds = A_CODE + B_CODE + (sc_isA ? 0 : A_SC) + (sc_pl * sc_R + sc_row) * 8;
-
-    uint4 pre[CPT];
-    uint4 pre_sc = {0u, 0u, 0u, 0u};
-
-    auto load_step = [&](int st) {
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const bool isA = j < A_CPT;
-            const int panel = 2 * st + c_pl[j];
-            const int row = (isA ? m0 : n0) + c_row[j];
-            const int Rp = isA ? a.Mp : a.Np;
-            const uint8_t* base = isA ? a.a_codes : a.b_codes;
-            uint4 v = {0u, 0u, 0u, 0u};
-            if (panel < a.P && row < Rp)
-                v = *reinterpret_cast<const uint4*>(
-                    base + ((int64_t)panel * Rp + row) * 32 + c_half[j] * 16);
-            pre[j] = v;
-        }
-        if (sc_active) {
-            const int panel = 2 * st + sc_pl;
-            const int row = (sc_isA ? m0 : n0) + sc_row;
-            const int Rp = sc_isA ? a.Mp : a.Np;
-            const uint8_t* base = sc_isA ? a.a_scales : a.b_scales;
-            uint4 v = {0u, 0u, 0u, 0u};
-            if (panel < a.P && row < Rp)
-                v = *reinterpret_cast<const uint4*>(base + ((int64_t)panel * Rp + row) * 4);
-            pre_sc = v;
-        }
-    };
-    auto store_step = [&](int buf) {
-        uint8_t* b = lds + buf * BUF;
+    for (int i = 0; i < SCH / 4; ++i) {
+        const int k = wave + 4 * i;
+        const bool isA = k < A_SCH;
+        const int R = isA ? BM : BN;
+        const int c = (isA ? k : k - A_SCH) % (R / 64);
+        const int row = min((isA ? m0 : n0) + c * 64 + lane, (isA ? a.Mp : a.Np) - 1);
+        s_voff[i] = (uint32_t)row * 4u;
+    }
+
+    // Issue the direct loads of step st into stage buffer sb (LPS per wave).
+    auto issue = [&](int st, int sb) {
+        const uint32_t b = lds0 + (uint32_t)(sb * STAGE);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) *reinterpret_cast<uint4*>(b + c_lds[j]) = pre[j];
-        if (sc_active) {
-            h2 s[8];
-            s[0] = e4m3x2_lo(pre_sc.x); s[1] = e4m3x2_hi(pre_sc.x);
-            s[2] = e4m3x2_lo(pre_sc.y); s[3] = e4m3x2_hi(pre_sc.y);
-            s[4] = e4m3x2_lo(pre_sc.z); s[5] = e4m3x2_hi(pre_sc.z);
-            s[6] = e4m3x2_lo(pre_sc.w); s[7] = e4m3x2_hi(pre_sc.w);
-            uint4 w0, w1;
-            w0.x = __builtin_bit_cast(uint32_t, s[0]); w0.y = __builtin_bit_cast(uint32_t, s[1]);
-            w0.z = __builtin_bit_cast(uint32_t, s[2]); w0.w = __builtin_bit_cast(uint32_t, s[3]);
-            w1.x = __builtin_bit_cast(uint32_t, s[4]); w1.y = __builtin_bit_cast(uint32_t, s[5]);
-            w1.z = __builtin_bit_cast(uint32_t, s[6]); w1.w = __builtin_bit_cast(uint32_t, s[7]);
-            *reinterpret_cast<uint4*>(b + sc_lds) = w0;
-            *reinterpret_cast<uint4*>(b + sc_lds + 16) = w1;
+        for (int i = 0; i < CCH / 4; ++i) {
+            const int k = wave + 4 * i;
+            const bool isA = k < A_CCH;
+            const int R = isA ? BM : BN;
+            const int kk = isA ? k : k - A_CCH;
+            const int pl = kk / (R / 32), grp = kk % (R / 32);
+            const uint32_t panel = (uint32_t)(2 * st + pl);
+            const uint32_t soff = panel * (uint32_t)(isA ? a.Mp : a.Np) * 32u;
+            dma16(isA ? rac : rbc, c_voff[i], soff,
+                  b + (uint32_t)((isA ? 0 : OFF_B) + (pl * (R / 32) + grp) * 1024));
+        }
+#pragma unroll
+        for (int i = 0; i < SCH / 4; ++i) {
+            const int k = wave + 4 * i;
+            const bool isA = k < A_SCH;
+            const int R = isA ? BM : BN;
+            const int kk = isA ? k : k - A_SCH;
+            const int pl = kk / (R / 64), c = kk % (R / 64);
+            const uint32_t panel = (uint32_t)(2 * st + pl);
+            const uint32_t soff = panel * (uint32_t)(isA ? a.Mp : a.Np) * 4u;
+            dma4(isA ? ras : rbs, s_voff[i], soff,
+                 b + (uint32_t)((isA ? OFF_SA : OFF_SB) + (pl * R + c * 64) * 4));
         }
     };
 
@@ -204,16 +271,8 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    if (st0 < st1) {
-        load_step(st0);
-        store_step(0);
-        __syncthreads();
-    }
-    for (int st = st0; st < st1; ++st) {
-        const int buf = (st - st0) & 1;
-        const bool more = st + 1 < st1;
-        if (more) load_step(st + 1);
-        const uint8_t* b = lds + buf * BUF;
+    // Multiply one step (two panels) held in buffer b.
+    auto compute = [&](const uint8_t* b) {
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) {
             uint4 ca[MI], cb[NI];
@@ -221,73 +280,107 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const int g = wm * MI + i;
-                ca[i] = *reinterpret_cast<const uint4*>(b + pl * BM * 32 + g * 1024 + h * 512 +
-                                                        q * 16);
-                sa[i] = *reinterpret_cast<const h2*>(b + A_CODE + B_CODE +
-                                                     (pl * BM + g * 32 + q) * 8 + h * 4);
+                ca[i] = *reinterpret_cast<const uint4*>(b + pl * BM * 32 + g * 1024 + h * 512 + q * 16);
+                const uint32_t raw = *reinterpret_cast<const uint16_t*>(
+                    b + OFF_SA + (pl * BM + g * 32 + q) * 4 + h * 2);
+                sa[i] = e4m3x2_lo(raw);
             }
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 const int g = wn * NI + j;
-                cb[j] = *reinterpret_cast<const uint4*>(b + A_CODE + pl * BN * 32 + g * 1024 +
-                                                        h * 512 + q * 16);
-                sb[j] = *reinterpret_cast<const h2*>(b + A_CODE + B_CODE + A_SC +
-                                                     (pl * BN + g * 32 + q) * 8 + h * 4);
+                cb[j] = *reinterpret_cast<const uint4*>(b + OFF_B + pl * BN * 32 + g * 1024 + h * 512 + q * 16);
+                const uint32_t raw = *reinterpret_cast<const uint16_t*>(
+                    b + OFF_SB + (pl * BN + g * 32 + q) * 4 + h * 2);
+                sb[j] = e4m3x2_lo(raw);
             }
+            h8 av[2][MI], bv[2][NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) av[0][i] = decode8(word_of(ca[i], 0), sa[i][0]);
+#pragma unroll
+            for (int j = 0; j < NI; ++j) bv[0][j] = decode8(word_of(cb[j], 0), sb[j][0]);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                h8 av[MI], bv[NI];
+                const int cur = s & 1, nxt = cur ^ 1;
+                if (s < 3) {
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    av[i] = decode8(word_of(ca[i], s), s < 2 ? sa[i][0] : sa[i][1]);
+                    for (int i = 0; i < MI; ++i)
+                        av[nxt][i] = decode8(word_of(ca[i], s + 1), (s + 1) < 2 ? sa[i][0] : sa[i][1]);
 #pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    bv[j] = decode8(word_of(cb[j], s), s < 2 ? sb[j][0] : sb[j][1]);
+                    for (int j = 0; j < NI; ++j)
+                        bv[nxt][j] = decode8(word_of(cb[j], s + 1), (s + 1) < 2 ? sb[j][0] : sb[j][1]);
+                }
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j],
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j],
                                                                            acc[i][j], 0, 0, 0);
+                if (s < 3) {
+#pragma unroll
+                    for (int m = 0; m < MI * NI; ++m) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, (8 * (MI + NI) + MI * NI - 1) / (MI * NI), 0);
+                    }
+                }
             }
         }
-        if (more) store_step(buf ^ 1);
-        __syncthreads();
+    };
+
+    // Prologue: NS-1 steps in flight.
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+        if (st0 + u < st1) issue(st0 + u, u);
+
+    int sb = 0;  // stage buffer of step st
+    for (int st = st0; st < st1; ++st) {
+        // Loads issued after step st's: steps st+1 .. min(st+NS-2, st1-1).
+        const int later = min(NS - 2, st1 - 1 - st);
+        if (later >= 2) wait_vmcnt<2 * LPS>();
+        else if (later == 1) wait_vmcnt<LPS>();
+        else wait_vmcnt<0>();
+        wg_barrier();  // step st is in LDS; step st-1's buffer is free
+        if (st + NS - 1 < st1) issue(st + NS - 1, sb == 0 ? NS - 1 : sb - 1);
+        compute(lds + sb * STAGE);
+        sb = sb == NS - 1 ? 0 : sb + 1;
     }
 
-    // Split-K: publish the partial tile; the last arrival reduces.
-    if (S > 1) {
+    // Split-K: publish the partial tile; the last arrival reduces in split order.
+    if (SPLIT) {
         float* mine = a.partials + ((int64_t)t * S + z) * (BM * BN);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mine[((i * NI + j) * 16 + v) * 256 + tid] = acc[i][j][v];
-        __threadfence();
-        __syncthreads();
+                for (int v = 0; v < 16; ++v)
+                    publish(mine + ((i * NI + j) * 16 + v) * 256 + tid, acc[i][j][v]);
         __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
         if (tid == 0) {
-            const uint32_t old = atomicAdd(a.counters + t, 1u);
+            const uint32_t old = arrive(a.counters + t);
             s_last = (old == (uint32_t)(S - 1));
-            if (s_last) a.counters[t] = 0u;  // every split has arrived: reset for the next call
+            if (s_last) reset_counter(a.counters + t);  // all splits arrived
         }
         __syncthreads();
         if (!s_last) return;
-        __threadfence();
         const float* all = a.partials + (int64_t)t * S * (BM * BN);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int idx = ((i * NI + j) * 16 + v) * 256 + tid;
-                    float sum = 0.0f;
-                    for (int zz = 0; zz < S; ++zz)
-                        sum += (zz == z) ? acc[i][j][v] : all[(int64_t)zz * (BM * BN) + idx];
-                    acc[i][j][v] = sum;
-                }
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        for (int zz = 0; zz < S; ++zz) {
+            const float* pz = all + (int64_t)zz * (BM * BN);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        acc[i][j][v] += fetch(pz + ((i * NI + j) * 16 + v) * 256 + tid);
+        }
     }
 
     // Epilogue: y = alpha * acc (FP32), bfloat16 round-to-nearest-even.
@@ -297,19 +390,22 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
+            // one 32 x 32 block at a time keeps few accumulators in VGPRs
+            __builtin_amdgcn_sched_barrier(0);
             const int col = n0 + wn * (BN / 2) + j * 32 + q;
-            if (col >= a.N) continue;
+            if (col < a.N) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (row < a.M) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * acc[i][j][v]);
+                for (int v = 0; v < 16; ++v) {
+                    const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (row < a.M) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * acc[i][j][v]);
+                }
             }
         }
 }
 
 // ---------------------------------------------------------------------------
 // Skinny-M kernel (M <= 16), for decode-sized GEMMs that are bound by
-// streaming B from HBM.
+// streaming B from HBM and by latency.
 //
 // v_mfma_f32_16x16x32_f16 with the (zero-padded) 16 rows of A as the MFMA A
 // operand and 16 rows of B as the B operand.  Work unit: 16 B rows x 128 K
@@ -317,77 +413,95 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 // half (g % 2) of panel (g / 2): one 16-byte load of codes and one 2-byte
 // load of scales per operand, straight from HBM (B is used once, so it does
 // not pass through LDS).  Each MFMA sub-step s takes word s of every lane.
+// Lanes whose A row is at or beyond M skip their A loads (zeros).
 //
-// Grid: (N / 16 row groups) x split_k workgroups of 4 waves; a workgroup
-// owns one row group and a contiguous range of work units, dealt to its
-// waves in turn.  The 4 wave partials are added in LDS (fixed order), then
-// across workgroups through the workspace by the last arrival (fixed order).
+// Grid: (N / 16 row groups) x split_k workgroups of WAVES waves; a
+// workgroup owns one row group and a contiguous range of work units, dealt
+// to its waves in turn; each wave issues the loads of up to UNITS work units
+// before it waits, so one memory round trip covers them.  The wave partials
+// are added in LDS in wave order; with split_k > 1 the workgroup partials
+// are added by the last arrival in split order (deterministic).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) skinny_kernel(GemmArgs a) {
+template <int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) skinny_kernel(GemmArgs a) {
+    constexpr int UNITS = 4;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int S = a.split_k;
     const int g = blockIdx.x / S;
     const int z = blockIdx.x % S;
-    const int C = (a.P + 1) / 2;
+    const int C = a.P / 2;
     const int c0 = (int)((int64_t)z * C / S);
     const int c1 = (int)((int64_t)(z + 1) * C / S);
     const int r16 = lane & 15;
     const int grp = lane >> 4;
     const int pl = grp >> 1, half = grp & 1;
     const int nrow = g * 16 + r16;
+    const bool a_row = r16 < a.M;
 
     f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = c0 + wave; c < c1; c += 4) {
-        const int panel = 2 * c + pl;
-        uint4 bw = {0u, 0u, 0u, 0u}, aw = {0u, 0u, 0u, 0u};
-        uint32_t bs = 0u, as = 0u;
-        if (panel < a.P) {
-            const int64_t bo = (int64_t)panel * a.Np + nrow;
-            const int64_t ao = (int64_t)panel * a.Mp + r16;
-            bw = *reinterpret_cast<const uint4*>(a.b_codes + bo * 32 + half * 16);
-            bs = *reinterpret_cast<const uint16_t*>(a.b_scales + bo * 4 + half * 2);
-            aw = *reinterpret_cast<const uint4*>(a.a_codes + ao * 32 + half * 16);
-            as = *reinterpret_cast<const uint16_t*>(a.a_scales + ao * 4 + half * 2);
-        }
-        const h2 sbh = e4m3x2_lo(bs);
-        const h2 sah = e4m3x2_lo(as);
+    for (int base = c0 + wave; base < c1; base += WAVES * UNITS) {
+        uint4 bw[UNITS], aw[UNITS];
+        uint32_t bs[UNITS], as[UNITS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const h8 av = decode8(word_of(aw, s), s < 2 ? sah[0] : sah[1]);
-            const h8 bv = decode8(word_of(bw, s), s < 2 ? sbh[0] : sbh[1]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+        for (int u = 0; u < UNITS; ++u) {
+            const int c = base + WAVES * u;
+            const int panel = 2 * c + pl;
+            bw[u] = uint4{0u, 0u, 0u, 0u};
+            aw[u] = uint4{0u, 0u, 0u, 0u};
+            bs[u] = 0u;
+            as[u] = 0u;
+            if (c < c1 && panel < a.P) {
+                const int64_t bo = (int64_t)panel * a.Np + nrow;
+                bw[u] = *reinterpret_cast<const uint4*>(a.b_codes + bo * 32 + half * 16);
+                bs[u] = *reinterpret_cast<const uint16_t*>(a.b_scales + bo * 4 + half * 2);
+                if (a_row) {
+                    const int64_t ao = (int64_t)panel * a.Mp + r16;
+                    aw[u] = *reinterpret_cast<const uint4*>(a.a_codes + ao * 32 + half * 16);
+                    as[u] = *reinterpret_cast<const uint16_t*>(a.a_scales + ao * 4 + half * 2);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const h2 sbh = e4m3x2_lo(bs[u]);
+            const h2 sah = e4m3x2_lo(as[u]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const h8 av = decode8(word_of(aw[u], s), s < 2 ? sah[0] : sah[1]);
+                const h8 bv = decode8(word_of(bw[u], s), s < 2 ? sbh[0] : sbh[1]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+            }
         }
     }
 
-    __shared__ f4v red[4][64];
+    __shared__ f4v red[WAVES][64];
     red[wave][lane] = acc;
     __syncthreads();
     if (wave != 0) return;
     f4v sum = red[0][lane];
-    sum += red[1][lane];
-    sum += red[2][lane];
-    sum += red[3][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
 
     if (S > 1) {
         float* mine = a.partials + ((int64_t)g * S + z) * 256;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mine[v * 64 + lane] = sum[v];
-        __threadfence();
+        for (int v = 0; v < 4; ++v) publish(mine + v * 64 + lane, sum[v]);
         uint32_t old = 0;
-        if (lane == 0) old = atomicAdd(a.counters + g, 1u);
+        if (lane == 0) old = arrive(a.counters + g);
         old = __shfl(old, 0);
         if (old != (uint32_t)(S - 1)) return;
-        if (lane == 0) a.counters[g] = 0u;  // every split has arrived: reset for the next call
-        __threadfence();
+        if (lane == 0) reset_counter(a.counters + g);  // all splits arrived
         const float* all = a.partials + (int64_t)g * S * 256;
+        f4v t = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int zz = 0; zz < S; ++zz) {
+            f4v p;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float t = 0.0f;
-            for (int zz = 0; zz < S; ++zz) t += (zz == z) ? sum[v] : all[zz * 256 + v * 64 + lane];
-            sum[v] = t;
+            for (int v = 0; v < 4; ++v) p[v] = fetch(all + zz * 256 + v * 64 + lane);
+            t += p;
         }
+        sum = t;
     }
 
     // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + v.
@@ -422,17 +536,27 @@ size_t skinny_counters(const GemmArgs& a) {
 hipError_t launch_tile(int cfg, const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.split_k));
     const dim3 block(256);
+    const bool split = a.split_k > 1;
     switch (cfg) {
-        case TILE_256x256: hipLaunchKernelGGL((tile_kernel<256, 256>), grid, block, 0, stream, a); break;
-        case TILE_128x128: hipLaunchKernelGGL((tile_kernel<128, 128>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((tile_kernel<64, 64>), grid, block, 0, stream, a); break;
+        case TILE_256x256:
+            if (split) hipLaunchKernelGGL((tile_kernel<256, 256, 4, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((tile_kernel<256, 256, 4, false>), grid, block, 0, stream, a);
+            break;
+        case TILE_128x128:
+            if (split) hipLaunchKernelGGL((tile_kernel<128, 128, 4, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((tile_kernel<128, 128, 4, false>), grid, block, 0, stream, a);
+            break;
+        default:
+            if (split) hipLaunchKernelGGL((tile_kernel<64, 64, 4, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((tile_kernel<64, 64, 4, false>), grid, block, 0, stream, a);
+            break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.Np / 16) * a.split_k));
-    hipLaunchKernelGGL(skinny_kernel, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(skinny_kernel<kSkinnyWaves>, grid, dim3(kSkinnyWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 

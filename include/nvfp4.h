@@ -24,7 +24,7 @@
  *                       element 2j+1 in bits 7:4;
  *   scales [rows][K/16] byte b scales elements 16b .. 16b+15.
  * Packed layout (what nvfp4_gemm consumes; produced by nvfp4_pack): rows are
- * padded to Rp = roundup(rows, 16) and K to Kp = roundup(K, 64) with zero
+ * padded to Rp = roundup(rows, 16) and K to Kp = roundup(K, 128) with zero
  * codes and zero scales; the data is split into Kp/64 panels of 64 elements:
  *   packed codes  [Kp/64][Rp][32]  (32 bytes = 64 codes of one row, same
  *                                   byte/nibble order as canonical)
@@ -105,7 +105,9 @@ void nvfp4_shutdown(void);
  * All device buffers are caller-owned and must be 16-byte aligned (else
  * NVFP4_ERR_MISALIGNED).  The call is asynchronous: it returns after the
  * kernels are enqueued; device-side faults surface at the caller's next
- * synchronisation.  Split-K paths use a library-owned workspace per
+ * synchronisation.  The tile path needs each packed code buffer to stay
+ * below 2 GiB (else NVFP4_ERR_UNSUPPORTED).  Split-K paths use a
+ * library-owned workspace per
  * (device, stream) pair, allocated on the first call that needs it (the
  * only allocation the library makes); calls on one stream are ordered, calls
  * on different streams use different workspaces.  Launch failures return

@@ -40,7 +40,7 @@ def test_status_strings():
 def test_packed_size(rows, K):
     cb, sb = nv.packed_size(rows, K)
     Rp = -(-rows // 16) * 16
-    Kp = -(-K // 64) * 64
+    Kp = -(-K // 128) * 128
     assert cb == Rp * Kp // 2 and sb == Rp * Kp // 16
 
 
@@ -60,14 +60,14 @@ def test_pack_roundtrip_and_layout(rows, K):
     c2, s2 = nv.unpack(pc, ps, rows, K)
     assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
     # layout: panel p, row r holds canonical bytes [32p, 32p+32) and scales [4p, 4p+4)
-    Rp, P = -(-rows // 16) * 16, -(-K // 64)
+    Rp, P = -(-rows // 16) * 16, 2 * -(-K // 128)
     pc3 = pc.reshape(P, Rp, 32)
     ps3 = ps.reshape(P, Rp, 4)
     for p in range(P):
-        n = min(32, K // 2 - 32 * p)
+        n = max(0, min(32, K // 2 - 32 * p))
         assert np.array_equal(pc3[p, :rows, :n], codes[:, 32 * p:32 * p + n])
         assert not pc3[p, :rows, n:].any() and not pc3[p, rows:].any()
-        ns = min(4, K // 16 - 4 * p)
+        ns = max(0, min(4, K // 16 - 4 * p))
         assert np.array_equal(ps3[p, :rows, :ns], scales[:, 4 * p:4 * p + ns])
         assert not ps3[p, :rows, ns:].any() and not ps3[p, rows:].any()
 
