@@ -90,6 +90,20 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
+// Wait until at most `steps` (0 .. 6, wave-uniform) groups of L vector-memory
+// instructions are in flight.
+template <int L>
+__device__ __forceinline__ void wait_steps(int steps) {
+    switch (steps) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<L>(); break;
+        case 2: wait_vmcnt<(2 * L < 64 ? 2 * L : 0)>(); break;
+        case 3: wait_vmcnt<(3 * L < 64 ? 3 * L : 0)>(); break;
+        case 4: wait_vmcnt<(4 * L < 64 ? 4 * L : 0)>(); break;
+        case 5: wait_vmcnt<(5 * L < 64 ? 5 * L : 0)>(); break;
+        default: wait_vmcnt<(6 * L < 64 ? 6 * L : 0)>(); break;
+    }
+}
 
 typedef __attribute__((address_space(3))) uint8_t* lds_u8;
 
@@ -128,12 +142,12 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 //
 // Workgroup: 256 threads = 4 waves in a 2 x 2 grid; workgroup tile BM x BN,
 // wave tile (BM/2) x (BN/2) made of 32 x 32 MFMA blocks
-// (v_mfma_f32_32x32x16_f16).  K advances in steps of two 64-element panels.
+// (v_mfma_f32_32x32x16_f16).  K advances one 64-element panel at a time.
 //
-// HBM -> LDS: each step's packed codes (4 bits/element) and raw E4M3 scale
+// HBM -> LDS: each panel's packed codes (4 bits/element) and raw E4M3 scale
 // bytes are copied with direct-to-LDS loads (16 and 4 bytes per lane) into a
-// ring of NS stage buffers, NS-1 steps ahead of the step being multiplied, so
-// several steps of loads are always in flight and no VGPRs are spent on
+// ring of NS stage buffers, NS-1 panels ahead of the panel being multiplied,
+// so several panels of loads are always in flight and no VGPRs are spent on
 // staging.
 //
 // LDS code layout of one operand and panel: rows in groups of 32; within a
@@ -141,15 +155,21 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // (one 1 KB direct load per group):
 //   offset(row, half) = (row / 32) * 1024 + half * 512 + (row % 32) * 16.
 // MFMA lane l reads row l % 32, half l / 32 as one 16-byte read, so the lanes
-// of each LDS phase touch consecutive bytes.  Scales: [panel][row][4 bytes].
+// of each LDS phase touch consecutive bytes.  Scales: the rows' 4-byte scale
+// words in (half tile, row within a 32-row block, block) order, so that a
+// lane gets the words of all its row blocks with one read.
 //
 // Decode and MFMA are software-pipelined: the operands of sub-step s+1 are
-// decoded while the 16 MFMAs of sub-step s run, with the instruction
-// scheduler told to alternate one MFMA and a few VALU instructions.
+// decoded while the MFMAs of sub-step s run (the scheduler is told to
+// alternate one MFMA and a few VALU instructions), and the next panel's LDS
+// reads are issued a whole panel ahead, so a panel's first sub-step never
+// waits for LDS.  One barrier per panel both publishes the next panel's
+// loads and hands the previous panel's buffer back to the loads.
 //
 // Rows past the padded operand are clamped to its last row (their results
-// are never stored).  The packed K is a whole number of steps (the packer
-// pads with zeros), so every step holds two panels.
+// are never stored).  The packed K is a whole number of 128-element steps
+// (the packer pads with zeros), so every workgroup runs an even number of
+// panels.
 //
 // Split-K (split_k > 1): the K steps are divided into split_k contiguous
 // ranges; each workgroup publishes its FP32 tile to the workspace, and the
@@ -160,21 +180,18 @@ template <int BM, int BN, int NS, bool SPLIT>
 __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     constexpr int MI = BM / 64;  // 32-row blocks per wave
     constexpr int NI = BN / 64;  // 32-column blocks per wave
-    constexpr int A_CODE = 2 * BM * 32;
-    constexpr int B_CODE = 2 * BN * 32;
-    constexpr int A_SC = 2 * BM * 4;
-    constexpr int B_SC = 2 * BN * 4;
-    constexpr int OFF_B = A_CODE;
-    constexpr int OFF_SA = A_CODE + B_CODE;
-    constexpr int OFF_SB = OFF_SA + A_SC;
-    constexpr int STAGE = OFF_SB + B_SC;
-    constexpr int A_CCH = 2 * BM / 32;           // 1 KB code chunks of A per step
-    constexpr int CCH = A_CCH + 2 * BN / 32;
-    constexpr int A_SCH = 2 * BM / 64;           // 256 B scale chunks of A per step
-    constexpr int SCH = A_SCH + 2 * BN / 64;
-    static_assert(CCH % 4 == 0 && SCH % 4 == 0, "chunks must split evenly over 4 waves");
-    constexpr int LPS = CCH / 4 + SCH / 4;       // direct loads per wave per step
-    static_assert(NS >= 3 && NS <= 4 && (NS - 2) * LPS < 64, "pipeline depth");
+    constexpr int OFF_B = BM * 32;
+    constexpr int OFF_SA = OFF_B + BN * 32;
+    constexpr int OFF_SB = OFF_SA + BM * 4;
+    constexpr int STAGE = OFF_SB + BN * 4;
+    constexpr int A_CCH = BM / 32;               // 1 KB code chunks of A per panel
+    constexpr int CCH = A_CCH + BN / 32;
+    constexpr int A_SCH = BM / 64;               // 256 B scale chunks of A per panel
+    constexpr int SCH = A_SCH + BN / 64;
+    constexpr int CPW = (CCH + 3) / 4;           // code chunks per wave
+    constexpr int SPW = (SCH + 3) / 4;           // scale chunks per wave
+    constexpr int LPS = CPW + SPW;               // direct loads per wave per panel
+    static_assert(NS >= 3 && NS <= 8 && (NS - 2) * LPS < 64, "pipeline depth");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
 
@@ -202,65 +219,68 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int nst = a.P / 2;
-    const int st0 = (int)((int64_t)z * nst / S);
-    const int st1 = (int)((int64_t)(z + 1) * nst / S);
+    const int p0 = 2 * (int)((int64_t)z * nst / S);
+    const int p1 = 2 * (int)((int64_t)(z + 1) * nst / S);
 
     const uint32_t lds0 = lds_addr(lds);
 
-    // Direct-load plan of this wave (constant over K steps): for each of its
-    // code and scale chunks, the lane's byte offset inside a panel and the
-    // chunk's place in the stage buffer.
+    // Direct-load plan of this wave (constant over panels): for each of its
+    // code and scale chunks, the lane's byte offset inside a panel.  When an
+    // operand has fewer chunks than there are waves, chunks are issued twice
+    // (same bytes to the same place), so every wave issues LPS loads.
     const __amdgpu_buffer_rsrc_t rac = make_rsrc(a.a_codes, (uint32_t)a.P * a.Mp * 32u);
     const __amdgpu_buffer_rsrc_t rbc = make_rsrc(a.b_codes, (uint32_t)a.P * a.Np * 32u);
     const __amdgpu_buffer_rsrc_t ras = make_rsrc(a.a_scales, (uint32_t)a.P * a.Mp * 4u);
     const __amdgpu_buffer_rsrc_t rbs = make_rsrc(a.b_scales, (uint32_t)a.P * a.Np * 4u);
-    uint32_t c_voff[CCH / 4], s_voff[SCH / 4];
+    uint32_t c_voff[CPW], s_voff[SPW];
 #pragma unroll
-    for (int i = 0; i < CCH / 4; ++i) {
-        const int k = wave + 4 * i;
+    for (int i = 0; i < CPW; ++i) {
+        const int k = (wave + 4 * i) % CCH;
         const bool isA = k < A_CCH;
-        const int R = isA ? BM : BN;
-        const int grp = (isA ? k : k - A_CCH) % (R / 32);
+        const int grp = isA ? k : k - A_CCH;
         const int row = min((isA ? m0 : n0) + grp * 32 + q, (isA ? a.Mp : a.Np) - 1);
         c_voff[i] = (uint32_t)row * 32u + (uint32_t)h * 16u;
     }
 #pragma unroll
-    for (int i = 0; i < SCH / 4; ++i) {
-        const int k = wave + 4 * i;
+    for (int i = 0; i < SPW; ++i) {
+        const int k = (wave + 4 * i) % SCH;
         const bool isA = k < A_SCH;
         const int R = isA ? BM : BN;
-        const int c = (isA ? k : k - A_SCH) % (R / 64);
-        const int row = min((isA ? m0 : n0) + c * 64 + lane, (isA ? a.Mp : a.Np) - 1);
+        const int G = isA ? MI : NI;  // 32-row blocks per wave along this operand
+        const int c = isA ? k : k - A_SCH;
+        // LDS slot c*64 + lane holds the scales of tile row r: slots are in
+        // (half of the tile, row within its 32-row block, block) order.
+        const int slot = c * 64 + lane;
+        const int half = slot / (R / 2), sr = slot % (R / 2);
+        const int r = half * (R / 2) + (sr % G) * 32 + sr / G;
+        const int row = min((isA ? m0 : n0) + r, (isA ? a.Mp : a.Np) - 1);
         s_voff[i] = (uint32_t)row * 4u;
     }
 
-    // Issue the direct loads of step st into stage buffer sb (LPS per wave).
-    auto issue = [&](int st, int sb) {
+    // Issue direct load d (0 <= d < LPS) of panel p into stage buffer sb.
+    // Panels past the end are clamped to the last panel: those buffers are
+    // never read, and every panel then carries exactly LPS loads per wave.
+    auto issue_one = [&](int p, int sb, int d) {
         const uint32_t b = lds0 + (uint32_t)(sb * STAGE);
-#pragma unroll
-        for (int i = 0; i < CCH / 4; ++i) {
-            const int k = wave + 4 * i;
+        const uint32_t pc = (uint32_t)min(p, a.P - 1);
+        if (d < CPW) {
+            const int k = (wave + 4 * d) % CCH;
             const bool isA = k < A_CCH;
-            const int R = isA ? BM : BN;
-            const int kk = isA ? k : k - A_CCH;
-            const int pl = kk / (R / 32), grp = kk % (R / 32);
-            const uint32_t panel = (uint32_t)(2 * st + pl);
-            const uint32_t soff = panel * (uint32_t)(isA ? a.Mp : a.Np) * 32u;
-            dma16(isA ? rac : rbc, c_voff[i], soff,
-                  b + (uint32_t)((isA ? 0 : OFF_B) + (pl * (R / 32) + grp) * 1024));
-        }
-#pragma unroll
-        for (int i = 0; i < SCH / 4; ++i) {
-            const int k = wave + 4 * i;
+            const int grp = isA ? k : k - A_CCH;
+            const uint32_t soff = pc * (uint32_t)(isA ? a.Mp : a.Np) * 32u;
+            dma16(isA ? rac : rbc, c_voff[d], soff, b + (uint32_t)((isA ? 0 : OFF_B) + grp * 1024));
+        } else {
+            const int i = d - CPW;
+            const int k = (wave + 4 * i) % SCH;
             const bool isA = k < A_SCH;
-            const int R = isA ? BM : BN;
-            const int kk = isA ? k : k - A_SCH;
-            const int pl = kk / (R / 64), c = kk % (R / 64);
-            const uint32_t panel = (uint32_t)(2 * st + pl);
-            const uint32_t soff = panel * (uint32_t)(isA ? a.Mp : a.Np) * 4u;
-            dma4(isA ? ras : rbs, s_voff[i], soff,
-                 b + (uint32_t)((isA ? OFF_SA : OFF_SB) + (pl * R + c * 64) * 4));
+            const int c = isA ? k : k - A_SCH;
+            const uint32_t soff = pc * (uint32_t)(isA ? a.Mp : a.Np) * 4u;
+            dma4(isA ? ras : rbs, s_voff[i], soff, b + (uint32_t)((isA ? OFF_SA : OFF_SB) + c * 256));
         }
+    };
+    auto issue = [&](int p, int sb) {
+#pragma unroll
+        for (int d = 0; d < LPS; ++d) issue_one(p, sb, d);
     };
 
     f16v acc[MI][NI];
@@ -271,78 +291,98 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // Multiply one step (two panels) held in buffer b.
-    auto compute = [&](const uint8_t* b) {
+    // Operand registers of one panel: raw codes (one 16-byte LDS read per
+    // 32-row block: words 0..3 feed the four MFMA sub-steps) and the two
+    // block scales of the lane's half, widened to fp16.
+    struct PanelRegs {
+        uint4 ca[MI], cb[NI];
+        h2 sa[MI], sb[NI];
+    };
+    auto read_words = [&](const uint8_t* p, uint32_t (&w)[4], int n) {
+        if (n == 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(p);
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else if (n == 2) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            w[0] = v.x; w[1] = v.y;
+        } else {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        }
+    };
+    auto read_panel = [&](const uint8_t* b, PanelRegs& r) {
+        uint32_t wa[4], wb[4];
+        read_words(b + OFF_SA + (wm * (BM / 2) + q * MI) * 4, wa, MI);
+        read_words(b + OFF_SB + (wn * (BN / 2) + q * NI) * 4, wb, NI);
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl) {
-            uint4 ca[MI], cb[NI];
-            h2 sa[MI], sb[NI];
+        for (int i = 0; i < MI; ++i) {
+            r.ca[i] = *reinterpret_cast<const uint4*>(b + (wm * MI + i) * 1024 + h * 512 + q * 16);
+            r.sa[i] = e4m3x2_lo(wa[i] >> (16 * h));
+        }
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int g = wm * MI + i;
-                ca[i] = *reinterpret_cast<const uint4*>(b + pl * BM * 32 + g * 1024 + h * 512 + q * 16);
-                const uint32_t raw = *reinterpret_cast<const uint16_t*>(
-                    b + OFF_SA + (pl * BM + g * 32 + q) * 4 + h * 2);
-                sa[i] = e4m3x2_lo(raw);
-            }
+        for (int j = 0; j < NI; ++j) {
+            r.cb[j] = *reinterpret_cast<const uint4*>(b + OFF_B + (wn * NI + j) * 1024 + h * 512 + q * 16);
+            r.sb[j] = e4m3x2_lo(wb[j] >> (16 * h));
+        }
+    };
+    h8 av[2][MI], bv[2][NI];  // decoded operands of the current / next sub-step
+    auto decode = [&](const PanelRegs& r, int s, h8 (&ao)[MI], h8 (&bo)[NI]) {
 #pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int g = wn * NI + j;
-                cb[j] = *reinterpret_cast<const uint4*>(b + OFF_B + pl * BN * 32 + g * 1024 + h * 512 + q * 16);
-                const uint32_t raw = *reinterpret_cast<const uint16_t*>(
-                    b + OFF_SB + (pl * BN + g * 32 + q) * 4 + h * 2);
-                sb[j] = e4m3x2_lo(raw);
-            }
-            h8 av[2][MI], bv[2][NI];
+        for (int i = 0; i < MI; ++i) ao[i] = decode8(word_of(r.ca[i], s), s < 2 ? r.sa[i][0] : r.sa[i][1]);
 #pragma unroll
-            for (int i = 0; i < MI; ++i) av[0][i] = decode8(word_of(ca[i], 0), sa[i][0]);
+        for (int j = 0; j < NI; ++j) bo[j] = decode8(word_of(r.cb[j], s), s < 2 ? r.sb[j][0] : r.sb[j][1]);
+    };
+    // The four sub-steps of panel `cur` (its sub-step 0 is already decoded
+    // in av/bv[0]); the decode of each following sub-step -- the last one
+    // being sub-step 0 of panel `nxt` -- runs under the MFMAs, and so do the
+    // direct loads of panel `lp` (spread over the sub-steps).
+    auto run_panel = [&](const PanelRegs& cur, const PanelRegs& nxt, int lp, int lsb) {
 #pragma unroll
-            for (int j = 0; j < NI; ++j) bv[0][j] = decode8(word_of(cb[j], 0), sb[j][0]);
+        for (int s = 0; s < 4; ++s) {
+            const int c = s & 1, n = c ^ 1;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int cur = s & 1, nxt = cur ^ 1;
-                if (s < 3) {
+            for (int d = s * LPS / 4; d < (s + 1) * LPS / 4; ++d) issue_one(lp, lsb, d);
+            if (s < 3) decode(cur, s + 1, av[n], bv[n]);
+            else decode(nxt, 0, av[n], bv[n]);
 #pragma unroll
-                    for (int i = 0; i < MI; ++i)
-                        av[nxt][i] = decode8(word_of(ca[i], s + 1), (s + 1) < 2 ? sa[i][0] : sa[i][1]);
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
-                    for (int j = 0; j < NI; ++j)
-                        bv[nxt][j] = decode8(word_of(cb[j], s + 1), (s + 1) < 2 ? sb[j][0] : sb[j][1]);
-                }
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[c][i], bv[c][j], acc[i][j], 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int j = 0; j < NI; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j],
-                                                                           acc[i][j], 0, 0, 0);
-                if (s < 3) {
-#pragma unroll
-                    for (int m = 0; m < MI * NI; ++m) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, (8 * (MI + NI) + MI * NI - 1) / (MI * NI), 0);
-                    }
-                }
+            for (int m = 0; m < MI * NI; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, (8 * (MI + NI) + MI * NI - 1) / (MI * NI), 0);
             }
         }
     };
+    // One panel: wait until panel p+1 is resident (loads of panels p+2 ..
+    // p+NS-2 may still be in flight), barrier (everyone is past panel p-1,
+    // whose buffer now takes panel p+NS-1), read panel p+1 (a stale buffer
+    // after the last panel; those values go unused), multiply panel p while
+    // the loads of panel p+NS-1 are issued.
+    auto step = [&](int p, const PanelRegs& cur, PanelRegs& nxt) {
+        wait_steps<LPS>(NS - 3);
+        wg_barrier();
+        read_panel(lds + ((p + 1 - p0) % NS) * STAGE, nxt);
+        run_panel(cur, nxt, p + NS - 1, (p + NS - 1 - p0) % NS);
+    };
 
-    // Prologue: NS-1 steps in flight.
+    // Prologue: NS-1 panels in flight; wait for the first and decode its
+    // first sub-step.
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u)
-        if (st0 + u < st1) issue(st0 + u, u);
-
-    int sb = 0;  // stage buffer of step st
-    for (int st = st0; st < st1; ++st) {
-        // Loads issued after step st's: steps st+1 .. min(st+NS-2, st1-1).
-        const int later = min(NS - 2, st1 - 1 - st);
-        if (later >= 2) wait_vmcnt<2 * LPS>();
-        else if (later == 1) wait_vmcnt<LPS>();
-        else wait_vmcnt<0>();
-        wg_barrier();  // step st is in LDS; step st-1's buffer is free
-        if (st + NS - 1 < st1) issue(st + NS - 1, sb == 0 ? NS - 1 : sb - 1);
-        compute(lds + sb * STAGE);
-        sb = sb == NS - 1 ? 0 : sb + 1;
+    for (int u = 0; u < NS - 1; ++u) issue(p0 + u, u);
+    PanelRegs r0, r1;
+    if (p0 < p1) {
+        wait_steps<LPS>(NS - 2);
+        wg_barrier();
+        read_panel(lds, r0);
+        decode(r0, 0, av[0], bv[0]);
     }
+    for (int p = p0; p < p1; p += 2) {  // p1 - p0 is even
+        step(p, r0, r1);
+        step(p + 1, r1, r0);
+    }
+    wait_vmcnt<0>();  // drain the look-ahead loads before the LDS is released
 
     // Split-K: publish the partial tile; the last arrival reduces in split order.
     if (SPLIT) {
@@ -539,16 +579,16 @@ hipError_t launch_tile(int cfg, const GemmArgs& a, hipStream_t stream) {
     const bool split = a.split_k > 1;
     switch (cfg) {
         case TILE_256x256:
-            if (split) hipLaunchKernelGGL((tile_kernel<256, 256, 4, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((tile_kernel<256, 256, 4, false>), grid, block, 0, stream, a);
+            if (split) hipLaunchKernelGGL((tile_kernel<256, 256, 8, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((tile_kernel<256, 256, 8, false>), grid, block, 0, stream, a);
             break;
         case TILE_128x128:
-            if (split) hipLaunchKernelGGL((tile_kernel<128, 128, 4, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((tile_kernel<128, 128, 4, false>), grid, block, 0, stream, a);
+            if (split) hipLaunchKernelGGL((tile_kernel<128, 128, 8, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((tile_kernel<128, 128, 8, false>), grid, block, 0, stream, a);
             break;
         default:
-            if (split) hipLaunchKernelGGL((tile_kernel<64, 64, 4, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((tile_kernel<64, 64, 4, false>), grid, block, 0, stream, a);
+            if (split) hipLaunchKernelGGL((tile_kernel<64, 64, 8, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((tile_kernel<64, 64, 8, false>), grid, block, 0, stream, a);
             break;
     }
     return hipGetLastError();
