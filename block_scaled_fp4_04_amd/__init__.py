@@ -32,6 +32,7 @@ ERR_ALLOC = 5
 PATH_AUTO = 0
 PATH_TILE = 1
 PATH_SKINNY = 2
+PATH_WSPLIT = 3
 
 EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_pack",
            "nvfp4_unpack", "nvfp4_init", "nvfp4_shutdown", "nvfp4_gemm",

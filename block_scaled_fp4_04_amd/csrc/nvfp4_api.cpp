@@ -107,7 +107,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int path, int split_req) {
     Plan p{};
     const int64_t P = num_panels(K);
     const int steps = (int)(P / 2);
-    if (path == NVFP4_PATH_AUTO) path = (M <= 16) ? NVFP4_PATH_SKINNY : NVFP4_PATH_TILE;
+    if (path == NVFP4_PATH_AUTO && M <= 16) path = NVFP4_PATH_SKINNY;
     p.path = path;
     if (path == NVFP4_PATH_SKINNY) {
         // One workgroup of kSkinnyWaves waves per 16 output columns covers the
@@ -126,6 +126,33 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int path, int split_req) {
         p.split_k = s < 1 ? 1 : s;
         p.tiles_m = 1;
         p.tiles_n = (int)groups;
+        return p;
+    }
+    if (path == NVFP4_PATH_AUTO) {
+        // Large shapes whose 256 x 256 tiles nearly fill the machine use the
+        // LDS-fed tile kernel; the rest use the kernel whose waves split K.
+        const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+        path = t256 >= (3 * kCUs) / 4 ? NVFP4_PATH_TILE : NVFP4_PATH_WSPLIT;
+        p.path = path;
+    }
+    if (path == NVFP4_PATH_WSPLIT) {
+        const int cfg = WSPLIT_64x64;
+        const TileShape s = wsplit_shape(cfg);
+        p.cfg = cfg;
+        p.tiles_m = (int)((M + s.bm - 1) / s.bm);
+        p.tiles_n = (int)((N + s.bn - 1) / s.bn);
+        const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+        int sk = split_req;
+        if (sk <= 0) {
+            // A workgroup (8 waves, ~236 VGPRs each) occupies a whole CU, so
+            // split K across workgroups only while every workgroup still has
+            // a CU of its own (a second round of workgroups costs more than
+            // the split saves), keeping at least one panel per wave.
+            sk = 1;
+            while (tiles * (sk + 1) <= kCUs && (int64_t)(sk + 1) * 8 <= 2 * steps) ++sk;
+        }
+        if (sk > steps) sk = steps;
+        p.split_k = sk < 1 ? 1 : sk;
         return p;
     }
     // Tile path: largest tile that still gives a reasonably full machine,
@@ -158,7 +185,7 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     if (!a_packed || !a_scales || !b_packed || !b_scales || !out) return NVFP4_ERR_INVALID_VALUE;
     if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim) return NVFP4_ERR_INVALID_VALUE;
     if (!valid_rows_k(1, K)) return NVFP4_ERR_INVALID_VALUE;
-    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_SKINNY || split_k < 0)
+    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_WSPLIT || split_k < 0)
         return NVFP4_ERR_INVALID_VALUE;
     if (!aligned16(a_packed) || !aligned16(a_scales) || !aligned16(b_packed) ||
         !aligned16(b_scales) || !aligned16(out))
@@ -195,8 +222,9 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     a.tiles_m = plan.tiles_m;
     a.tiles_n = plan.tiles_n;
 
-    const size_t floats = plan.path == NVFP4_PATH_SKINNY ? skinny_partial_floats(a)
-                                                         : tile_partial_floats(plan.cfg, a);
+    const size_t floats = plan.path == NVFP4_PATH_SKINNY   ? skinny_partial_floats(a)
+                          : plan.path == NVFP4_PATH_WSPLIT ? wsplit_partial_floats(plan.cfg, a)
+                                                           : tile_partial_floats(plan.cfg, a);
     const size_t counters =
         plan.path == NVFP4_PATH_SKINNY ? skinny_counters(a) : tile_counters(plan.cfg, a);
     if (floats || counters) {
@@ -207,8 +235,9 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
         a.counters = ws->counters;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e =
-        plan.path == NVFP4_PATH_SKINNY ? launch_skinny(a, s) : launch_tile(plan.cfg, a, s);
+    const hipError_t e = plan.path == NVFP4_PATH_SKINNY   ? launch_skinny(a, s)
+                         : plan.path == NVFP4_PATH_WSPLIT ? launch_wsplit(plan.cfg, a, s)
+                                                          : launch_tile(plan.cfg, a, s);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
@@ -331,7 +360,9 @@ int nvfp4_plan(int64_t M, int64_t N, int64_t K, int* path, int* split_k, int* ti
     const Plan p = make_plan(M, N, K, NVFP4_PATH_AUTO, 0);
     if (path) *path = p.path;
     if (split_k) *split_k = p.split_k;
-    const TileShape s = p.path == NVFP4_PATH_SKINNY ? TileShape{16, 16} : tile_shape(p.cfg);
+    const TileShape s = p.path == NVFP4_PATH_SKINNY   ? TileShape{16, 16}
+                        : p.path == NVFP4_PATH_WSPLIT ? wsplit_shape(p.cfg)
+                                                      : tile_shape(p.cfg);
     if (tile_m) *tile_m = s.bm;
     if (tile_n) *tile_n = s.bn;
     return NVFP4_OK;

@@ -53,7 +53,15 @@ size_t tile_counters(int cfg, const GemmArgs& a);
 size_t skinny_partial_floats(const GemmArgs& a);
 size_t skinny_counters(const GemmArgs& a);
 
+// Mid-size kernel configurations (waves split K inside a workgroup).
+enum WsplitConfig { WSPLIT_64x64 = 0, WSPLIT_128x64 = 1 };
+inline TileShape wsplit_shape(int cfg) {
+    return cfg == WSPLIT_64x64 ? TileShape{64, 64} : TileShape{128, 64};
+}
+size_t wsplit_partial_floats(int cfg, const GemmArgs& a);
+
 hipError_t launch_tile(int cfg, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace nvfp4

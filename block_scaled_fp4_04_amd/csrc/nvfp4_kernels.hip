@@ -555,6 +555,191 @@ __global__ void __launch_bounds__(WAVES * 64) skinny_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Mid-size kernel: the waves of a workgroup split K.
+//
+// For GEMMs with a few hundred rows the large-M kernel has too few tiles to
+// fill the machine without splitting K across workgroups, and small wave
+// tiles make every operand block be decoded by several waves.  Here each of
+// the WAVES waves owns the whole BM x BN tile (BM/32 x BN/32 blocks of
+// v_mfma_f32_32x32x16_f16) over every WAVES-th panel of the workgroup's K
+// range, so each element is decoded exactly once per tile and the waves
+// share nothing until the end: no LDS staging and no barriers in the main
+// loop.  Lane l of a 32-row block reads row l % 32, half l / 32 of a panel
+// (16 bytes of codes, 2 bytes of scales) straight from HBM -- a wave's
+// reads of one block are 1 KB contiguous -- with DEPTH panels of loads in
+// flight.  At the end the wave tiles are added in LDS in wave order, then
+// (split_k > 1) across workgroups by the last arrival in split order.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WAVES, bool SPLIT>
+__global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
+    constexpr int MI = BM / 32;
+    constexpr int NI = BN / 32;
+    constexpr int DEPTH = 4;  // panels of loads in flight per wave (ring of DEPTH slots)
+    __shared__ __attribute__((aligned(16))) float red[WAVES][MI * NI * 16][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int q = lane & 31, h = lane >> 5;
+
+    const int S = SPLIT ? a.split_k : 1;
+    int bid = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int z = bid % S;
+    const int t = bid / S;
+    const int tm = t / a.tiles_n, tn = t % a.tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int nst = a.P / 2;
+    const int p0 = 2 * (int)((int64_t)z * nst / S);
+    const int p1 = 2 * (int)((int64_t)(z + 1) * nst / S);
+    // this wave's panels: p0 + wave, p0 + wave + WAVES, ...
+    const int count = (p1 - p0 > wave) ? (p1 - p0 - wave + WAVES - 1) / WAVES : 0;
+
+    // lane byte offsets of its rows inside one panel (rows clamped to the
+    // padded operand; their results are not stored)
+    int64_t a_off[MI], b_off[NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a_off[i] = min(m0 + i * 32 + q, a.Mp - 1);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) b_off[j] = min(n0 + j * 32 + q, a.Np - 1);
+
+    struct Regs {
+        uint4 ca[MI], cb[NI];
+        uint32_t sa[MI], sb[NI];
+    };
+    auto load = [&](int k, Regs& r) {  // k-th panel of this wave
+        if (k < count) {
+            const int64_t panel = p0 + wave + (int64_t)k * WAVES;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int64_t row = panel * a.Mp + a_off[i];
+                r.ca[i] = *reinterpret_cast<const uint4*>(a.a_codes + row * 32 + h * 16);
+                r.sa[i] = *reinterpret_cast<const uint16_t*>(a.a_scales + row * 4 + h * 2);
+            }
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const int64_t row = panel * a.Np + b_off[j];
+                r.cb[j] = *reinterpret_cast<const uint4*>(a.b_codes + row * 32 + h * 16);
+                r.sb[j] = *reinterpret_cast<const uint16_t*>(a.b_scales + row * 4 + h * 2);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < MI; ++i) { r.ca[i] = uint4{0u, 0u, 0u, 0u}; r.sa[i] = 0u; }
+#pragma unroll
+            for (int j = 0; j < NI; ++j) { r.cb[j] = uint4{0u, 0u, 0u, 0u}; r.sb[j] = 0u; }
+        }
+    };
+
+    f16v acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    auto compute = [&](const Regs& r) {
+        h2 sa[MI], sb[NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) sa[i] = e4m3x2_lo(r.sa[i]);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) sb[j] = e4m3x2_lo(r.sb[j]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            h8 av[MI], bv[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) av[i] = decode8(word_of(r.ca[i], s), s < 2 ? sa[i][0] : sa[i][1]);
+#pragma unroll
+            for (int j = 0; j < NI; ++j) bv[j] = decode8(word_of(r.cb[j], s), s < 2 ? sb[j][0] : sb[j][1]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    Regs ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load(d, ring[d]);
+    for (int k = 0; k < count; k += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            compute(ring[d]);            // panel k + d (zeros past the end)
+            load(k + d + DEPTH, ring[d]);
+        }
+    }
+
+    // Add the wave tiles in wave order.
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) red[wave][(i * NI + j) * 16 + v][lane] = acc[i][j][v];
+    __syncthreads();
+    constexpr int IDX = MI * NI * 16;  // accumulator slots per lane
+    constexpr int PER = (IDX + WAVES - 1) / WAVES;
+    float sum[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int idx = wave + u * WAVES;
+        float x = 0.0f;
+        if (idx < IDX) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) x += red[w][idx][lane];
+        }
+        sum[u] = x;
+    }
+
+    if (SPLIT) {
+        // publish this workgroup's tile (slot order idx * 64 + lane); the
+        // last arrival adds the S partial tiles in split order
+        float* mine = a.partials + ((int64_t)t * S + z) * (BM * BN);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = wave + u * WAVES;
+            if (idx < IDX) publish(mine + idx * 64 + lane, sum[u]);
+        }
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t old = arrive(a.counters + t);
+            s_last = (old == (uint32_t)(S - 1));
+            if (s_last) reset_counter(a.counters + t);  // all splits arrived
+        }
+        __syncthreads();
+        if (!s_last) return;
+        const float* all = a.partials + (int64_t)t * S * (BM * BN);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) sum[u] = 0.0f;
+        for (int zz = 0; zz < S; ++zz) {  // one batch of independent loads per split
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int idx = wave + u * WAVES;
+                if (idx < IDX) sum[u] += fetch(all + (int64_t)zz * (BM * BN) + idx * 64 + lane);
+            }
+        }
+    }
+
+    // Epilogue: slot idx = (i * NI + j) * 16 + v of lane l is row
+    // i*32 + 8*(v/4) + 4*(l/32) + v%4, column j*32 + l%32 of the tile.
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int idx = wave + u * WAVES;
+        if (idx >= IDX) continue;
+        const int v = idx & 15, ij = idx >> 4;
+        const int i = ij / NI, j = ij % NI;
+        const int row = m0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int col = n0 + j * 32 + q;
+        if (row < a.M && col < a.N) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * sum[u]);
+    }
+}
+
 }  // namespace
 
 size_t tile_partial_floats(int cfg, const GemmArgs& a) {
@@ -589,6 +774,28 @@ hipError_t launch_tile(int cfg, const GemmArgs& a, hipStream_t stream) {
         default:
             if (split) hipLaunchKernelGGL((tile_kernel<64, 64, 8, true>), grid, block, 0, stream, a);
             else hipLaunchKernelGGL((tile_kernel<64, 64, 8, false>), grid, block, 0, stream, a);
+            break;
+    }
+    return hipGetLastError();
+}
+
+size_t wsplit_partial_floats(int cfg, const GemmArgs& a) {
+    if (a.split_k <= 1) return 0;
+    const TileShape s = wsplit_shape(cfg);
+    return (size_t)a.tiles_m * a.tiles_n * a.split_k * s.bm * s.bn;
+}
+
+hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.split_k));
+    const bool split = a.split_k > 1;
+    switch (cfg) {
+        case WSPLIT_64x64:
+            if (split) hipLaunchKernelGGL((wsplit_kernel<64, 64, 8, true>), grid, dim3(512), 0, stream, a);
+            else hipLaunchKernelGGL((wsplit_kernel<64, 64, 8, false>), grid, dim3(512), 0, stream, a);
+            break;
+        default:  // WSPLIT_128x64
+            if (split) hipLaunchKernelGGL((wsplit_kernel<128, 64, 4, true>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((wsplit_kernel<128, 64, 4, false>), grid, dim3(256), 0, stream, a);
             break;
     }
     return hipGetLastError();

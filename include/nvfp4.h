@@ -57,8 +57,9 @@ typedef enum nvfp4_status {
 /* Kernel paths for nvfp4_gemm_with_path. */
 enum {
     NVFP4_PATH_AUTO = 0,   /* library's choice from M, N, K */
-    NVFP4_PATH_TILE = 1,   /* large-M MFMA tile kernel (LDS double buffer) */
-    NVFP4_PATH_SKINNY = 2  /* M <= 16: split-K MFMA kernel for decode shapes */
+    NVFP4_PATH_TILE = 1,   /* large shapes: MFMA tiles fed through an LDS ring */
+    NVFP4_PATH_SKINNY = 2, /* M <= 16: decode shapes, one wave per K range */
+    NVFP4_PATH_WSPLIT = 3  /* mid-size shapes: the waves of a workgroup split K */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -124,7 +125,7 @@ int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void*
                          const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
                          int64_t K, int path, int split_k, void* stream);
 
-/* The path (NVFP4_PATH_TILE / NVFP4_PATH_SKINNY) and split-K factor that
+/* The path (NVFP4_PATH_TILE / _SKINNY / _WSPLIT) and split-K factor that
  * nvfp4_gemm would use for a shape; also the tile sizes.  Any output pointer
  * may be NULL.  Host-only, no device work. */
 int nvfp4_plan(int64_t M, int64_t N, int64_t K, int* path, int* split_k, int* tile_m,

@@ -58,7 +58,7 @@ def check_full(o, ops, gpu_bits, label, min_exact=0.999):
 
 # ------------------------------------------------------------ decode and layout
 
-@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_SKINNY])
+@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_WSPLIT, nv.PATH_SKINNY])
 def test_decode_exhaustive(o, path):
     """Every E4M3 scale byte times every E2M1 code, through the GEMM: one
     operand has a single 1.0 at k=0 with scale s in row s, the other has code
@@ -71,7 +71,7 @@ def test_decode_exhaustive(o, path):
     cd_rows = np.zeros((16, K // 2), np.uint8)
     cd_rows[:, 0] = np.arange(16, dtype=np.uint8)          # code c at k = 0 in row c
     cd_scales = np.full((16, K // 16), 0x38, np.uint8)
-    if path == nv.PATH_TILE:
+    if path != nv.PATH_SKINNY:
         ops = synth.Operands(sc_rows, sc_scales, cd_rows, cd_scales, 1.0, 256, 16, K)
     else:   # skinny: M <= 16, so the code rows are A
         ops = synth.Operands(cd_rows, cd_scales, sc_rows, sc_scales, 1.0, 16, 256, K)
@@ -85,7 +85,7 @@ def test_decode_exhaustive(o, path):
     assert np.all(same), np.argwhere(~same)[:10]
 
 
-@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_SKINNY])
+@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_WSPLIT, nv.PATH_SKINNY])
 def test_onehot_positions(o, path):
     """One non-zero product at a time, at positions across tile, panel and
     scale-block boundaries: pins nibble order, K slots, scale blocks, the
@@ -161,7 +161,7 @@ EDGE_SHAPES = [(1, 1, 16), (1, 17, 32), (2, 33, 48), (15, 16, 80), (16, 255, 616
 @pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
 def test_edge_shapes(o, M, N, K):
     ops = synth.random_operands(1000 * M + N + K, M, N, K, alpha=0.75)
-    paths = [nv.PATH_AUTO, nv.PATH_TILE] + ([nv.PATH_SKINNY] if M <= 16 else [])
+    paths = [nv.PATH_AUTO, nv.PATH_TILE, nv.PATH_WSPLIT] + ([nv.PATH_SKINNY] if M <= 16 else [])
     for path in paths:
         g = run_gpu(ops, path=path, label="edge")
         check_full(o, ops, g, f"edge {M}x{N}x{K} path {path}")
@@ -172,6 +172,8 @@ def test_split_k_variants(o, split_k):
     ops = synth.quantized_operands(91, 200, 160, 2048, alpha=1.25)
     g = run_gpu(ops, path=nv.PATH_TILE, split_k=split_k, label="split-k tile")
     check_full(o, ops, g, f"tile split {split_k}")
+    g = run_gpu(ops, path=nv.PATH_WSPLIT, split_k=split_k, label="split-k wsplit")
+    check_full(o, ops, g, f"wsplit split {split_k}")
     ops16 = synth.quantized_operands(92, 9, 300, 2048, alpha=-0.5)
     g = run_gpu(ops16, path=nv.PATH_SKINNY, split_k=split_k, label="split-k skinny")
     check_full(o, ops16, g, f"skinny split {split_k}")
@@ -186,7 +188,7 @@ def test_wide_scale_range(o):
                          g0.choice(fin, (M, K // 16)).astype(np.uint8),
                          g0.integers(0, 256, (N, K // 2), dtype=np.uint8),
                          g0.choice(fin, (N, K // 16)).astype(np.uint8), 1.0, M, N, K)
-    for path in (nv.PATH_TILE,):
+    for path in (nv.PATH_TILE, nv.PATH_WSPLIT):
         g = run_gpu(ops, path=path, label="wide scales")
         check_full(o, ops, g, "wide scales", min_exact=0.99)
 
@@ -198,6 +200,9 @@ def test_determinism_and_symmetry(o):
     g1 = run_gpu(ops, split_k=4, path=nv.PATH_TILE, label="determinism 1")
     g2 = run_gpu(ops, split_k=4, path=nv.PATH_TILE, label="determinism 2")
     assert np.array_equal(g1, g2)
+    w1 = run_gpu(ops, split_k=3, path=nv.PATH_WSPLIT, label="determinism wsplit 1")
+    w2 = run_gpu(ops, split_k=3, path=nv.PATH_WSPLIT, label="determinism wsplit 2")
+    assert np.array_equal(w1, w2) and np.array_equal(w1, g1)
     t = synth.Operands(ops.b_codes, ops.b_scales, ops.a_codes, ops.a_scales, 1.0, 96, 64, 1024)
     gt = run_gpu(t, path=nv.PATH_TILE, label="transpose")
     assert np.array_equal(gt, g1.T)
@@ -213,7 +218,7 @@ def test_out_guard_and_stream(o):
     ops = synth.random_operands(8, 33, 70, 192)
     a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
     b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
-    for path in (nv.PATH_TILE, nv.PATH_SKINNY) if ops.M <= 16 else (nv.PATH_TILE,):
+    for path in (nv.PATH_TILE, nv.PATH_SKINNY) if ops.M <= 16 else (nv.PATH_TILE, nv.PATH_WSPLIT):
         say(f"guard path={path}")
         buf = torch.full((33 * 70 + 2 * 64,), -12345, dtype=torch.int16, device=DEV)
         out = buf[64:64 + 33 * 70].view(torch.bfloat16).view(33, 70)
