@@ -118,4 +118,7 @@ def test_plan():
     assert p["path"] == nv.PATH_TILE and p["split_k"] == 1 and p["tile_m"] == 256
     for M, N, K in [(512, 768, 6144), (512, 2048, 6144), (17, 8, 16), (300, 5000, 64)]:
         p = nv.plan(M, N, K)
-        assert p["path"] == nv.PATH_TILE and p["split_k"] >= 1
+        assert p["path"] == nv.PATH_WSPLIT and p["split_k"] >= 1
+        # split K only while every workgroup keeps a CU to itself
+        tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
+        assert p["split_k"] == 1 or tiles * p["split_k"] <= 256
