@@ -47,7 +47,94 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--cold", action="store_true",
                     help="also time with operand copies rotated beyond the last-level cache")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                           "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs of --workload into "
+                         "profiles/traffic_<workload>.json (no GPU needed)")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20   # size of the copy used to scale the HBM counters
+KERNEL_SRC = os.path.join(ROOT, "block_scaled_fp4_04_amd", "csrc", "nvfp4_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_path(cfg) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
+
+
+def stored_traffic(cfg):
+    """HBM bytes per launch measured with rocprofv3 counters for this
+    workload, if they were taken on the current kernel source; else None."""
+    try:
+        with open(traffic_path(cfg)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _counter_per_dispatch(directory: str, counter: str, name_filter):
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter or not name_filter(r["Kernel_Name"]):
+                continue
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def traffic_summary(cfg, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    nv_kernel = lambda n: "nvfp4" in n
+    copy_kernel = lambda n: "nvfp4" not in n and ("copy" in n.lower() or "elementwise" in n.lower())
+    f = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", nv_kernel)
+    w = _counter_per_dispatch(write_dir, "WRITE_SIZE", nv_kernel)
+    cf = _counter_per_dispatch(cfetch_dir, "FETCH_SIZE", copy_kernel)
+    cw = _counter_per_dispatch(cwrite_dir, "WRITE_SIZE", copy_kernel)
+    if not (f and w and cf and cw):
+        raise SystemExit("missing counter records")
+    # median dispatch of each; the copy moves COPY_BYTES each way
+    med = lambda v: sorted(v)[len(v) // 2]
+    kf, kw, ccf, ccw = med(f), med(w), med(cf), med(cw)
+    scale_f = COPY_BYTES / (ccf * 1024.0)
+    scale_w = COPY_BYTES / (ccw * 1024.0)
+    fetch_b = kf * 1024.0 * scale_f
+    write_b = kw * 1024.0 * scale_w
+    out = {"workload": cfg.name, "M": cfg.M, "N": cfg.N, "K": cfg.K,
+           "fetch_size_kib_per_dispatch": kf, "write_size_kib_per_dispatch": kw,
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": ccf, "copy_write_kib": ccw,
+           "fetch_scale": scale_f, "write_scale": scale_w,
+           "bytes_per_launch": fetch_b + write_b,
+           "algorithmic_bytes_per_launch": synth.algorithmic_bytes(cfg.M, cfg.N, cfg.K),
+           "kernel_source_sha256_16": kernel_source_hash()}
+    with open(traffic_path(cfg), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def copy_calibration(steps):
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(max(1, steps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "calls": max(1, steps)}))
+
+
+def path_name(nv, path: int) -> str:
+    return {nv.PATH_SKINNY: "skinny", nv.PATH_WSPLIT: "wsplit", nv.PATH_TILE: "tile"}.get(path, str(path))
 
 
 def roofline_for(cfg, seconds_per_call):
@@ -153,6 +240,9 @@ def cpu_baseline(cfg, ops, budget_s):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(synth.config(args.workload), *args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM's "
               "multi-GPU sharding is described in the design notes but not built.",
@@ -164,6 +254,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     nv.init(torch.cuda.current_device())
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
 
     cfg = synth.config(args.workload)
     r = time_workload(nv, torch, cfg, args.steps, args.warmup)
@@ -178,13 +271,13 @@ def main():
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"{cfg.name} M={cfg.M} N={cfg.N} K={cfg.K} alpha={cfg.alpha}",
                    "M": cfg.M, "N": cfg.N, "K": cfg.K, "alpha": cfg.alpha,
-                   "path": "skinny" if plan["path"] == nv.PATH_SKINNY else "tile",
+                   "path": path_name(nv, plan["path"]),
                    "split_k": plan["split_k"], "tile": [plan["tile_m"], plan["tile_n"]],
                    "operands": "E2M1 codes + E4M3 per-16 scales (packed), bf16 out, "
                                "fp16 MFMA with fp32 accumulation",
                    "timing": "HIP graph of the timed calls replayed between HIP events",
                    "parallelism": "none (1 GPU)"},
-        "roofline": roofline_for(cfg, ms * 1e-3),
+        "roofline": dict(roofline_for(cfg, ms * 1e-3), traffic=stored_traffic(cfg)),
         "eager_ms_per_step": r["eager_ms"],
         "wall_s_timed_region": r["wall_s"],
     }
@@ -204,7 +297,7 @@ def main():
             per[c.name] = {"M": c.M, "N": c.N, "K": c.K, "ms": cms, "tflops": ctf,
                            "eager_ms": cr["eager_ms"],
                            "roofline": roofline_for(c, cms * 1e-3),
-                           "path": "skinny" if cr["plan"]["path"] == nv.PATH_SKINNY else "tile",
+                           "path": path_name(nv, cr["plan"]["path"]),
                            "split_k": cr["plan"]["split_k"],
                            "pages_tflops_other_gpu": PAGES_TFLOPS.get(c.index)}
         line["per_shape"] = per
