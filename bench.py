@@ -134,7 +134,8 @@ def copy_calibration(steps):
 
 
 def path_name(nv, path: int) -> str:
-    return {nv.PATH_SKINNY: "skinny", nv.PATH_WSPLIT: "wsplit", nv.PATH_TILE: "tile"}.get(path, str(path))
+    return {nv.PATH_SKINNY: "skinny", nv.PATH_WSPLIT: "wsplit", nv.PATH_TILE: "tile",
+            nv.PATH_GEMV: "gemv"}.get(path, str(path))
 
 
 def roofline_for(cfg, seconds_per_call):

@@ -33,6 +33,7 @@ PATH_AUTO = 0
 PATH_TILE = 1
 PATH_SKINNY = 2
 PATH_WSPLIT = 3
+PATH_GEMV = 4
 
 EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_pack",
            "nvfp4_unpack", "nvfp4_init", "nvfp4_shutdown", "nvfp4_gemm",

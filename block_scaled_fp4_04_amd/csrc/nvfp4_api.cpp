@@ -107,8 +107,15 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int path, int split_req) {
     Plan p{};
     const int64_t P = num_panels(K);
     const int steps = (int)(P / 2);
+    if (path == NVFP4_PATH_AUTO && M <= 4) path = NVFP4_PATH_GEMV;
     if (path == NVFP4_PATH_AUTO && M <= 16) path = NVFP4_PATH_SKINNY;
     p.path = path;
+    if (path == NVFP4_PATH_GEMV) {
+        p.split_k = 1;
+        p.tiles_m = 1;
+        p.tiles_n = (int)(round_up(N, kRowPad) / 4);
+        return p;
+    }
     if (path == NVFP4_PATH_SKINNY) {
         // One workgroup of kSkinnyWaves waves per 16 output columns covers the
         // whole K range: the split-K hand-off costs more than it saves once
@@ -185,12 +192,13 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     if (!a_packed || !a_scales || !b_packed || !b_scales || !out) return NVFP4_ERR_INVALID_VALUE;
     if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim) return NVFP4_ERR_INVALID_VALUE;
     if (!valid_rows_k(1, K)) return NVFP4_ERR_INVALID_VALUE;
-    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_WSPLIT || split_k < 0)
+    if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_GEMV || split_k < 0)
         return NVFP4_ERR_INVALID_VALUE;
     if (!aligned16(a_packed) || !aligned16(a_scales) || !aligned16(b_packed) ||
         !aligned16(b_scales) || !aligned16(out))
         return NVFP4_ERR_MISALIGNED;
     if (path == NVFP4_PATH_SKINNY && M > 16) return NVFP4_ERR_UNSUPPORTED;
+    if (path == NVFP4_PATH_GEMV && M > 4) return NVFP4_ERR_UNSUPPORTED;
 
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return NVFP4_ERR_HIP;
@@ -222,11 +230,13 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     a.tiles_m = plan.tiles_m;
     a.tiles_n = plan.tiles_n;
 
-    const size_t floats = plan.path == NVFP4_PATH_SKINNY   ? skinny_partial_floats(a)
+    const size_t floats = plan.path == NVFP4_PATH_GEMV     ? 0
+                          : plan.path == NVFP4_PATH_SKINNY ? skinny_partial_floats(a)
                           : plan.path == NVFP4_PATH_WSPLIT ? wsplit_partial_floats(plan.cfg, a)
                                                            : tile_partial_floats(plan.cfg, a);
-    const size_t counters =
-        plan.path == NVFP4_PATH_SKINNY ? skinny_counters(a) : tile_counters(plan.cfg, a);
+    const size_t counters = plan.path == NVFP4_PATH_GEMV     ? 0
+                            : plan.path == NVFP4_PATH_SKINNY ? skinny_counters(a)
+                                                             : tile_counters(plan.cfg, a);
     if (floats || counters) {
         Workspace* ws = nullptr;
         const int wst = get_workspace(device, stream, floats, counters, &ws);
@@ -235,7 +245,8 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
         a.counters = ws->counters;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = plan.path == NVFP4_PATH_SKINNY   ? launch_skinny(a, s)
+    const hipError_t e = plan.path == NVFP4_PATH_GEMV     ? launch_gemv(a, s)
+                         : plan.path == NVFP4_PATH_SKINNY ? launch_skinny(a, s)
                          : plan.path == NVFP4_PATH_WSPLIT ? launch_wsplit(plan.cfg, a, s)
                                                           : launch_tile(plan.cfg, a, s);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
@@ -360,7 +371,8 @@ int nvfp4_plan(int64_t M, int64_t N, int64_t K, int* path, int* split_k, int* ti
     const Plan p = make_plan(M, N, K, NVFP4_PATH_AUTO, 0);
     if (path) *path = p.path;
     if (split_k) *split_k = p.split_k;
-    const TileShape s = p.path == NVFP4_PATH_SKINNY   ? TileShape{16, 16}
+    const TileShape s = p.path == NVFP4_PATH_GEMV     ? TileShape{4, 1}
+                        : p.path == NVFP4_PATH_SKINNY ? TileShape{16, 16}
                         : p.path == NVFP4_PATH_WSPLIT ? wsplit_shape(p.cfg)
                                                       : tile_shape(p.cfg);
     if (tile_m) *tile_m = s.bm;

@@ -740,6 +740,120 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Dot-product kernel for M <= MR (MR <= 4): decode-sized GEMMs with one to
+// four rows of A, bound by streaming B and by latency.
+//
+// With so few rows an MFMA would spend half its decode work on the padding
+// rows of A, and one workgroup per 16 columns leaves most CUs idle.  Here
+// each wave owns one row n of B over the whole of K, so 4-wave workgroups
+// cover N/4 CUs' worth of work without any cross-workgroup reduction:
+//   * A (M rows) is decoded once per workgroup into LDS as exact fp16;
+//   * B codes are widened to fp16 without their scale (v_cvt_scalef32_pk_
+//     f16_fp4, scale 1.0) and dotted with A in pairs (v_dot2_f32_f16): within
+//     a 16-element block every term shares one A and one B scale, so the
+//     block sum of (code_b * a') is exact in FP32, and one FMA then applies
+//     the block's B scale (also exact, at most 20 significant bits);
+//   * lane l reads half-panels l, l+64, ... of its row (16 bytes of codes and
+//     2 bytes of scales each), all issued before the wave waits;
+//   * the 64 lane sums are added by a fixed butterfly, lane 0 stores.
+// K is processed in chunks of KC elements so A fits in LDS for any K.
+// ---------------------------------------------------------------------------
+template <int MR>
+__global__ void __launch_bounds__(256) gemv_kernel(GemmArgs a) {
+    constexpr int KC = 8192;                 // K elements per chunk (128 panels)
+    constexpr int HPL = KC / 32 / 64;        // half-panels per lane per chunk (4)
+    __shared__ __attribute__((aligned(16))) _Float16 as[MR][KC];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n = blockIdx.x * 4 + wave;     // B row (< Np: the grid is Np / 4)
+    const int M = a.M;
+    const int Kp = a.P * 64;
+
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+
+    for (int k0 = 0; k0 < Kp; k0 += KC) {
+        const int kc = min(KC, Kp - k0);     // elements in this chunk (multiple of 128)
+        const int hp_total = kc / 32;        // half-panels in this chunk
+        // B loads of this chunk first, so their latency overlaps the A decode.
+        uint4 bw[HPL];
+        uint32_t bsc[HPL];
+#pragma unroll
+        for (int i = 0; i < HPL; ++i) {
+            const int hp = lane + 64 * i;
+            bw[i] = uint4{0u, 0u, 0u, 0u};
+            bsc[i] = 0u;
+            if (hp < hp_total) {
+                const int64_t panel = (int64_t)(k0 / 64) + hp / 2;
+                const int64_t row = panel * a.Np + n;
+                bw[i] = *reinterpret_cast<const uint4*>(a.b_codes + row * 32 + (hp & 1) * 16);
+                bsc[i] = *reinterpret_cast<const uint16_t*>(a.b_scales + row * 4 + (hp & 1) * 2);
+            }
+        }
+        // A rows of this chunk -> LDS (exact fp16), one 8-element word per item.
+        __syncthreads();  // the previous chunk's A is no longer read
+        const int words = M * (kc / 8);
+        for (int w = tid; w < words; w += 256) {
+            const int m = w / (kc / 8), wk = w % (kc / 8);  // word wk of row m in the chunk
+            const int64_t panel = (int64_t)(k0 / 64) + wk / 8;
+            const int64_t row = panel * a.Mp + m;
+            const uint32_t code = *reinterpret_cast<const uint32_t*>(a.a_codes + row * 32 + (wk & 7) * 4);
+            const uint32_t sw = *reinterpret_cast<const uint32_t*>(a.a_scales + row * 4);
+            const h2 s2 = (wk & 7) < 4 ? e4m3x2_lo(sw) : e4m3x2_hi(sw);
+            const _Float16 sc = ((wk & 7) & 2) ? s2[1] : s2[0];  // block (wk & 7) / 2
+            const h8 v = decode8(code, sc);
+            *reinterpret_cast<h8*>(&as[m][wk * 8]) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < HPL; ++i) {
+            const int hp = lane + 64 * i;
+            if (hp >= hp_total) break;
+            const h2 sb = e4m3x2_lo(bsc[i]);  // scales of blocks 2*(hp&1), 2*(hp&1)+1
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                float bs[MR];
+#pragma unroll
+                for (int m = 0; m < MR; ++m) bs[m] = 0.0f;
+#pragma unroll
+                for (int wd = 0; wd < 2; ++wd) {
+                    const uint32_t word = word_of(bw[i], 2 * blk + wd);
+                    const int kk = hp * 32 + (2 * blk + wd) * 8;  // chunk-relative element
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        if (m >= M) break;
+                        const h8 av = *reinterpret_cast<const h8*>(&as[m][kk]);
+                        bs[m] = __builtin_amdgcn_fdot2(h2{av[0], av[1]}, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0), bs[m], false);
+                        bs[m] = __builtin_amdgcn_fdot2(h2{av[2], av[3]}, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1), bs[m], false);
+                        bs[m] = __builtin_amdgcn_fdot2(h2{av[4], av[5]}, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2), bs[m], false);
+                        bs[m] = __builtin_amdgcn_fdot2(h2{av[6], av[7]}, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3), bs[m], false);
+                    }
+                }
+                const float sbf = (float)sb[blk];
+#pragma unroll
+                for (int m = 0; m < MR; ++m) acc[m] = __builtin_fmaf(bs[m], sbf, acc[m]);
+            }
+        }
+    }
+    // Fixed butterfly over the 64 lanes of the wave.
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        float x = acc[m];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+        acc[m] = x;
+    }
+    if (lane == 0 && n < a.N) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            if (m < M) a.out[(int64_t)m * a.N + n] = to_bf16(a.alpha * acc[m]);
+    }
+}
+
 }  // namespace
 
 size_t tile_partial_floats(int cfg, const GemmArgs& a) {
@@ -798,6 +912,14 @@ hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream) {
             else hipLaunchKernelGGL((wsplit_kernel<128, 64, 4, false>), grid, dim3(256), 0, stream, a);
             break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.Np / 4));
+    if (a.M <= 1) hipLaunchKernelGGL(gemv_kernel<1>, grid, dim3(256), 0, stream, a);
+    else if (a.M <= 2) hipLaunchKernelGGL(gemv_kernel<2>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(gemv_kernel<4>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -59,7 +59,8 @@ enum {
     NVFP4_PATH_AUTO = 0,   /* library's choice from M, N, K */
     NVFP4_PATH_TILE = 1,   /* large shapes: MFMA tiles fed through an LDS ring */
     NVFP4_PATH_SKINNY = 2, /* M <= 16: decode shapes, one wave per K range */
-    NVFP4_PATH_WSPLIT = 3  /* mid-size shapes: the waves of a workgroup split K */
+    NVFP4_PATH_WSPLIT = 3, /* mid-size shapes: the waves of a workgroup split K */
+    NVFP4_PATH_GEMV = 4    /* M <= 4: one wave per column of C, dot products */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -120,12 +121,12 @@ int nvfp4_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
 /* nvfp4_gemm with an explicit kernel path (NVFP4_PATH_*) and split-K factor
  * (0 = library's choice, else the number of K slices, clamped to the number
  * of K steps).  Same contract as nvfp4_gemm; NVFP4_ERR_UNSUPPORTED if the
- * forced path cannot run the shape (skinny needs M <= 16). */
+ * forced path cannot run the shape (skinny needs M <= 16, gemv M <= 4). */
 int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void* b_packed,
                          const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
                          int64_t K, int path, int split_k, void* stream);
 
-/* The path (NVFP4_PATH_TILE / _SKINNY / _WSPLIT) and split-K factor that
+/* The path (NVFP4_PATH_TILE / _SKINNY / _WSPLIT / _GEMV) and split-K factor that
  * nvfp4_gemm would use for a shape; also the tile sizes.  Any output pointer
  * may be NULL.  Host-only, no device work. */
 int nvfp4_plan(int64_t M, int64_t N, int64_t K, int* path, int* split_k, int* tile_m,

@@ -98,6 +98,8 @@ def test_gemm_rejects_bad_arguments_before_launch():
     # a forced skinny path needs M <= 16
     assert lib.nvfp4_gemm_with_path(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 17, 4, 64,
                                     nv.PATH_SKINNY, 0, None) == nv.ERR_UNSUPPORTED
+    assert lib.nvfp4_gemm_with_path(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 5, 4, 64,
+                                    nv.PATH_GEMV, 0, None) == nv.ERR_UNSUPPORTED
     assert lib.nvfp4_gemm_with_path(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64,
                                     7, 0, None) == nv.ERR_INVALID_VALUE
     assert lib.nvfp4_gemm_with_path(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64,
@@ -112,7 +114,9 @@ def test_python_gemm_rejects_k_mismatch():
 
 
 def test_plan():
-    assert nv.plan(1, 768, 6144)["path"] == nv.PATH_SKINNY
+    assert nv.plan(1, 768, 6144)["path"] == nv.PATH_GEMV
+    assert nv.plan(4, 768, 6144)["path"] == nv.PATH_GEMV
+    assert nv.plan(5, 768, 6144)["path"] == nv.PATH_SKINNY
     assert nv.plan(16, 256, 6144)["path"] == nv.PATH_SKINNY
     p = nv.plan(16384, 8192, 8192)
     assert p["path"] == nv.PATH_TILE and p["split_k"] == 1 and p["tile_m"] == 256

@@ -58,7 +58,7 @@ def check_full(o, ops, gpu_bits, label, min_exact=0.999):
 
 # ------------------------------------------------------------ decode and layout
 
-@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_WSPLIT, nv.PATH_SKINNY])
+@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_WSPLIT, nv.PATH_SKINNY, nv.PATH_GEMV])
 def test_decode_exhaustive(o, path):
     """Every E4M3 scale byte times every E2M1 code, through the GEMM: one
     operand has a single 1.0 at k=0 with scale s in row s, the other has code
@@ -71,6 +71,19 @@ def test_decode_exhaustive(o, path):
     cd_rows = np.zeros((16, K // 2), np.uint8)
     cd_rows[:, 0] = np.arange(16, dtype=np.uint8)          # code c at k = 0 in row c
     cd_scales = np.full((16, K // 16), 0x38, np.uint8)
+    if path == nv.PATH_GEMV:   # M <= 4: four code rows at a time as A
+        for c0 in range(0, 16, 4):
+            ops = synth.Operands(cd_rows[c0:c0 + 4].copy(), cd_scales[c0:c0 + 4].copy(), sc_rows,
+                                 sc_scales, 1.0, 4, 256, K)
+            g = run_gpu(ops, path=path, label=f"decode codes {c0}..{c0 + 3}")
+            bits, _, _ = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, 1.0)
+            nan_o = ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
+            nan_g = ((g & 0x7F80) == 0x7F80) & ((g & 0x7F) != 0)
+            assert np.array_equal(nan_o, nan_g)
+            ok = ~nan_o
+            same = (g[ok] == bits[ok]) | (((g[ok] & 0x7FFF) == 0) & ((bits[ok] & 0x7FFF) == 0))
+            assert np.all(same), np.argwhere(~same)[:10]
+        return
     if path != nv.PATH_SKINNY:
         ops = synth.Operands(sc_rows, sc_scales, cd_rows, cd_scales, 1.0, 256, 16, K)
     else:   # skinny: M <= 16, so the code rows are A
@@ -85,12 +98,12 @@ def test_decode_exhaustive(o, path):
     assert np.all(same), np.argwhere(~same)[:10]
 
 
-@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_WSPLIT, nv.PATH_SKINNY])
+@pytest.mark.parametrize("path", [nv.PATH_TILE, nv.PATH_WSPLIT, nv.PATH_SKINNY, nv.PATH_GEMV])
 def test_onehot_positions(o, path):
     """One non-zero product at a time, at positions across tile, panel and
     scale-block boundaries: pins nibble order, K slots, scale blocks, the
     packer and the MFMA operand/result layouts."""
-    M = 16 if path == nv.PATH_SKINNY else 300
+    M = {nv.PATH_SKINNY: 16, nv.PATH_GEMV: 4}.get(path, 300)
     N, K = 290, 320
     g = np.random.Generator(np.random.PCG64(77))
     for t in range(6):
@@ -161,7 +174,8 @@ EDGE_SHAPES = [(1, 1, 16), (1, 17, 32), (2, 33, 48), (15, 16, 80), (16, 255, 616
 @pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
 def test_edge_shapes(o, M, N, K):
     ops = synth.random_operands(1000 * M + N + K, M, N, K, alpha=0.75)
-    paths = [nv.PATH_AUTO, nv.PATH_TILE, nv.PATH_WSPLIT] + ([nv.PATH_SKINNY] if M <= 16 else [])
+    paths = [nv.PATH_AUTO, nv.PATH_TILE, nv.PATH_WSPLIT] + ([nv.PATH_SKINNY] if M <= 16 else []) \
+        + ([nv.PATH_GEMV] if M <= 4 else [])
     for path in paths:
         g = run_gpu(ops, path=path, label="edge")
         check_full(o, ops, g, f"edge {M}x{N}x{K} path {path}")
@@ -177,6 +191,14 @@ def test_split_k_variants(o, split_k):
     ops16 = synth.quantized_operands(92, 9, 300, 2048, alpha=-0.5)
     g = run_gpu(ops16, path=nv.PATH_SKINNY, split_k=split_k, label="split-k skinny")
     check_full(o, ops16, g, f"skinny split {split_k}")
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (2, 8320), (3, 16400), (4, 24576)])
+def test_gemv_k_chunks(o, M, K):
+    """The dot-product path over K longer than one 8192-element chunk."""
+    ops = synth.quantized_operands(93 + M, M, 72, K, alpha=0.25)
+    g = run_gpu(ops, path=nv.PATH_GEMV, label="gemv chunks")
+    check_full(o, ops, g, f"gemv {M}x72x{K}")
 
 
 def test_wide_scale_range(o):
