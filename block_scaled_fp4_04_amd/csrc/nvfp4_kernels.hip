@@ -58,6 +58,13 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int s) {
     return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
 
+// Scale of MFMA sub-step s (0..3) from the pair (block of words 0-1, block of
+// words 2-3).  Taken by value: selecting between two array elements by
+// reference would keep the array in private memory.
+__device__ __forceinline__ _Float16 scale_of(h2 pair, int s) {
+    return s < 2 ? pair[0] : pair[1];
+}
+
 // ---------------------------------------------------------------------------
 // Split-K hand-off between workgroups.
 //
@@ -296,7 +303,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     // block scales of the lane's half, widened to fp16.
     struct PanelRegs {
         uint4 ca[MI], cb[NI];
-        h2 sa[MI], sb[NI];
+        uint32_t sa[MI], sb[NI];  // the lane's two E4M3 block scales in bits 15:0
     };
     auto read_words = [&](const uint8_t* p, uint32_t (&w)[4], int n) {
         if (n == 4) {
@@ -316,20 +323,20 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             r.ca[i] = *reinterpret_cast<const uint4*>(b + (wm * MI + i) * 1024 + h * 512 + q * 16);
-            r.sa[i] = e4m3x2_lo(wa[i] >> (16 * h));
+            r.sa[i] = wa[i] >> (16 * h);
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             r.cb[j] = *reinterpret_cast<const uint4*>(b + OFF_B + (wn * NI + j) * 1024 + h * 512 + q * 16);
-            r.sb[j] = e4m3x2_lo(wb[j] >> (16 * h));
+            r.sb[j] = wb[j] >> (16 * h);
         }
     };
     h8 av[2][MI], bv[2][NI];  // decoded operands of the current / next sub-step
     auto decode = [&](const PanelRegs& r, int s, h8 (&ao)[MI], h8 (&bo)[NI]) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) ao[i] = decode8(word_of(r.ca[i], s), s < 2 ? r.sa[i][0] : r.sa[i][1]);
+        for (int i = 0; i < MI; ++i) ao[i] = decode8(word_of(r.ca[i], s), scale_of(e4m3x2_lo(r.sa[i]), s));
 #pragma unroll
-        for (int j = 0; j < NI; ++j) bo[j] = decode8(word_of(r.cb[j], s), s < 2 ? r.sb[j][0] : r.sb[j][1]);
+        for (int j = 0; j < NI; ++j) bo[j] = decode8(word_of(r.cb[j], s), scale_of(e4m3x2_lo(r.sb[j]), s));
     };
     // The four sub-steps of panel `cur` (its sub-step 0 is already decoded
     // in av/bv[0]); the decode of each following sub-step -- the last one
@@ -509,8 +516,8 @@ __global__ void __launch_bounds__(WAVES * 64) skinny_kernel(GemmArgs a) {
             const h2 sah = e4m3x2_lo(as[u]);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const h8 av = decode8(word_of(aw[u], s), s < 2 ? sah[0] : sah[1]);
-                const h8 bv = decode8(word_of(bw[u], s), s < 2 ? sbh[0] : sbh[1]);
+                const h8 av = decode8(word_of(aw[u], s), scale_of(sah, s));
+                const h8 bv = decode8(word_of(bw[u], s), scale_of(sbh, s));
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
             }
         }
@@ -651,9 +658,9 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
         for (int s = 0; s < 4; ++s) {
             h8 av[MI], bv[NI];
 #pragma unroll
-            for (int i = 0; i < MI; ++i) av[i] = decode8(word_of(r.ca[i], s), s < 2 ? sa[i][0] : sa[i][1]);
+            for (int i = 0; i < MI; ++i) av[i] = decode8(word_of(r.ca[i], s), scale_of(sa[i], s));
 #pragma unroll
-            for (int j = 0; j < NI; ++j) bv[j] = decode8(word_of(r.cb[j], s), s < 2 ? sb[j][0] : sb[j][1]);
+            for (int j = 0; j < NI; ++j) bv[j] = decode8(word_of(r.cb[j], s), scale_of(sb[j], s));
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
