@@ -759,8 +759,10 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
 //   * B codes are widened to fp16 without their scale (v_cvt_scalef32_pk_
 //     f16_fp4, scale 1.0) and dotted with A in pairs (v_dot2_f32_f16): within
 //     a 16-element block every term shares one A and one B scale, so the
-//     block sum of (code_b * a') is exact in FP32, and one FMA then applies
-//     the block's B scale (also exact, at most 20 significant bits);
+//     block sum of (code_b * a') needs at most 12 significant bits and is
+//     exact in FP32; one FMA then applies the block's B scale and adds the
+//     block to the running sum (the only rounding, as in an MFMA
+//     accumulator);
 //   * lane l reads half-panels l, l+64, ... of its row (16 bytes of codes and
 //     2 bytes of scales each), all issued before the wave waits;
 //   * the 64 lane sums are added by a fixed butterfly, lane 0 stores.
