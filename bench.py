@@ -60,10 +60,18 @@ COPY_BYTES = 256 << 20   # size of the copy used to scale the HBM counters
 KERNEL_SRC = os.path.join(ROOT, "block_scaled_fp4_04_amd", "csrc", "nvfp4_kernels.hip")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(text: str | None = None) -> str:
+    """Hash of the kernel source with comments and whitespace removed, so
+    that edits of comments do not invalidate counters taken on the code."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    if text is None:
+        with open(KERNEL_SRC, encoding="utf-8") as f:
+            text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def traffic_path(cfg) -> str:
