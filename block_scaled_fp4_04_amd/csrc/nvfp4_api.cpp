@@ -248,7 +248,7 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     const hipError_t e = plan.path == NVFP4_PATH_GEMV     ? launch_gemv(a, s)
                          : plan.path == NVFP4_PATH_SKINNY ? launch_skinny(a, s)
                          : plan.path == NVFP4_PATH_WSPLIT ? launch_wsplit(plan.cfg, a, s)
-                                                          : launch_tile(plan.cfg, a, s);
+                                                          : launch_tile(plan.cfg, a, device, s);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

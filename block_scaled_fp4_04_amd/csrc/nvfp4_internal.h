@@ -60,7 +60,7 @@ inline TileShape wsplit_shape(int cfg) {
 }
 size_t wsplit_partial_floats(int cfg, const GemmArgs& a);
 
-hipError_t launch_tile(int cfg, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_tile(int cfg, const GemmArgs& a, int device, hipStream_t stream);
 hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream);  // M <= 4

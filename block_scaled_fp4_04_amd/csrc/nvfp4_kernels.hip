@@ -54,6 +54,16 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
+// One accumulator element read out of the AGPR it lives in.  Done in asm so
+// the accumulators stay in AGPRs until their block is stored (otherwise the
+// compiler copies the whole accumulator file to VGPRs at once).  Only for
+// accumulators that come straight from the MFMAs.
+__device__ __forceinline__ float acc_read(float x) {
+    float r;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int s) {
     return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
@@ -64,7 +74,6 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int s) {
 __device__ __forceinline__ _Float16 scale_of(h2 pair, int s) {
     return s < 2 ? pair[0] : pair[1];
 }
-
 // ---------------------------------------------------------------------------
 // Split-K hand-off between workgroups.
 //
@@ -173,10 +182,16 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // waits for LDS.  One barrier per panel both publishes the next panel's
 // loads and hands the previous panel's buffer back to the loads.
 //
-// Rows past the padded operand are clamped to its last row (their results
-// are never stored).  The packed K is a whole number of 128-element steps
+// Tile rows past the padded operand read whatever lies beyond it (the next
+// panel's first rows, or zeros past the end of the buffer); their results are
+// never stored.  The packed K is a whole number of 128-element steps
 // (the packer pads with zeros), so every workgroup runs an even number of
 // panels.
+//
+// Without split-K the grid is persistent (as many workgroups as fit on the
+// GPU at once) and each workgroup walks several tiles; its load ring runs on
+// across tile boundaries, so a tile's first panels arrive while the previous
+// tile is still being multiplied and stored.
 //
 // Split-K (split_k > 1): the K steps are divided into split_k contiguous
 // ranges; each workgroup publishes its FP32 tile to the workspace, and the
@@ -204,99 +219,111 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // (& 3: the compiler then knows which direct loads are A's and which B's)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
     const int wm = wave >> 1, wn = wave & 1;
     const int q = lane & 31, h = lane >> 5;
 
-    // Workgroup -> (tile, split).  Consecutive workgroup ids are dealt to the
-    // eight XCDs in turn; remap so that each XCD gets a contiguous range of
-    // tiles, then walk tiles in groups of 8 along M for L2 reuse.
-    int bid = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    // Work items.  Without split-K the grid is persistent: workgroup w takes
+    // tiles w, w + G, w + 2G, ... (G = gridDim.x, a multiple of 8 whenever a
+    // workgroup gets more than one tile).  With split-K, workgroup w takes
+    // the single (tile, K range) pair w.  Consecutive ids are dealt to the
+    // eight XCDs in turn; the id is remapped so that each XCD works on a
+    // contiguous range of tiles, walked in groups of 8 along M for L2 reuse.
+    const int T = a.tiles_m * a.tiles_n;
     const int S = SPLIT ? a.split_k : 1;
-    const int z = bid % S;
-    const int t = bid / S;
-    constexpr int GROUP_M = 8;
-    const int in_group = GROUP_M * a.tiles_n;
-    const int first_m = (t / in_group) * GROUP_M;
-    const int gsize = min(a.tiles_m - first_m, GROUP_M);
-    const int tm = first_m + (t % in_group) % gsize;
-    const int tn = (t % in_group) / gsize;
-    const int m0 = tm * BM, n0 = tn * BN;
-
+    const int G = SPLIT ? 1 : (int)gridDim.x;
+    const int n_items = SPLIT ? 1 : (T - (int)blockIdx.x + G - 1) / G;
+    auto item_of = [&](int it, int& t, int& z) {
+        int bid = (int)blockIdx.x + it * G;
+        const int total = T * S;
+        if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+        z = bid % S;
+        t = bid / S;
+    };
+    auto origin_of = [&](int t, int& m0, int& n0) {
+        constexpr int GROUP_M = 8;
+        const int in_group = GROUP_M * a.tiles_n;
+        const int first_m = (t / in_group) * GROUP_M;
+        const int gsize = min(a.tiles_m - first_m, GROUP_M);
+        m0 = (first_m + (t % in_group) % gsize) * BM;
+        n0 = ((t % in_group) / gsize) * BN;
+    };
+    int t0, z0;
+    item_of(0, t0, z0);
     const int nst = a.P / 2;
-    const int p0 = 2 * (int)((int64_t)z * nst / S);
-    const int p1 = 2 * (int)((int64_t)(z + 1) * nst / S);
+    const int p0 = 2 * (int)((int64_t)z0 * nst / S);
+    const int p1 = 2 * (int)((int64_t)(z0 + 1) * nst / S);
 
     const uint32_t lds0 = lds_addr(lds);
 
-    // Direct-load plan of this wave (constant over panels): for each of its
-    // code and scale chunks, the lane's byte offset inside a panel.  When an
-    // operand has fewer chunks than there are waves, chunks are issued twice
-    // (same bytes to the same place), so every wave issues LPS loads.
-    const __amdgpu_buffer_rsrc_t rac = make_rsrc(a.a_codes, (uint32_t)a.P * a.Mp * 32u);
-    const __amdgpu_buffer_rsrc_t rbc = make_rsrc(a.b_codes, (uint32_t)a.P * a.Np * 32u);
-    const __amdgpu_buffer_rsrc_t ras = make_rsrc(a.a_scales, (uint32_t)a.P * a.Mp * 4u);
-    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(a.b_scales, (uint32_t)a.P * a.Np * 4u);
-    uint32_t c_voff[CPW], s_voff[SPW];
+    // Direct-load plan (constant over the panels of one tile): for each of
+    // the wave's code and scale chunks, the lane's byte offset inside a
+    // panel.  When an operand has fewer chunks than there are waves, chunks
+    // are issued twice (same bytes to the same place), so every wave issues
+    // LPS loads per panel.
+    // Direct-load plan.  Lane offsets inside a tile's panel are the same for
+    // every tile: the panel's and the tile's first row go into the scalar
+    // offset.  Past the bottom or right edge of an operand a lane reads the
+    // following panel's first rows, or, past the end of the operand, zeros
+    // (the buffer range check covers the scalar offset too).  Either way
+    // those rows only feed results that are never stored.
+    uint32_t c_lane[CPW], s_lane[SPW];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         const int k = (wave + 4 * i) % CCH;
-        const bool isA = k < A_CCH;
-        const int grp = isA ? k : k - A_CCH;
-        const int row = min((isA ? m0 : n0) + grp * 32 + q, (isA ? a.Mp : a.Np) - 1);
-        c_voff[i] = (uint32_t)row * 32u + (uint32_t)h * 16u;
+        const int grp = k < A_CCH ? k : k - A_CCH;
+        c_lane[i] = (uint32_t)(grp * 32 + q) * 32u + (uint32_t)h * 16u;
     }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         const int k = (wave + 4 * i) % SCH;
         const bool isA = k < A_SCH;
         const int R = isA ? BM : BN;
-        const int G = isA ? MI : NI;  // 32-row blocks per wave along this operand
+        const int G2 = isA ? MI : NI;  // 32-row blocks per wave along this operand
         const int c = isA ? k : k - A_SCH;
         // LDS slot c*64 + lane holds the scales of tile row r: slots are in
         // (half of the tile, row within its 32-row block, block) order.
         const int slot = c * 64 + lane;
         const int half = slot / (R / 2), sr = slot % (R / 2);
-        const int r = half * (R / 2) + (sr % G) * 32 + sr / G;
-        const int row = min((isA ? m0 : n0) + r, (isA ? a.Mp : a.Np) - 1);
-        s_voff[i] = (uint32_t)row * 4u;
+        s_lane[i] = (uint32_t)(half * (R / 2) + (sr % G2) * 32 + sr / G2) * 4u;
     }
-
-    // Issue direct load d (0 <= d < LPS) of panel p into stage buffer sb.
-    // Panels past the end are clamped to the last panel: those buffers are
-    // never read, and every panel then carries exactly LPS loads per wave.
-    auto issue_one = [&](int p, int sb, int d) {
+    const __amdgpu_buffer_rsrc_t rac = make_rsrc(a.a_codes, (uint32_t)a.P * a.Mp * 32u);
+    const __amdgpu_buffer_rsrc_t rbc = make_rsrc(a.b_codes, (uint32_t)a.P * a.Np * 32u);
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(a.a_scales, (uint32_t)a.P * a.Mp * 4u);
+    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(a.b_scales, (uint32_t)a.P * a.Np * 4u);
+    // Tile whose panels are being loaded: byte offsets of its first A and B
+    // rows inside a code panel (inside a scale panel: / 8).
+    uint32_t base_a = 0, base_b = 0;
+    auto load_tile = [&](int m0, int n0) {
+        base_a = (uint32_t)m0 * 32u;
+        base_b = (uint32_t)n0 * 32u;
+    };
+    const uint32_t a_stride = (uint32_t)a.Mp * 32u, b_stride = (uint32_t)a.Np * 32u;
+    // Issue direct load d (0 <= d < LPS) of the panel at code offsets
+    // (pa, pb) of A and B into stage buffer sb.  Scale offsets are the code
+    // offsets / 8 (4 scale bytes per 32 code bytes).
+    auto issue_one = [&](int sb, int d, uint32_t pa, uint32_t pb) {
         const uint32_t b = lds0 + (uint32_t)(sb * STAGE);
-        const uint32_t pc = (uint32_t)min(p, a.P - 1);
         if (d < CPW) {
             const int k = (wave + 4 * d) % CCH;
             const bool isA = k < A_CCH;
             const int grp = isA ? k : k - A_CCH;
-            const uint32_t soff = pc * (uint32_t)(isA ? a.Mp : a.Np) * 32u;
-            dma16(isA ? rac : rbc, c_voff[d], soff, b + (uint32_t)((isA ? 0 : OFF_B) + grp * 1024));
+            dma16(isA ? rac : rbc, c_lane[d], isA ? pa + base_a : pb + base_b,
+                  b + (uint32_t)((isA ? 0 : OFF_B) + grp * 1024));
         } else {
             const int i = d - CPW;
             const int k = (wave + 4 * i) % SCH;
             const bool isA = k < A_SCH;
             const int c = isA ? k : k - A_SCH;
-            const uint32_t soff = pc * (uint32_t)(isA ? a.Mp : a.Np) * 4u;
-            dma4(isA ? ras : rbs, s_voff[i], soff, b + (uint32_t)((isA ? OFF_SA : OFF_SB) + c * 256));
+            dma4(isA ? ras : rbs, s_lane[i], (isA ? pa + base_a : pb + base_b) >> 3,
+                 b + (uint32_t)((isA ? OFF_SA : OFF_SB) + c * 256));
         }
     };
-    auto issue = [&](int p, int sb) {
-#pragma unroll
-        for (int d = 0; d < LPS; ++d) issue_one(p, sb, d);
-    };
 
+    // Accumulators; each tile's first MFMAs start from zero, so they carry
+    // nothing from one tile to the next.
     f16v acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     // Operand registers of one panel: raw codes (one 16-byte LDS read per
     // 32-row block: words 0..3 feed the four MFMA sub-steps) and the two
@@ -341,20 +368,26 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     // The four sub-steps of panel `cur` (its sub-step 0 is already decoded
     // in av/bv[0]); the decode of each following sub-step -- the last one
     // being sub-step 0 of panel `nxt` -- runs under the MFMAs, and so do the
-    // direct loads of panel `lp` (spread over the sub-steps).
-    auto run_panel = [&](const PanelRegs& cur, const PanelRegs& nxt, int lp, int lsb) {
+    // direct loads of the cursor's panel into buffer lsb (spread over the
+    // sub-steps).  B is the MFMA's first operand, so each 32 x 32 result
+    // block holds its part of C transposed (see the epilogue).
+    auto run_panel = [&](const PanelRegs& cur, const PanelRegs& nxt, int lsb, uint32_t pc,
+                         bool first) {
+        const uint32_t pa = pc * a_stride, pb = pc * b_stride;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int c = s & 1, n = c ^ 1;
 #pragma unroll
-            for (int d = s * LPS / 4; d < (s + 1) * LPS / 4; ++d) issue_one(lp, lsb, d);
+            for (int d = s * LPS / 4; d < (s + 1) * LPS / 4; ++d) issue_one(lsb, d, pa, pb);
             if (s < 3) decode(cur, s + 1, av[n], bv[n]);
             else decode(nxt, 0, av[n], bv[n]);
+            // (j outermost: consecutive MFMAs share their first operand)
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int j = 0; j < NI; ++j)
 #pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[c][i], bv[c][j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < MI; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        bv[c][j], av[c][i], (first && s == 0) ? f16v{} : acc[i][j], 0, 0, 0);
 #pragma unroll
             for (int m = 0; m < MI * NI; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -362,38 +395,140 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
             }
         }
     };
-    // One panel: wait until panel p+1 is resident (loads of panels p+2 ..
-    // p+NS-2 may still be in flight), barrier (everyone is past panel p-1,
-    // whose buffer now takes panel p+NS-1), read panel p+1 (a stale buffer
-    // after the last panel; those values go unused), multiply panel p while
-    // the loads of panel p+NS-1 are issued.
-    auto step = [&](int p, const PanelRegs& cur, PanelRegs& nxt) {
+    // Panels of the current item (relative index 0 .. np-1).  The panel
+    // NS-1 ahead of relative panel r lies in the workgroup's next tile when
+    // r + NS - 1 >= np (np >= NS - 1 whenever there is a next tile): at
+    // r = np - (NS-1) the load offsets switch to that tile.  Without a next
+    // tile the last panel is loaded again: those buffers are never read, and
+    // every panel then carries exactly LPS loads per wave (the wait counts
+    // rely on it).
+    const int np = p1 - p0;
+    int cur_it = 0;           // item being multiplied
+    int next_m0 = 0, next_n0 = 0;  // origin of item cur_it + 1, if any
+    auto load_panel = [&](int r) -> uint32_t {
+        const int q = r + NS - 1;
+        if (q < np) return (uint32_t)(p0 + q);
+        return (uint32_t)(cur_it + 1 < n_items ? p0 + q - np : p1 - 1);
+    };
+    auto start_item = [&](int it, int& m0, int& n0) {
+        int t, z;
+        item_of(it, t, z);
+        origin_of(t, m0, n0);
+        cur_it = it;
+        if (it + 1 < n_items) {
+            item_of(it + 1, t, z);
+            origin_of(t, next_m0, next_n0);
+        }
+    };
+    // One panel (the g-th this workgroup multiplies, relative panel r of its
+    // item): wait until panel g+1 is resident (loads of panels g+2 ..
+    // g+NS-2 may still be in flight), barrier (everyone is past panel g-1,
+    // whose buffer now takes panel g+NS-1), read panel g+1 (a stale buffer
+    // after the last panel; those values go unused), multiply panel g while
+    // the loads of panel g+NS-1 are issued.  `first`: relative panel 0,
+    // whose first MFMAs start from zero.
+    auto step = [&](int g, int r, const PanelRegs& cur, PanelRegs& nxt, bool first) {
         wait_steps<LPS>(NS - 3);
         wg_barrier();
-        read_panel(lds + ((p + 1 - p0) % NS) * STAGE, nxt);
-        run_panel(cur, nxt, p + NS - 1, (p + NS - 1 - p0) % NS);
+        read_panel(lds + ((g + 1) % NS) * STAGE, nxt);
+        if (r == np - (NS - 1) && cur_it + 1 < n_items) load_tile(next_m0, next_n0);
+        run_panel(cur, nxt, (g + NS - 1) % NS, load_panel(r), first);
+    };
+
+    // Epilogue of one tile: y = alpha * acc (FP32), bfloat16 round-to-nearest
+    // even.  The 32x32 MFMA result layout puts column l % 32 of a block and
+    // rows 8 * (v / 4) + 4 * (l / 32) + v % 4 in lane l; the blocks hold C
+    // transposed, so lane l has row l % 32 of C and, for each v / 4, four
+    // consecutive columns, stored as one 8-byte write when N % 4 == 0.
+    auto store_tile = [&](int m0, int n0) {
+        const bool vec = (a.N & 3) == 0;
+        // Lane coordinates recomputed here (cheap, and no VGPR has to stay
+        // live across the main loop for them); each 32 x 32 block is stored
+        // through a uniform base address plus a 32-bit lane offset
+        // (32 * N * 2 bytes < 4 GiB: the packed-size limit of this path
+        // keeps N below 2^25).
+        const uint32_t ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int lq = (int)(ln & 31u), lh = (int)(ln >> 5);
+        const uint32_t lane_off = (uint32_t)lq * (uint32_t)a.N * 2u + (uint32_t)lh * 8u;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                // one 32 x 32 block at a time keeps few values in VGPRs
+                __builtin_amdgcn_sched_barrier(0);
+                const int row0 = m0 + wm * (BM / 2) + i * 32;
+                const int col0 = n0 + wn * (BN / 2) + j * 32;
+                uint8_t* base = reinterpret_cast<uint8_t*>(a.out + (int64_t)row0 * a.N + col0);
+                if (row0 + lq < a.M) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int col = col0 + 8 * u + 4 * lh;
+                        const uint16_t e0 = to_bf16(a.alpha * (SPLIT ? acc[i][j][4 * u + 0] : acc_read(acc[i][j][4 * u + 0])));
+                        const uint16_t e1 = to_bf16(a.alpha * (SPLIT ? acc[i][j][4 * u + 1] : acc_read(acc[i][j][4 * u + 1])));
+                        const uint16_t e2 = to_bf16(a.alpha * (SPLIT ? acc[i][j][4 * u + 2] : acc_read(acc[i][j][4 * u + 2])));
+                        const uint16_t e3 = to_bf16(a.alpha * (SPLIT ? acc[i][j][4 * u + 3] : acc_read(acc[i][j][4 * u + 3])));
+                        uint8_t* p = base + lane_off + 16u * u;
+                        if (vec) {
+                            if (col < a.N)
+                                *reinterpret_cast<uint2*>(p) =
+                                    uint2{(uint32_t)e0 | ((uint32_t)e1 << 16), (uint32_t)e2 | ((uint32_t)e3 << 16)};
+                        } else {
+                            uint16_t* o = reinterpret_cast<uint16_t*>(p);
+                            if (col + 0 < a.N) o[0] = e0;
+                            if (col + 1 < a.N) o[1] = e1;
+                            if (col + 2 < a.N) o[2] = e2;
+                            if (col + 3 < a.N) o[3] = e3;
+                        }
+                    }
+                }
+            }
     };
 
     // Prologue: NS-1 panels in flight; wait for the first and decode its
     // first sub-step.
+    int m0, n0;
+    start_item(0, m0, n0);
+    load_tile(m0, n0);
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) issue(p0 + u, u);
+    for (int u = 0; u < NS - 1; ++u) {
+        const uint32_t pc = load_panel(u - (NS - 1));
+#pragma unroll
+        for (int d = 0; d < LPS; ++d) issue_one(u, d, pc * a_stride, pc * b_stride);
+    }
     PanelRegs r0, r1;
-    if (p0 < p1) {
-        wait_steps<LPS>(NS - 2);
-        wg_barrier();
-        read_panel(lds, r0);
-        decode(r0, 0, av[0], bv[0]);
-    }
-    for (int p = p0; p < p1; p += 2) {  // p1 - p0 is even
-        step(p, r0, r1);
-        step(p + 1, r1, r0);
-    }
-    wait_vmcnt<0>();  // drain the look-ahead loads before the LDS is released
+    wait_steps<LPS>(NS - 2);
+    wg_barrier();
+    read_panel(lds, r0);
+    decode(r0, 0, av[0], bv[0]);
 
-    // Split-K: publish the partial tile; the last arrival reduces in split order.
-    if (SPLIT) {
-        float* mine = a.partials + ((int64_t)t * S + z) * (BM * BN);
+    if (!SPLIT) {
+        // The tiles of this workgroup in turn; a tile's result is stored
+        // right after its last panel, while the loads of the next tile's
+        // first panels are in flight.
+        int g = 0;
+        for (int it = 0; it < n_items; ++it) {
+            if (it > 0) start_item(it, m0, n0);
+            step(g, 0, r0, r1, true);
+            step(g + 1, 1, r1, r0, false);
+            g += 2;
+            for (int r = 2; r < np; r += 2) {  // np is even
+                step(g, r, r0, r1, false);
+                step(g + 1, r + 1, r1, r0, false);
+                g += 2;
+            }
+            store_tile(m0, n0);
+        }
+    } else {
+        step(0, 0, r0, r1, true);
+        step(1, 1, r1, r0, false);
+        for (int r = 2; r < np; r += 2) {  // np is even
+            step(r, r, r0, r1, false);
+            step(r + 1, r + 1, r1, r0, false);
+        }
+        // Split-K: publish the partial tile; the last arrival reduces in
+        // split order.
+        wait_vmcnt<0>();  // drain the look-ahead loads before the LDS is released
+        float* mine = a.partials + ((int64_t)t0 * S + z0) * (BM * BN);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -405,13 +540,13 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
-            const uint32_t old = arrive(a.counters + t);
+            const uint32_t old = arrive(a.counters + t0);
             s_last = (old == (uint32_t)(S - 1));
-            if (s_last) reset_counter(a.counters + t);  // all splits arrived
+            if (s_last) reset_counter(a.counters + t0);  // all splits arrived
         }
         __syncthreads();
         if (!s_last) return;
-        const float* all = a.partials + (int64_t)t * S * (BM * BN);
+        const float* all = a.partials + (int64_t)t0 * S * (BM * BN);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -428,26 +563,9 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
                     for (int v = 0; v < 16; ++v)
                         acc[i][j][v] += fetch(pz + ((i * NI + j) * 16 + v) * 256 + tid);
         }
+        store_tile(m0, n0);
     }
-
-    // Epilogue: y = alpha * acc (FP32), bfloat16 round-to-nearest-even.
-    // 32x32 MFMA result layout: lane l holds column l % 32 and rows
-    // 8 * (v / 4) + 4 * (l / 32) + v % 4 of its block.
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            // one 32 x 32 block at a time keeps few accumulators in VGPRs
-            __builtin_amdgcn_sched_barrier(0);
-            const int col = n0 + wn * (BN / 2) + j * 32 + q;
-            if (col < a.N) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    if (row < a.M) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * acc[i][j][v]);
-                }
-            }
-        }
+    wait_vmcnt<0>();  // drain the look-ahead loads before the LDS is released
 }
 
 // ---------------------------------------------------------------------------
@@ -881,10 +999,42 @@ size_t skinny_counters(const GemmArgs& a) {
     return a.split_k <= 1 ? 0 : (size_t)(a.Np / 16);
 }
 
-hipError_t launch_tile(int cfg, const GemmArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.split_k));
-    const dim3 block(256);
+// Workgroups of a tile kernel that are resident on the device at once
+// (CUs x workgroups per CU), cached per device and configuration.
+int resident_tiles(int cfg, int device) {
+    constexpr int kMaxDevices = 64;
+    static int cache[kMaxDevices][3] = {};
+    if (device < 0 || device >= kMaxDevices || cfg < 0 || cfg > 2) return 0;
+    int& r = cache[device][cfg];
+    if (r == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+            return 0;
+        const void* k = cfg == TILE_256x256   ? (const void*)tile_kernel<256, 256, 8, false>
+                        : cfg == TILE_128x128 ? (const void*)tile_kernel<128, 128, 8, false>
+                                              : (const void*)tile_kernel<64, 64, 8, false>;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, 0) != hipSuccess)
+            return 0;
+        r = cus * per_cu;
+    }
+    return r;
+}
+
+hipError_t launch_tile(int cfg, const GemmArgs& a, int device, hipStream_t stream) {
+    const int tiles = a.tiles_m * a.tiles_n;
     const bool split = a.split_k > 1;
+    int blocks = tiles * a.split_k;
+    if (!split && a.P >= 8) {
+        // persistent grid: at most one workgroup per resident slot; when
+        // workgroups take several tiles their count is a multiple of 8, so
+        // that each keeps its XCD's tile range.  (The kernel's look-ahead of
+        // 7 panels may reach into the next tile only, hence K >= 512.)
+        const int r = resident_tiles(cfg, device);
+        if (r <= 0) return hipErrorInvalidValue;
+        if (tiles > r) blocks = r >= 8 ? r / 8 * 8 : r;
+    }
+    const dim3 grid((unsigned)blocks);
+    const dim3 block(256);
     switch (cfg) {
         case TILE_256x256:
             if (split) hipLaunchKernelGGL((tile_kernel<256, 256, 8, true>), grid, block, 0, stream, a);

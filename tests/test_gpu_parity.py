@@ -181,6 +181,20 @@ def test_edge_shapes(o, M, N, K):
         check_full(o, ops, g, f"edge {M}x{N}x{K} path {path}")
 
 
+@pytest.mark.parametrize("M,N,K", [(4100, 4198, 128), (4352, 4096, 640)])
+def test_tile_several_tiles_per_workgroup(o, M, N, K):
+    """More 256 x 256 tiles than workgroups resident on the GPU, so each
+    workgroup walks two tiles with its load ring running across them (with
+    K = 128 the look-ahead spans several tiles); ragged edge tiles, both
+    output store forms (N % 4 != 0 and N % 4 == 0), and tile counts with and
+    without the XCD remap (289 and 272 tiles)."""
+    p = nv.plan(M, N, K)
+    assert p["path"] == nv.PATH_TILE and p["split_k"] == 1 and p["tile_m"] == 256, p
+    ops = synth.random_operands(7 * M + N + K, M, N, K, alpha=0.625)
+    g = run_gpu(ops, label="several tiles per workgroup")
+    check_full(o, ops, g, f"tile {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("split_k", [1, 2, 3, 5, 16])
 def test_split_k_variants(o, split_k):
     ops = synth.quantized_operands(91, 200, 160, 2048, alpha=1.25)
