@@ -330,7 +330,9 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     // block scales of the lane's half, widened to fp16.
     struct PanelRegs {
         uint4 ca[MI], cb[NI];
-        uint32_t sa[MI], sb[NI];  // the lane's two E4M3 block scales in bits 15:0
+        // scale words of the lane's rows; the lane's two E4M3 block scales
+        // are in bits 16h+15:16h until ready_scales moves them to bits 15:0
+        uint32_t sa[MI], sb[NI];
     };
     auto read_words = [&](const uint8_t* p, uint32_t (&w)[4], int n) {
         if (n == 4) {
@@ -350,13 +352,21 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             r.ca[i] = *reinterpret_cast<const uint4*>(b + (wm * MI + i) * 1024 + h * 512 + q * 16);
-            r.sa[i] = wa[i] >> (16 * h);
+            r.sa[i] = wa[i];
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             r.cb[j] = *reinterpret_cast<const uint4*>(b + OFF_B + (wn * NI + j) * 1024 + h * 512 + q * 16);
-            r.sb[j] = wb[j] >> (16 * h);
+            r.sb[j] = wb[j];
         }
+    };
+    // Done where a panel is first decoded (not right after its LDS reads,
+    // which would make the wave wait for them there).
+    auto ready_scales = [&](PanelRegs& r) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) r.sa[i] >>= 16 * h;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) r.sb[j] >>= 16 * h;
     };
     h8 av[2][MI], bv[2][NI];  // decoded operands of the current / next sub-step
     auto decode = [&](const PanelRegs& r, int s, h8 (&ao)[MI], h8 (&bo)[NI]) {
@@ -371,7 +381,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     // direct loads of the cursor's panel into buffer lsb (spread over the
     // sub-steps).  B is the MFMA's first operand, so each 32 x 32 result
     // block holds its part of C transposed (see the epilogue).
-    auto run_panel = [&](const PanelRegs& cur, const PanelRegs& nxt, int lsb, uint32_t pc,
+    auto run_panel = [&](const PanelRegs& cur, PanelRegs& nxt, int lsb, uint32_t pc,
                          bool first) {
         const uint32_t pa = pc * a_stride, pb = pc * b_stride;
 #pragma unroll
@@ -379,8 +389,12 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
             const int c = s & 1, n = c ^ 1;
 #pragma unroll
             for (int d = s * LPS / 4; d < (s + 1) * LPS / 4; ++d) issue_one(lsb, d, pa, pb);
-            if (s < 3) decode(cur, s + 1, av[n], bv[n]);
-            else decode(nxt, 0, av[n], bv[n]);
+            if (s < 3) {
+                decode(cur, s + 1, av[n], bv[n]);
+            } else {
+                ready_scales(nxt);
+                decode(nxt, 0, av[n], bv[n]);
+            }
             // (j outermost: consecutive MFMAs share their first operand)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
@@ -428,9 +442,13 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     // the loads of panel g+NS-1 are issued.  `first`: relative panel 0,
     // whose first MFMAs start from zero.
     auto step = [&](int g, int r, const PanelRegs& cur, PanelRegs& nxt, bool first) {
+        // (the scheduling barriers keep the previous panel's MFMAs before the
+        // workgroup barrier, and the LDS reads here, a panel ahead of use)
+        __builtin_amdgcn_sched_barrier(0);
         wait_steps<LPS>(NS - 3);
         wg_barrier();
         read_panel(lds + ((g + 1) % NS) * STAGE, nxt);
+        __builtin_amdgcn_sched_barrier(0);
         if (r == np - (NS - 1) && cur_it + 1 < n_items) load_tile(next_m0, next_n0);
         run_panel(cur, nxt, (g + NS - 1) % NS, load_panel(r), first);
     };
@@ -499,6 +517,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     wait_steps<LPS>(NS - 2);
     wg_barrier();
     read_panel(lds, r0);
+    ready_scales(r0);
     decode(r0, 0, av[0], bv[0]);
 
     if (!SPLIT) {
