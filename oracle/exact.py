@@ -115,3 +115,20 @@ def gemm_exact(a_codes, a_scales, b_codes, b_scales, alpha, M: int, N: int, K: i
             # results by value, not by sign bit.
             bits[m][n] = bf16_round_exact(y)
     return bits, exact, mags
+
+
+def grouped_gemm_exact(a_codes, a_scales, b_codes, b_scales, offsets, alpha, N: int, K: int):
+    """Grouped GEMM brute force: output row r belongs to the group g with
+    offsets[g] <= r < offsets[g+1] (found by scanning the table), and its
+    elements are the exact dot products with that group's weight rows
+    b_codes[g], b_scales[g].  Returns bits[M][N] (same conventions as
+    gemm_exact)."""
+    M = int(offsets[-1])
+    bits = [[0] * N for _ in range(M)]
+    for r in range(M):
+        g = 0
+        while not (offsets[g] <= r < offsets[g + 1]):
+            g += 1
+        rb, _, _ = gemm_exact([a_codes[r]], [a_scales[r]], b_codes[g], b_scales[g], alpha, 1, N, K)
+        bits[r] = rb[0]
+    return bits

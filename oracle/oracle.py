@@ -161,6 +161,35 @@ class Oracle:
         return out, exact, mag
 
 
+    def grouped_gemm(self, a_codes, a_scales, b_codes, b_scales, offsets, alpha: float = 1.0):
+        """Grouped GEMM (mixture-of-experts layer) by its definition: group g
+        owns rows offsets[g] .. offsets[g+1]-1 of A and of C, and those rows
+        are the ordinary GEMM of the group's A rows with the group's own
+        weight operand B_g = b_codes[g], b_scales[g] ("Peeling the Kernel
+        Onion", section "The Critical Connection to Real Inference": each
+        expert multiplies the tokens routed to it).  b_codes is [G, N, K/2],
+        b_scales [G, N, K/16]; offsets has G + 1 non-decreasing entries from 0
+        to the number of rows of A.  Returns (bits, alpha*S, T) for all rows."""
+        offsets = np.asarray(offsets, dtype=np.int64)
+        G = b_codes.shape[0]
+        M, N = a_codes.shape[0], b_codes.shape[1]
+        assert offsets.shape == (G + 1,) and offsets[0] == 0 and offsets[-1] == M
+        assert np.all(np.diff(offsets) >= 0)
+        bits = np.zeros((M, N), np.uint16)
+        exact = np.zeros((M, N), np.float64)
+        mag = np.zeros((M, N), np.float64)
+        for g in range(G):
+            r0, r1 = int(offsets[g]), int(offsets[g + 1])
+            if r0 == r1:
+                continue
+            gb, ge, gm = self.gemm(np.ascontiguousarray(a_codes[r0:r1]),
+                                   np.ascontiguousarray(a_scales[r0:r1]),
+                                   np.ascontiguousarray(b_codes[g]),
+                                   np.ascontiguousarray(b_scales[g]), alpha)
+            bits[r0:r1], exact[r0:r1], mag[r0:r1] = gb, ge, gm
+        return bits, exact, mag
+
+
 def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
     """Widen bfloat16 bit patterns to float64 (exact)."""
     u32 = np.asarray(bits, dtype=np.uint32) << 16

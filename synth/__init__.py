@@ -189,3 +189,111 @@ def algorithmic_bytes(M: int, N: int, K: int) -> int:
 def flops(M: int, N: int, K: int) -> int:
     """Two operations (multiply, add) per term of the contraction."""
     return 2 * M * N * K
+
+
+# ---------------------------------------------------------------------------
+# Grouped (mixture-of-experts) workloads: every token is routed to top_k of
+# the experts; the rows of A are the routed (token, expert) pairs in expert
+# order and group g holds the rows of expert g.  The routing is a seeded
+# uniform choice of top_k distinct experts per token (a stand-in for a
+# router: no model or dataset is involved).  Sizes follow "Peeling the
+# Kernel Onion", section "The Critical Connection to Real Inference" (256
+# experts, 8 per token, 512 requests: about 16 tokens per expert) and the
+# eight-way N share of the MoE up-projection of section "The Chain of
+# Reasoning That Led to This Benchmark" (N = 2048 / 8, K = 6144).
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class GroupedConfig:
+    name: str
+    tokens: int
+    experts: int
+    top_k: int
+    N: int
+    K: int
+    alpha: float
+    index: int          # seeds: 1000+i (tokens), 2000+i (weights), 3000+i (routing)
+    description: str
+
+    @property
+    def M(self) -> int:
+        """Rows of A (routed token-expert pairs)."""
+        return self.tokens * self.top_k
+
+
+GROUPED_CONFIGS = [
+    GroupedConfig("moe_up_grouped_e256", 512, 256, 8, 256, 6144, 1.0, 6,
+                  "MoE up-projection eight-way share, all 256 experts in one launch, "
+                  "512 tokens routed to 8 experts each (about 16 rows per expert)"),
+]
+
+
+def grouped_config(name: str) -> GroupedConfig:
+    for c in GROUPED_CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
+
+
+@dataclass
+class GroupedOperands:
+    a_codes: np.ndarray    # [M, K/2]   rows in group order
+    a_scales: np.ndarray   # [M, K/16]
+    b_codes: np.ndarray    # [G, N, K/2]
+    b_scales: np.ndarray   # [G, N, K/16]
+    offsets: np.ndarray    # int32 [G + 1]: group g holds rows offsets[g] .. offsets[g+1]-1
+    alpha: float
+    M: int
+    N: int
+    K: int
+    G: int
+
+
+def moe_routing(seed: int, tokens: int, experts: int, top_k: int):
+    """Seeded routing: each token picks top_k distinct experts uniformly.
+    Returns (offsets int32 [experts + 1], token index of each routed row,
+    rows sorted by expert then token)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    keys = g.random((tokens, experts))
+    choice = np.argsort(keys, axis=1)[:, :top_k]             # [tokens, top_k]
+    expert = choice.reshape(-1)
+    token = np.repeat(np.arange(tokens), top_k)
+    order = np.lexsort((token, expert))
+    counts = np.bincount(expert, minlength=experts)
+    offsets = np.zeros(experts + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return offsets, token[order]
+
+
+def grouped_operands(seed: int, tokens: int, experts: int, top_k: int, N: int, K: int,
+                     alpha: float = 1.0, offsets: np.ndarray | None = None,
+                     token_of_row: np.ndarray | None = None) -> GroupedOperands:
+    """Seeded N(0,1) token activations and expert weights, quantised; the
+    quantised token rows are gathered into group order (quantisation is per
+    row, so this equals quantising the gathered rows).  A routing may be
+    passed in (offsets, token_of_row); else it is drawn with seed 3000+seed."""
+    if offsets is None:
+        offsets, token_of_row = moe_routing(3000 + seed, tokens, experts, top_k)
+    ga = np.random.Generator(np.random.PCG64(1000 + seed))
+    gb = np.random.Generator(np.random.PCG64(2000 + seed))
+    x = ga.standard_normal((tokens, K), dtype=np.float32)
+    tc, ts = quantize_nvfp4(x)
+    del x
+    a_codes = np.ascontiguousarray(tc[token_of_row])
+    a_scales = np.ascontiguousarray(ts[token_of_row])
+    b_codes = np.empty((experts, N, K // 2), np.uint8)
+    b_scales = np.empty((experts, N, K // 16), np.uint8)
+    for e in range(experts):
+        w = gb.standard_normal((N, K), dtype=np.float32)
+        b_codes[e], b_scales[e] = quantize_nvfp4(w)
+    return GroupedOperands(a_codes, a_scales, b_codes, b_scales, np.asarray(offsets, np.int32),
+                           alpha, int(offsets[-1]), N, K, experts)
+
+
+def make_grouped_inputs(cfg: GroupedConfig) -> GroupedOperands:
+    return grouped_operands(cfg.index, cfg.tokens, cfg.experts, cfg.top_k, cfg.N, cfg.K, cfg.alpha)
+
+
+def grouped_algorithmic_bytes(M: int, N: int, K: int, G: int) -> int:
+    """Packed A (M rows), G packed weight operands (N rows each), the FP8
+    scales of both, and the 2-byte output."""
+    return (M * K // 2) + G * (K * N // 2) + (M * K // 16) + G * (K * N // 16) + (M * N * 2)

@@ -375,9 +375,48 @@ def pin_points_match_full(o) -> list[str]:
     return []
 
 
+
+
+def pin_grouped_bruteforce(o, cases: int = 300, seed: int = 17, grouped=None) -> list[str]:
+    """Grouped GEMM vs the exact brute force on tiny problems: 1-4 groups of
+    0-3 rows each (empty groups included), N in 1..3, K in 16, 32, random
+    codes and finite scales, random alpha.  ``grouped`` replaces the
+    oracle's grouped_gemm (to check that this pin catches a wrong one)."""
+    bad = []
+    grouped = grouped or o.grouped_gemm
+    g = np.random.Generator(np.random.PCG64(seed))
+    fin = _finite_scale_bytes()
+    for i in range(cases):
+        G = int(g.integers(1, 5))
+        N = int(g.integers(1, 4))
+        K = int(g.choice([16, 32]))
+        sizes = g.integers(0, 4, size=G)
+        if sizes.sum() == 0:
+            sizes[int(g.integers(0, G))] = 1
+        offsets = np.zeros(G + 1, np.int64)
+        offsets[1:] = np.cumsum(sizes)
+        M = int(offsets[-1])
+        ac = g.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+        as_ = g.choice(fin, size=(M, K // 16)).astype(np.uint8)
+        bc = g.integers(0, 256, size=(G, N, K // 2), dtype=np.uint8)
+        bs = g.choice(fin, size=(G, N, K // 16)).astype(np.uint8)
+        alpha = float(np.float32(g.choice([1.0, 0.5, -1.5, 0.3])))
+        bits, _, _ = grouped(ac, as_, bc, bs, offsets, alpha)
+        want = ex.grouped_gemm_exact(ac.tolist(), as_.tolist(), bc.tolist(), bs.tolist(),
+                                     offsets.tolist(), alpha, N, K)
+        for r in range(M):
+            for n in range(N):
+                if not same_bits_or_zero(int(bits[r, n]), want[r][n]):
+                    bad.append(f"case {i} G={G} sizes={sizes.tolist()} ({r},{n}): "
+                               f"0x{int(bits[r, n]):04x} != 0x{want[r][n]:04x}")
+        if len(bad) > 10:
+            break
+    return bad
+
+
 ALL_PINS = [pin_e4m3_vs_torch, pin_e2m1_vs_table, pin_element_order, pin_bf16_rounding, pin_hand_blocks,
             pin_bruteforce, pin_unit_scales_matmul, pin_onehot, pin_invariants,
-            pin_cancellation, pin_nan_scale, pin_points_match_full]
+            pin_cancellation, pin_nan_scale, pin_points_match_full, pin_grouped_bruteforce]
 
 
 def run_all(o, quick: bool = False) -> dict[str, list[str]]:
@@ -385,6 +424,8 @@ def run_all(o, quick: bool = False) -> dict[str, list[str]]:
     for p in ALL_PINS:
         if quick and p is pin_bruteforce:
             out[p.__name__] = p(o, cases=600)
+        elif quick and p is pin_grouped_bruteforce:
+            out[p.__name__] = p(o, cases=40)
         else:
             out[p.__name__] = p(o)
     return out

@@ -41,3 +41,31 @@ def test_pins_catch_planted_mistake(tmp_path, mutant):
     results = pins.run_all(mo, quick=True)
     caught = [name for name, fails in results.items() if fails]
     assert caught, f"no pin catches mutant {mutant} ({MUTANTS[mutant]})"
+
+
+def _wrong_grouped_weights(o):
+    """Grouped GEMM that gives each group the next group's weights."""
+    import numpy as np
+
+    def f(ac, as_, bc, bs, offsets, alpha):
+        G = bc.shape[0]
+        return o.grouped_gemm(ac, as_, np.roll(bc, 1, axis=0), np.roll(bs, 1, axis=0), offsets, alpha)
+    return f
+
+
+def _wrong_grouped_rows(o):
+    """Grouped GEMM whose row ranges are shifted by one row."""
+    import numpy as np
+
+    def f(ac, as_, bc, bs, offsets, alpha):
+        M = ac.shape[0]
+        off = np.minimum(np.asarray(offsets) + 1, M)
+        off[0] = 0
+        return o.grouped_gemm(ac, as_, bc, bs, off, alpha)
+    return f
+
+
+@pytest.mark.parametrize("wrong", [_wrong_grouped_weights, _wrong_grouped_rows],
+                         ids=["weights of another group", "row ranges off by one"])
+def test_grouped_pin_catches_planted_mistake(o, wrong):
+    assert pins.pin_grouped_bruteforce(o, cases=60, grouped=wrong(o)), "pin missed the mistake"
