@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--only-headline", action="store_true",
                     help="skip the per-shape lines for the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--grouped-only", action="store_true",
+                    help="time only the grouped (all experts in one launch) workload")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--cold", action="store_true",
@@ -228,6 +230,57 @@ def time_workload(nv, torch, cfg, steps, warmup, cold=False, ops=None):
     return {"graph_ms": graph_ms, "eager_ms": eager_ms, "wall_s": wall, "plan": plan, "ops": ops}
 
 
+def grouped_roofline(g, seconds_per_call):
+    b = synth.grouped_algorithmic_bytes(g.M, g.N, g.K, g.experts)
+    ach = b / seconds_per_call / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
+            "frac": ach / HBM_GBPS, "traffic": None, "algorithmic_bytes_per_launch": b}
+
+
+def time_grouped(nv, torch, g, steps, warmup, ops=None):
+    """Per-call time of nvfp4_grouped_gemm (all experts of one layer in one
+    launch) on resident operands, graph-replayed like time_workload."""
+    if ops is None:
+        ops = synth.make_grouped_inputs(g)
+    a = nv.to_device(ops.a_codes, ops.a_scales, "cuda")
+    b = nv.groups_to_device(ops.b_codes, ops.b_scales, "cuda")
+    off = torch.from_numpy(ops.offsets).to("cuda")
+    out = torch.empty((ops.M, ops.N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            nv.grouped_gemm(a, b, off, g.alpha, out=out, stream=stream)
+    stream.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=stream):
+        cap = torch.cuda.current_stream()
+        for _ in range(steps):
+            nv.grouped_gemm(a, b, off, g.alpha, out=out, stream=cap)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        gr.replay()
+        start.record(stream)
+        gr.replay()
+        stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    del gr
+    return {"graph_ms": ms, "ops": ops}
+
+
+def grouped_line(nv, torch, steps, warmup):
+    g = synth.GROUPED_CONFIGS[0]
+    r = time_grouped(nv, torch, g, steps, warmup)
+    ms = r["graph_ms"]
+    counts = np.diff(r["ops"].offsets)
+    return g.name, {"experts": g.experts, "tokens": g.tokens, "top_k": g.top_k, "M": g.M,
+                    "N": g.N, "K": g.K, "rows_per_expert": [int(counts.min()), int(counts.max())],
+                    "ms": ms, "tflops": synth.flops(g.M, g.N, g.K) / (ms * 1e-3) / 1e12,
+                    "roofline": grouped_roofline(g, ms * 1e-3), "path": "grouped",
+                    "pages_tflops_other_gpu": None}
+
+
 def cpu_baseline(cfg, ops, budget_s):
     from oracle import oracle as orc
     o = orc.load()
@@ -265,6 +318,11 @@ def main():
     nv.init(torch.cuda.current_device())
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+
+    if args.grouped_only:
+        name, g = grouped_line(nv, torch, args.steps, args.warmup)
+        print(json.dumps({"workload": name, **g}), flush=True)
         return
 
     cfg = synth.config(args.workload)
@@ -309,6 +367,8 @@ def main():
                            "path": path_name(nv, cr["plan"]["path"]),
                            "split_k": cr["plan"]["split_k"],
                            "pages_tflops_other_gpu": PAGES_TFLOPS.get(c.index)}
+        name, g = grouped_line(nv, torch, args.steps, args.warmup)
+        per[name] = g
         line["per_shape"] = per
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, ops, args.cpu_seconds)

@@ -37,7 +37,7 @@ PATH_GEMV = 4
 
 EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_pack",
            "nvfp4_unpack", "nvfp4_init", "nvfp4_shutdown", "nvfp4_gemm",
-           "nvfp4_gemm_with_path", "nvfp4_plan"]
+           "nvfp4_gemm_with_path", "nvfp4_plan", "nvfp4_grouped_gemm"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemm_with_path.restype = ctypes.c_int
         L.nvfp4_gemm_with_path.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
                                            _i64, ctypes.c_int, ctypes.c_int, _vp]
+        L.nvfp4_grouped_gemm.restype = ctypes.c_int
+        L.nvfp4_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float, _vp, _i64,
+                                         _i64, _i64, _vp]
         ip = ctypes.POINTER(ctypes.c_int)
         L.nvfp4_plan.restype = ctypes.c_int
         L.nvfp4_plan.argtypes = [_i64, _i64, _i64, ip, ip, ip, ip]
@@ -223,3 +226,68 @@ def gemm_raw(a_codes: int, a_scales: int, b_codes: int, b_scales: int, alpha: fl
     """Direct call of nvfp4_gemm with raw device addresses; returns the status."""
     return int(lib().nvfp4_gemm(a_codes, a_scales, b_codes, b_scales, float(alpha), out, M, N, K,
                                 stream))
+
+
+@dataclass
+class PackedGroups:
+    """The weight operands of a grouped GEMM, each ``rows`` x ``K``, packed
+    and concatenated (group g at g * code_bytes / g * scale_bytes), resident
+    on a device."""
+    codes: "object"
+    scales: "object"
+    groups: int
+    rows: int
+    K: int
+
+    def check(self, name: str) -> None:
+        import torch
+        cb, sb = packed_size(self.rows, self.K)
+        for what, t, need in ((".codes", self.codes, cb * self.groups),
+                              (".scales", self.scales, sb * self.groups)):
+            if t.dtype != torch.uint8 or t.numel() != need or not t.is_contiguous():
+                raise ValueError(f"{name}{what} must be a contiguous uint8 tensor of {need} bytes")
+
+
+def pack_groups(codes: np.ndarray, scales: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Canonical weights [G, rows, K/2] and [G, rows, K/16] -> the
+    concatenated packed arrays (nvfp4_pack per group)."""
+    if codes.ndim != 3 or scales.ndim != 3 or codes.shape[0] != scales.shape[0]:
+        raise ValueError("codes and scales must be [G, rows, K/2] and [G, rows, K/16]")
+    parts = [pack(codes[g], scales[g]) for g in range(codes.shape[0])]
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+
+
+def groups_to_device(codes: np.ndarray, scales: np.ndarray, device="cuda") -> PackedGroups:
+    import torch
+    G, rows, kh = codes.shape
+    pc, ps = pack_groups(codes, scales)
+    return PackedGroups(torch.from_numpy(pc).to(device), torch.from_numpy(ps).to(device), G, rows,
+                        2 * kh)
+
+
+def grouped_gemm(a: PackedOperand, b: PackedGroups, row_offsets, alpha: float = 1.0, out=None,
+                 stream=None):
+    """Grouped GEMM (nvfp4_grouped_gemm): rows row_offsets[g] ..
+    row_offsets[g+1]-1 of A and C belong to group g, whose weights are
+    b's g-th operand.  ``row_offsets`` is an int32 device tensor of G + 1
+    entries.  Returns C (M x N bfloat16)."""
+    import torch
+    if a.K != b.K:
+        raise ValueError(f"K dimension mismatch: A has K={a.K}, B has K={b.K}")
+    M, N, K = a.rows, b.rows, a.K
+    if (row_offsets.dtype != torch.int32 or row_offsets.numel() != b.groups + 1
+            or not row_offsets.is_contiguous() or row_offsets.device != a.codes.device):
+        raise ValueError(f"row_offsets must be a contiguous int32 tensor of {b.groups + 1} "
+                         "entries on A's device")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
+    a.check("a")
+    b.check("b")
+    st = lib().nvfp4_grouped_gemm(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+                                  b.scales.data_ptr(), row_offsets.data_ptr(), b.groups,
+                                  float(alpha), out.data_ptr(), M, N, K, _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_grouped_gemm(G={b.groups}, M={M}, N={N}, K={K})")
+    return out

@@ -364,6 +364,42 @@ int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void*
                     stream);
 }
 
+int nvfp4_grouped_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
+                       const void* b_scales, const int32_t* row_offsets, int64_t groups,
+                       float alpha, void* out, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!a_packed || !a_scales || !b_packed || !b_scales || !row_offsets || !out)
+        return NVFP4_ERR_INVALID_VALUE;
+    if (M < 0 || N < 1 || M > kMaxDim || N > kMaxDim || groups < 1 || !valid_rows_k(1, K))
+        return NVFP4_ERR_INVALID_VALUE;
+    const int64_t Np = round_up(N, kRowPad);
+    if (groups * (Np / 16) > INT32_MAX) return NVFP4_ERR_INVALID_VALUE;
+    if (!aligned16(a_packed) || !aligned16(a_scales) || !aligned16(b_packed) ||
+        !aligned16(b_scales) || !aligned16(out) || (reinterpret_cast<uintptr_t>(row_offsets) & 3u))
+        return NVFP4_ERR_MISALIGNED;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return NVFP4_ERR_HIP;
+    const int dst = check_device(device);
+    if (dst != NVFP4_OK) return dst;
+    if (M == 0) return NVFP4_OK;  // no rows: nothing to compute or write
+
+    GroupedArgs a{};
+    a.a_codes = static_cast<const uint8_t*>(a_packed);
+    a.a_scales = static_cast<const uint8_t*>(a_scales);
+    a.b_codes = static_cast<const uint8_t*>(b_packed);
+    a.b_scales = static_cast<const uint8_t*>(b_scales);
+    a.offsets = row_offsets;
+    a.out = static_cast<uint16_t*>(out);
+    a.alpha = alpha;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.Mp = (int)round_up(M, kRowPad);
+    a.Np = (int)Np;
+    a.P = (int)num_panels(K);
+    a.G = (int)groups;
+    const hipError_t e = launch_grouped(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 int nvfp4_plan(int64_t M, int64_t N, int64_t K, int* path, int* split_k, int* tile_m,
                int* tile_n) {
     if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim || !valid_rows_k(1, K))

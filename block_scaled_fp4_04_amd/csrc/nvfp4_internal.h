@@ -65,4 +65,26 @@ hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream);  // M <= 4
 
+// Grouped (mixture-of-experts) GEMM: G weight operands of N x K, rows of A
+// assigned to groups by a device table of G + 1 offsets.
+constexpr int kGroupedWaves = 8;   // waves per workgroup (split K)
+constexpr int kGroupedChunks = 2;  // 16-row chunks of A per pass over B
+constexpr int kGroupedUnits = 1;   // 128-element K units of loads in flight per wave
+constexpr int kGroupedBlocks = 4;  // 16-row blocks of B per workgroup (share A's decode)
+
+struct GroupedArgs {
+    const uint8_t* a_codes;   // [P][Mp][32], all M rows
+    const uint8_t* a_scales;  // [P][Mp][4]
+    const uint8_t* b_codes;   // G x [P][Np][32]
+    const uint8_t* b_scales;  // G x [P][Np][4]
+    const int32_t* offsets;   // [G + 1] row offsets (device)
+    uint16_t* out;            // [M][N] bfloat16 bits
+    float alpha;
+    int M, N;                 // total rows of A / C, columns of C
+    int Mp, Np;               // padded row counts of the packed operands
+    int P;                    // number of 64-element K panels (even)
+    int G;                    // number of groups
+};
+hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -126,6 +126,34 @@ int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void*
                          const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
                          int64_t K, int path, int split_k, void* stream);
 
+/* Grouped GEMM for mixture-of-experts layers: `groups` weight operands B_g
+ * (each N x K) share one launch; group g owns rows
+ * row_offsets[g] .. row_offsets[g+1]-1 of A and of C:
+ *   C[r][n] = bf16_rne(alpha * sum_k a'[r][k] * b'_g[n][k])  for r in group g
+ * ("Peeling the Kernel Onion", sections "The Critical Connection to Real
+ * Inference" -- tokens routed to experts, about 16 rows per expert -- and
+ * "Knowledge Created and Its Impact" -- grouped GEMMs amortise the per-call
+ * overhead).
+ *   a_packed, a_scales : DEVICE, A (M x K, rows in group order) packed by
+ *                        nvfp4_pack as one operand (rows = M)
+ *   b_packed, b_scales : DEVICE, the `groups` weight operands, each N x K
+ *                        packed by nvfp4_pack, concatenated: group g starts at
+ *                        g * code_bytes and g * scale_bytes of
+ *                        nvfp4_packed_size(N, K)
+ *   row_offsets        : DEVICE int32[groups + 1], non-decreasing, from 0 to
+ *                        M (a router's output; read by the kernel; entries are
+ *                        clamped to [0, M], so a malformed table gives wrong
+ *                        rows but no access outside the buffers)
+ *   out                : DEVICE, M x N bfloat16, row-major; rows of every
+ *                        group are overwritten, rows outside every group are
+ *                        left untouched
+ *   M                  : total rows (0 is allowed: nothing is launched)
+ * Same alignment (row_offsets: 4 bytes), status and stream rules as
+ * nvfp4_gemm; no workspace, no allocation. */
+int nvfp4_grouped_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
+                       const void* b_scales, const int32_t* row_offsets, int64_t groups,
+                       float alpha, void* out, int64_t M, int64_t N, int64_t K, void* stream);
+
 /* The path (NVFP4_PATH_TILE / _SKINNY / _WSPLIT / _GEMV) and split-K factor that
  * nvfp4_gemm would use for a shape; also the tile sizes.  Any output pointer
  * may be NULL.  Host-only, no device work. */

@@ -106,6 +106,37 @@ def test_gemm_rejects_bad_arguments_before_launch():
                                     0, -1, None) == nv.ERR_INVALID_VALUE
 
 
+def _graw(a=0x1000, sa=0x2000, b=0x3000, sb=0x4000, off=0x6000, G=4, out=0x5000, M=4, N=4,
+          K=64):
+    return nv.lib().nvfp4_grouped_gemm(a, sa, b, sb, off, G, 1.0, out, M, N, K, None)
+
+
+def test_grouped_gemm_rejects_bad_arguments_before_launch():
+    assert _graw(a=None) == nv.ERR_INVALID_VALUE
+    assert _graw(off=None) == nv.ERR_INVALID_VALUE
+    assert _graw(out=None) == nv.ERR_INVALID_VALUE
+    assert _graw(G=0) == nv.ERR_INVALID_VALUE
+    assert _graw(M=-1) == nv.ERR_INVALID_VALUE
+    assert _graw(N=0) == nv.ERR_INVALID_VALUE
+    assert _graw(K=24) == nv.ERR_INVALID_VALUE
+    assert _graw(G=1 << 30, N=256) == nv.ERR_INVALID_VALUE   # grid too large
+    assert _graw(b=0x3008) == nv.ERR_MISALIGNED
+    assert _graw(off=0x6002) == nv.ERR_MISALIGNED
+
+
+def test_pack_groups_concatenates_per_group_packing():
+    g = np.random.Generator(np.random.PCG64(3))
+    codes = g.integers(0, 256, size=(3, 20, 80), dtype=np.uint8)
+    scales = g.integers(0, 256, size=(3, 20, 10), dtype=np.uint8)
+    pc, ps = nv.pack_groups(codes, scales)
+    cb, sb = nv.packed_size(20, 160)
+    assert pc.size == 3 * cb and ps.size == 3 * sb
+    for i in range(3):
+        c1, s1 = nv.pack(codes[i], scales[i])
+        assert np.array_equal(pc[i * cb:(i + 1) * cb], c1)
+        assert np.array_equal(ps[i * sb:(i + 1) * sb], s1)
+
+
 def test_python_gemm_rejects_k_mismatch():
     a = nv.PackedOperand(None, None, 4, 128)
     b = nv.PackedOperand(None, None, 4, 256)

@@ -1,0 +1,125 @@
+"""GPU parity of the grouped (mixture-of-experts) GEMM through the C ABI.
+
+Each group's rows are compared element by element with the oracle's grouped
+GEMM (each group an ordinary GEMM with its own weights), with the same bound
+as the single GEMM: 1 bf16 ulp + 1e-5 * |alpha| * sum_k |a'_k b'_k|, and the
+bit-exact fraction reported.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import oracle as orc
+from parity import compare
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_04_amd as nv  # noqa: E402
+
+DEV = "cuda"
+
+
+def say(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return orc.load()
+
+
+def random_grouped(seed, sizes, N, K, alpha=1.0):
+    """Uniformly random codes (all 16) and random positive scales."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    G = len(sizes)
+    offsets = np.zeros(G + 1, np.int32)
+    offsets[1:] = np.cumsum(sizes)
+    M = int(offsets[-1])
+    ac = g.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    as_ = g.integers(0x20, 0x49, size=(M, K // 16), dtype=np.uint8)
+    bc = g.integers(0, 256, size=(G, N, K // 2), dtype=np.uint8)
+    bs = g.integers(0x20, 0x49, size=(G, N, K // 16), dtype=np.uint8)
+    return synth.GroupedOperands(ac, as_, bc, bs, offsets, alpha, M, N, K, G)
+
+
+def run_grouped(ops, offsets=None, out=None, label=""):
+    offs = ops.offsets if offsets is None else np.asarray(offsets, np.int32)
+    say(f"{label} G={ops.G} M={ops.M} N={ops.N} K={ops.K} alpha={ops.alpha} "
+        f"offsets={offs.tolist() if offs.size <= 12 else '...'}")
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.groups_to_device(ops.b_codes, ops.b_scales, DEV)
+    off = torch.from_numpy(offs).to(DEV)
+    c = nv.grouped_gemm(a, b, off, ops.alpha, out=out)
+    torch.cuda.synchronize()
+    return c.view(torch.int16).cpu().numpy().astype(np.uint16)
+
+
+def check(o, ops, gpu_bits, label, rows=None):
+    bits, exact, mag = o.grouped_gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales,
+                                      ops.offsets, ops.alpha)
+    sel = slice(None) if rows is None else rows
+    r = compare(gpu_bits[sel], bits[sel], exact[sel], mag[sel], ops.alpha)
+    say(f"{label}: {r}")
+    assert r["over"] == 0, r
+    assert r["bit_exact_frac"] >= 0.999, r
+    return r
+
+
+@pytest.mark.parametrize("sizes,N,K", [
+    ([0, 1, 16, 17, 40], 40, 640),       # empty group, 1 row, one chunk, two, three (two passes)
+    ([3, 0, 0, 33], 16, 128),             # one K step (fewer units than waves)
+    ([16] * 9, 256, 6144),                # full K, N of the MoE share
+    ([5, 27, 2], 72, 16400),              # K not a multiple of 128 (zero panels)
+])
+def test_grouped_shapes(o, sizes, N, K):
+    ops = random_grouped(sum(sizes) * 7 + N + K, sizes, N, K, alpha=0.75)
+    g = run_grouped(ops, label="grouped")
+    check(o, ops, g, f"grouped sizes={sizes} N={N} K={K}")
+
+
+def test_grouped_moe_workload(o):
+    """512 tokens routed to 8 of 256 experts (N = 256, K = 6144): the
+    benchmark's grouped workload, every element."""
+    cfg = synth.grouped_config("moe_up_grouped_e256")
+    ops = synth.make_grouped_inputs(cfg)
+    g = run_grouped(ops, label="moe grouped workload")
+    check(o, ops, g, "moe grouped workload")
+
+
+def test_grouped_offsets_are_clamped_and_rows_outside_groups_untouched(o):
+    """A table with entries outside [0, M] is clamped (group 0 empty, group 2
+    ends at M); rows after the last group's end are not written."""
+    sizes = [4, 3, 7]
+    ops = random_grouped(5, sizes, 24, 256, alpha=-1.25)
+    M, N = ops.M, ops.N
+    # clamped table: [0, -5, 3, 100] acts as [0, 0, 3, M]
+    bad = np.array([0, -5, 3, 100], np.int32)
+    eff = synth.GroupedOperands(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales,
+                                np.array([0, 0, 3, M], np.int32), ops.alpha, M, N, ops.K, 3)
+    g = run_grouped(ops, offsets=bad, label="clamped offsets")
+    check(o, eff, g, "clamped offsets")
+    # last group ends two rows early: those rows keep their previous contents
+    short = np.array([0, 4, 7, M - 2], np.int32)
+    out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device=DEV)
+    g2 = run_grouped(ops, offsets=short, out=out, label="short table")
+    eff2 = synth.GroupedOperands(ops.a_codes[:M - 2], ops.a_scales[:M - 2], ops.b_codes,
+                                 ops.b_scales, short, ops.alpha, M - 2, N, ops.K, 3)
+    check(o, eff2, g2[:M - 2], "short table")
+    minus7 = int(torch.tensor([-7.0], dtype=torch.bfloat16).view(torch.int16).item()) & 0xFFFF
+    assert np.all(g2[M - 2:] == minus7)
+
+
+def test_grouped_no_rows():
+    """M = 0: nothing to do, success."""
+    st = nv.lib().nvfp4_grouped_gemm(0x1000, 0x2000, 0x3000, 0x4000, 0x6000, 4, 1.0, 0x5000,
+                                     0, 16, 128, None)
+    assert st == nv.OK
