@@ -59,21 +59,33 @@ def parse():
 
 
 COPY_BYTES = 256 << 20   # size of the copy used to scale the HBM counters
-KERNEL_SRC = os.path.join(ROOT, "block_scaled_fp4_04_amd", "csrc", "nvfp4_kernels.hip")
+CSRC = os.path.join(ROOT, "block_scaled_fp4_04_amd", "csrc")
+# the sources whose code the counters of a workload depend on
+KERNEL_SOURCES = {
+    "gemm": ["nvfp4_internal.h", "nvfp4_device.h", "nvfp4_kernels.hip"],
+    "grouped": ["nvfp4_internal.h", "nvfp4_device.h", "nvfp4_grouped.hip"],
+}
 
 
-def kernel_source_hash(text: str | None = None) -> str:
-    """Hash of the kernel source with comments and whitespace removed, so
-    that edits of comments do not invalidate counters taken on the code."""
+def _sources_for(cfg) -> list[str]:
+    kind = "grouped" if isinstance(cfg, synth.GroupedConfig) else "gemm"
+    return [os.path.join(CSRC, f) for f in KERNEL_SOURCES[kind]]
+
+
+def kernel_source_hash(cfg) -> str:
+    """Hash of the kernel sources a workload runs, with comments and
+    whitespace removed, so that edits of comments (or of other kernels) do
+    not invalidate counters taken on the code."""
     import hashlib
     import re
-    if text is None:
-        with open(KERNEL_SRC, encoding="utf-8") as f:
+    h = hashlib.sha256()
+    for path in _sources_for(cfg):
+        with open(path, encoding="utf-8") as f:
             text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(cfg) -> str:
@@ -88,7 +100,7 @@ def stored_traffic(cfg):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(cfg):
         return None
     return t.get("bytes_per_launch")
 
@@ -105,7 +117,7 @@ def _counter_per_dispatch(directory: str, counter: str, name_filter):
     return list(vals.values())
 
 
-def traffic_summary(cfg, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+def traffic_summary(cfg, fetch_dir, write_dir, cfetch_dir, cwrite_dir, alg_bytes=None):
     nv_kernel = lambda n: "nvfp4" in n
     copy_kernel = lambda n: "nvfp4" not in n and ("copy" in n.lower() or "elementwise" in n.lower())
     f = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", nv_kernel)
@@ -126,8 +138,9 @@ def traffic_summary(cfg, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
            "copy_bytes": COPY_BYTES, "copy_fetch_kib": ccf, "copy_write_kib": ccw,
            "fetch_scale": scale_f, "write_scale": scale_w,
            "bytes_per_launch": fetch_b + write_b,
-           "algorithmic_bytes_per_launch": synth.algorithmic_bytes(cfg.M, cfg.N, cfg.K),
-           "kernel_source_sha256_16": kernel_source_hash()}
+           "algorithmic_bytes_per_launch": (alg_bytes if alg_bytes is not None
+                                            else synth.algorithmic_bytes(cfg.M, cfg.N, cfg.K)),
+           "kernel_source_sha256_16": kernel_source_hash(cfg)}
     with open(traffic_path(cfg), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
@@ -277,7 +290,8 @@ def grouped_line(nv, torch, steps, warmup):
     return g.name, {"experts": g.experts, "tokens": g.tokens, "top_k": g.top_k, "M": g.M,
                     "N": g.N, "K": g.K, "rows_per_expert": [int(counts.min()), int(counts.max())],
                     "ms": ms, "tflops": synth.flops(g.M, g.N, g.K) / (ms * 1e-3) / 1e12,
-                    "roofline": grouped_roofline(g, ms * 1e-3), "path": "grouped",
+                    "roofline": dict(grouped_roofline(g, ms * 1e-3), traffic=stored_traffic(g)),
+                    "path": "grouped",
                     "pages_tflops_other_gpu": None}
 
 
@@ -303,7 +317,12 @@ def cpu_baseline(cfg, ops, budget_s):
 def main():
     args = parse()
     if args.traffic_summary:
-        traffic_summary(synth.config(args.workload), *args.traffic_summary)
+        if args.grouped_only:
+            g = synth.GROUPED_CONFIGS[0]
+            traffic_summary(g, *args.traffic_summary,
+                            alg_bytes=synth.grouped_algorithmic_bytes(g.M, g.N, g.K, g.experts))
+        else:
+            traffic_summary(synth.config(args.workload), *args.traffic_summary)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM's "
@@ -355,20 +374,24 @@ def main():
                         "roofline": roofline_for(cfg, c["graph_ms"] * 1e-3)}
     if not args.only_headline:
         per = {}
+        # the grouped workload first, then the single GEMMs by size; the
+        # allocator's cached blocks are released between workloads
+        torch.cuda.empty_cache()
+        name, g = grouped_line(nv, torch, args.steps, args.warmup)
+        per[name] = g
         for c in synth.CONFIGS:
             if c.index == cfg.index:
                 continue
+            torch.cuda.empty_cache()
             cr = time_workload(nv, torch, c, args.steps, args.warmup)
             cms = cr["graph_ms"]
             ctf = synth.flops(c.M, c.N, c.K) / (cms * 1e-3) / 1e12
             per[c.name] = {"M": c.M, "N": c.N, "K": c.K, "ms": cms, "tflops": ctf,
                            "eager_ms": cr["eager_ms"],
-                           "roofline": roofline_for(c, cms * 1e-3),
+                           "roofline": dict(roofline_for(c, cms * 1e-3), traffic=stored_traffic(c)),
                            "path": path_name(nv, cr["plan"]["path"]),
                            "split_k": cr["plan"]["split_k"],
                            "pages_tflops_other_gpu": PAGES_TFLOPS.get(c.index)}
-        name, g = grouped_line(nv, torch, args.steps, args.warmup)
-        per[name] = g
         line["per_shape"] = per
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, ops, args.cpu_seconds)

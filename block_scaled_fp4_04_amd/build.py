@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4.so")
-SOURCES = [os.path.join(CSRC, "nvfp4_api.cpp"), os.path.join(CSRC, "nvfp4_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "nvfp4_api.cpp"), os.path.join(CSRC, "nvfp4_kernels.hip"),
+           os.path.join(CSRC, "nvfp4_grouped.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

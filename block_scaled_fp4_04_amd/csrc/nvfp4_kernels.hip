@@ -19,139 +19,11 @@
 // so the kernels feed MFMA K-slots with whatever elements make the loads
 // contiguous, as long as A and B lanes agree and each 8-element group stays
 // inside one 16-element scale block.
-#include "nvfp4_internal.h"
+#include "nvfp4_device.h"
 
 namespace nvfp4 {
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f16v __attribute__((ext_vector_type(16)));
-typedef float f4v __attribute__((ext_vector_type(4)));
-
-// Two E4M3 bytes of a 32-bit word -> two fp16 (exact: every finite E4M3
-// value, subnormals included, is a normal fp16).
-__device__ __forceinline__ h2 e4m3x2_lo(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-}
-__device__ __forceinline__ h2 e4m3x2_hi(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
-}
-
-// Eight E2M1 codes (element 2j in bits 3:0 of byte j) times one fp16 scale.
-__device__ __forceinline__ h8 decode8(uint32_t w, _Float16 s) {
-    const h2 ss = {s, s};
-    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
-    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
-    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
-    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
-    return h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// FP32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t to_bf16(float x) {
-    __bf16 b = (__bf16)x;
-    return __builtin_bit_cast(uint16_t, b);
-}
-
-// One accumulator element read out of the AGPR it lives in.  Done in asm so
-// the accumulators stay in AGPRs until their block is stored (otherwise the
-// compiler copies the whole accumulator file to VGPRs at once).  Only for
-// accumulators that come straight from the MFMAs.
-__device__ __forceinline__ float acc_read(float x) {
-    float r;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
-    return r;
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int s) {
-    return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
-}
-
-// Scale of MFMA sub-step s (0..3) from the pair (block of words 0-1, block of
-// words 2-3).  Taken by value: selecting between two array elements by
-// reference would keep the array in private memory.
-__device__ __forceinline__ _Float16 scale_of(h2 pair, int s) {
-    return s < 2 ? pair[0] : pair[1];
-}
-// ---------------------------------------------------------------------------
-// Split-K hand-off between workgroups.
-//
-// Partial sums are written and read with relaxed device-scope atomic stores
-// and loads (on gfx950 these are plain stores/loads with the device-coherence
-// bit, so no cache-wide write-back or invalidate is needed); the writer waits
-// for its stores to complete before it increments the tile's arrival counter,
-// and the last arrival reads the partials only after its increment returned.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void publish(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float fetch(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Increments the counter once all earlier stores of the calling wave have
-// completed; returns the counter's previous value.
-__device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
-    __builtin_amdgcn_s_waitcnt(0);
-    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void reset_counter(uint32_t* counter) {
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until at most N vector-memory instructions of this wave are in flight
-// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-// Wait until at most `steps` (0 .. 6, wave-uniform) groups of L vector-memory
-// instructions are in flight.
-template <int L>
-__device__ __forceinline__ void wait_steps(int steps) {
-    switch (steps) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<L>(); break;
-        case 2: wait_vmcnt<(2 * L < 64 ? 2 * L : 0)>(); break;
-        case 3: wait_vmcnt<(3 * L < 64 ? 3 * L : 0)>(); break;
-        case 4: wait_vmcnt<(4 * L < 64 ? 4 * L : 0)>(); break;
-        case 5: wait_vmcnt<(5 * L < 64 ? 5 * L : 0)>(); break;
-        default: wait_vmcnt<(6 * L < 64 ? 6 * L : 0)>(); break;
-    }
-}
-
-typedef __attribute__((address_space(3))) uint8_t* lds_u8;
-
-// 32-bit LDS address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-    return (uint32_t)(uintptr_t)(lds_u8)(p);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
-// Direct HBM -> LDS copies (buffer_load ... lds): every lane fetches 16 (or
-// 4) bytes at voff + soff inside the buffer and the wave's 1024 (or 256)
-// bytes land contiguously at LDS address `lds` (wave-uniform, through M0).
-// Issued as inline assembly so that the compiler neither reorders LDS reads
-// around them nor inserts its own conservative wait for every LDS read; the
-// kernel waits for them explicitly with wait_vmcnt and orders LDS reuse with
-// barriers.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                      uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                     uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
-}
-// Workgroup barrier that is also a compiler barrier for memory operations
-// (it adds no wait for outstanding loads: those are waited for explicitly).
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // Large-M tile kernel.
@@ -1001,140 +873,6 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs a) {
 }
 
 
-// ---------------------------------------------------------------------------
-// Grouped skinny kernel: the experts of a mixture-of-experts layer in one
-// launch.  Group g multiplies rows [offsets[g], offsets[g+1]) of A (tokens
-// routed to expert g, typically about 16) by its own weight operand B_g; all
-// groups share N and K.  ("Peeling the Kernel Onion", sections "The Critical
-// Connection to Real Inference": 256 experts, 8 per token, about 16 tokens
-// per expert at 512 requests; "Knowledge Created and Its Impact": grouped
-// GEMMs to amortise the per-call overhead.)
-//
-// Workgroup: NB 16-row blocks of B_g (16 * NB columns of C) over the whole K
-// range, WAVES waves splitting the 128-element K units in turn, each with
-// the loads of UNITS units in flight (straight from HBM: B is used once).
-// A is taken in chunks of 16 rows; up to CH chunks share one pass over B.
-// Each A chunk is decoded once per K unit and feeds the
-// v_mfma_f32_16x16x32_f16 of all NB blocks (lane layout as in the skinny
-// kernel), so the decode of A is shared by 16 * NB columns.  Wave partials
-// are added in LDS in wave order.  The workgroups of one group are
-// consecutive and are kept on one XCD, so its A rows come from that XCD's L2
-// after the first read.  Offsets are clamped to [0, M] on the device, so a
-// malformed table cannot make the kernel read or write outside the buffers.
-// ---------------------------------------------------------------------------
-template <int WAVES, int CH, int UNITS, int NB>
-__global__ void __launch_bounds__(WAVES * 64) grouped_kernel(GroupedArgs a) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    int bid = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int blocks = a.Np / 16;                  // 16-row blocks of B per group
-    const int wgs = (blocks + NB - 1) / NB;        // workgroups per group
-    const int g = bid / wgs;
-    const int cb0 = (bid % wgs) * NB;              // first block of this workgroup
-    const int nb = min(NB, blocks - cb0);          // blocks of this workgroup
-    const int r0 = min(max(a.offsets[g], 0), a.M);
-    const int r1 = min(max(a.offsets[g + 1], r0), a.M);
-    if (r0 >= r1) return;
-
-    const int C = a.P / 2;  // 128-element K units
-    const int r16 = lane & 15;
-    const int grp = lane >> 4;
-    const int pl = grp >> 1, half = grp & 1;
-    const uint8_t* bc = a.b_codes + (int64_t)g * a.P * a.Np * 32;
-    const uint8_t* bsc = a.b_scales + (int64_t)g * a.P * a.Np * 4;
-
-    __shared__ f4v red[WAVES][CH * NB][64];
-    for (int m0 = r0; m0 < r1; m0 += 16 * CH) {
-        const int nch = min(CH, (r1 - m0 + 15) / 16);
-        f4v acc[CH][NB];
-#pragma unroll
-        for (int ch = 0; ch < CH; ++ch)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) acc[ch][j] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int base = wave; base < C; base += WAVES * UNITS) {
-            uint4 bw[UNITS][NB], aw[UNITS][CH];
-            uint32_t bs[UNITS][NB], as[UNITS][CH];
-#pragma unroll
-            for (int u = 0; u < UNITS; ++u) {
-                const int c = base + WAVES * u;
-                const int64_t panel = 2 * (int64_t)c + pl;
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    bw[u][j] = uint4{0u, 0u, 0u, 0u};
-                    bs[u][j] = 0u;
-                    if (c < C && j < nb) {
-                        const int64_t bo = panel * a.Np + (cb0 + j) * 16 + r16;
-                        bw[u][j] = *reinterpret_cast<const uint4*>(bc + bo * 32 + half * 16);
-                        bs[u][j] = *reinterpret_cast<const uint16_t*>(bsc + bo * 4 + half * 2);
-                    }
-                }
-#pragma unroll
-                for (int ch = 0; ch < CH; ++ch) {
-                    aw[u][ch] = uint4{0u, 0u, 0u, 0u};
-                    as[u][ch] = 0u;
-                    const int row = m0 + ch * 16 + r16;
-                    if (c < C && ch < nch && row < r1) {
-                        const int64_t ao = panel * a.Mp + row;
-                        aw[u][ch] = *reinterpret_cast<const uint4*>(a.a_codes + ao * 32 + half * 16);
-                        as[u][ch] = *reinterpret_cast<const uint16_t*>(a.a_scales + ao * 4 + half * 2);
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < UNITS; ++u) {
-                h2 sbh[NB], sah[CH];
-#pragma unroll
-                for (int j = 0; j < NB; ++j) sbh[j] = e4m3x2_lo(bs[u][j]);
-#pragma unroll
-                for (int ch = 0; ch < CH; ++ch) sah[ch] = e4m3x2_lo(as[u][ch]);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    h8 bv[NB];
-#pragma unroll
-                    for (int j = 0; j < NB; ++j) bv[j] = decode8(word_of(bw[u][j], s), scale_of(sbh[j], s));
-#pragma unroll
-                    for (int ch = 0; ch < CH; ++ch) {
-                        if (ch < nch) {
-                            const h8 av = decode8(word_of(aw[u][ch], s), scale_of(sah[ch], s));
-#pragma unroll
-                            for (int j = 0; j < NB; ++j)
-                                acc[ch][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[j], acc[ch][j], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-        }
-
-        // Add the wave partials in wave order; wave w finishes the (chunk,
-        // block) pairs w, w + WAVES, ...
-        __syncthreads();  // the previous pass's reads of red are done
-#pragma unroll
-        for (int ch = 0; ch < CH; ++ch)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) red[wave][ch * NB + j][lane] = acc[ch][j];
-        __syncthreads();
-        for (int idx = wave; idx < nch * NB; idx += WAVES) {
-            const int ch = idx / NB, j = idx % NB;
-            if (j >= nb) continue;
-            f4v sum = red[0][idx][lane];
-#pragma unroll
-            for (int w = 1; w < WAVES; ++w) sum += red[w][idx][lane];
-            // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + v.
-            const int col = (cb0 + j) * 16 + r16;
-            if (col < a.N) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = m0 + ch * 16 + 4 * grp + v;
-                    if (row < r1) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * sum[v]);
-                }
-            }
-        }
-    }
-}
-
 }  // namespace
 
 size_t tile_partial_floats(int cfg, const GemmArgs& a) {
@@ -1243,12 +981,5 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
 }
 
 
-hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream) {
-    const int blocks = a.Np / 16;
-    const dim3 grid((unsigned)((int64_t)a.G * ((blocks + kGroupedBlocks - 1) / kGroupedBlocks)));
-    hipLaunchKernelGGL((grouped_kernel<kGroupedWaves, kGroupedChunks, kGroupedUnits, kGroupedBlocks>), grid, dim3(kGroupedWaves * 64), 0,
-                       stream, a);
-    return hipGetLastError();
-}
 
 }  // namespace nvfp4
