@@ -291,3 +291,99 @@ int oracle_gemm_points(const uint8_t* a_codes, const uint8_t* a_scales, const ui
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * NVFP4 quantisation of fp32 rows: the step before the GEMM, activations
+ * quantised per 16-element block along K into E2M1 codes and one E4M3 scale
+ * per block (format: "Peeling the Kernel Onion", section "The Benchmark
+ * Design"; the recipe is the plainest reading of "scale = E4M3(amax / 6),
+ * codes = round-to-nearest-even E2M1").  Readings:
+ *   - amax / 6 and x / scale are single fp32 operations (correctly rounded);
+ *   - the scale byte is the non-negative finite E4M3 value nearest to
+ *     amax / 6, ties to the even byte; past 448 it saturates to 448;
+ *   - a block whose scale is 0 (all zeros, or amax / 6 below half the
+ *     smallest E4M3 subnormal) gets magnitude-0 codes;
+ *   - a code is the E2M1 magnitude nearest to |x / scale|, ties to the even
+ *     code, past 6 saturating to 6, with the sign bit of x (so -0.0 and
+ *     negative values that round to 0 give code 0x8);
+ *   - non-finite inputs are outside the contract (infinities saturate).
+ * Both roundings pick the nearest entry of the value table by exhaustive
+ * search, so the code states the definition directly.
+ * ------------------------------------------------------------------------- */
+static unsigned quant_scale_byte(float amax) {
+    const float t = amax / 6.0f;
+    if (t >= 448.0f) return 0x7E;     /* at or past the largest finite value */
+    unsigned best = 0;
+    double bestd = INFINITY;
+    for (unsigned b = 0; b <= 0x7E; ++b) {
+        const double v = oracle_e4m3(b);
+#if ORACLE_MUTANT == 12
+        /* planted mistake: truncation (largest value not above t) */
+        if (v <= (double)t) best = b;
+        continue;
+#endif
+        const double d = fabs(v - (double)t);
+        if (d < bestd || (d == bestd && (b & 1u) == 0)) {
+            best = b;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+static unsigned quant_code(float x, float s) {
+    unsigned sign = signbit(x) ? 8u : 0u;
+    if (s == 0.0f) return sign;
+#if ORACLE_MUTANT == 15
+    const float y = x * (1.0f / s);   /* planted mistake: reciprocal multiply */
+#else
+    const float y = x / s;
+#endif
+    const double ay = fabs((double)y);
+    if (ay >= 6.0) return sign | 7u;  /* at or past the largest magnitude */
+    unsigned best = 0;
+    double bestd = INFINITY;
+    for (unsigned c = 0; c < 8; ++c) {
+        const double d = fabs(oracle_e2m1(c) - ay);
+#if ORACLE_MUTANT == 13
+        /* planted mistake: ties away from zero */
+        if (d < bestd || d == bestd) {
+#else
+        if (d < bestd || (d == bestd && (c & 1u) == 0)) {
+#endif
+            best = c;
+            bestd = d;
+        }
+    }
+#if ORACLE_MUTANT == 14
+    if (best == 0) sign = 0;          /* planted mistake: zero codes lose the sign */
+#endif
+    return sign | best;
+}
+
+/* x: rows x K fp32 values, row stride ld (>= K) elements; codes [rows][K/2]
+ * (element 2j in bits 3:0 of byte j), scales [rows][K/16].  Returns 0, or -1
+ * for bad sizes. */
+int oracle_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, uint8_t* codes,
+                    uint8_t* scales) {
+    if (rows < 0 || K < 0 || K % 16 != 0 || ld < K) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t blk = 0; blk < K / 16; ++blk) {
+            const float* v = x + r * ld + blk * 16;
+            float amax = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                const float a = fabsf(v[i]);
+                if (a > amax) amax = a;
+            }
+            const unsigned sb = quant_scale_byte(amax);
+            scales[r * (K / 16) + blk] = (uint8_t)sb;
+            const float s = (float)oracle_e4m3(sb);
+            for (int i = 0; i < 16; i += 2) {
+                const unsigned c0 = quant_code(v[i], s), c1 = quant_code(v[i + 1], s);
+                codes[r * (K / 2) + blk * 8 + i / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+    }
+    return 0;
+}

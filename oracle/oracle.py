@@ -64,6 +64,8 @@ def _setup(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_gemm.restype = ctypes.c_int
     lib.oracle_gemm.argtypes = [_u8p, _u8p, _u8p, _u8p, ctypes.c_float, _i64, _i64, _i64,
                                 _u16p, _f64p, _f64p]
+    lib.oracle_quantize.restype = ctypes.c_int
+    lib.oracle_quantize.argtypes = [ctypes.POINTER(ctypes.c_float), _i64, _i64, _i64, _u8p, _u8p]
     lib.oracle_gemm_points.restype = ctypes.c_int
     lib.oracle_gemm_points.argtypes = [_u8p, _u8p, _u8p, _u8p, ctypes.c_float, _i64, _i64, _i64,
                                        _i64p, _i64p, _i64, _u16p, _f64p, _f64p]
@@ -160,6 +162,21 @@ class Oracle:
             raise ValueError(f"oracle_gemm_points failed with {rc}")
         return out, exact, mag
 
+
+    def quantize(self, x: np.ndarray):
+        """fp32 [rows, K] -> (codes uint8 [rows, K/2], scales uint8 [rows, K/16]):
+        per 16-element block, scale = E4M3 nearest-even of fp32(amax / 6)
+        (saturating at 448), code = E2M1 nearest-even of fp32(x / scale) with
+        the sign of x (see oracle_quantize in the C source)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        rows, K = x.shape
+        codes = np.zeros((rows, K // 2), np.uint8)
+        scales = np.zeros((rows, K // 16), np.uint8)
+        rc = self.lib.oracle_quantize(x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), rows, K, K,
+                                      _ptr(codes, _u8p), _ptr(scales, _u8p))
+        if rc != 0:
+            raise ValueError(f"oracle_quantize failed with {rc}")
+        return codes, scales
 
     def grouped_gemm(self, a_codes, a_scales, b_codes, b_scales, offsets, alpha: float = 1.0):
         """Grouped GEMM (mixture-of-experts layer) by its definition: group g
