@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grouped-only", action="store_true",
                     help="time only the grouped (all experts in one launch) workload")
+    ap.add_argument("--quantize-only", action="store_true",
+                    help="time only the fp32 -> NVFP4 quantisation shapes")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--cold", action="store_true",
@@ -295,6 +297,50 @@ def grouped_line(nv, torch, steps, warmup):
                     "pages_tflops_other_gpu": None}
 
 
+QUANT_SHAPES = [(16, 6144), (16384, 8192)]   # decode activations of one expert; saturation-shape A
+
+
+def quantize_bytes(rows: int, K: int) -> int:
+    """fp32 input read once plus the packed output written (padding included)."""
+    rp = -(-rows // 16) * 16
+    kp = -(-K // 128) * 128
+    return rows * K * 4 + rp * kp // 2 + rp * kp // 16
+
+
+def quantize_line(nv, torch, rows, K, steps, warmup):
+    """Per-call time of nvfp4_quantize on a resident fp32 tensor, graph-replayed."""
+    g = np.random.Generator(np.random.PCG64(rows + K))
+    x = torch.from_numpy(g.standard_normal((rows, K), dtype=np.float32)).to("cuda")
+    out = nv.quantize(x)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            nv.quantize(x, out=out, stream=stream)
+    stream.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=stream):
+        cap = torch.cuda.current_stream()
+        for _ in range(steps):
+            nv.quantize(x, out=out, stream=cap)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        gr.replay()
+        start.record(stream)
+        gr.replay()
+        stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    b = quantize_bytes(rows, K)
+    ach = b / (ms * 1e-3) / 1e9
+    del gr
+    return f"quantize_{rows}x{K}", {
+        "rows": rows, "K": K, "ms": ms, "gelem_per_s": rows * K / (ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
+                     "frac": ach / HBM_GBPS, "traffic": None, "algorithmic_bytes_per_launch": b},
+        "path": "quantize"}
+
+
 def cpu_baseline(cfg, ops, budget_s):
     from oracle import oracle as orc
     o = orc.load()
@@ -339,6 +385,11 @@ def main():
         copy_calibration(args.steps)
         return
 
+    if args.quantize_only:
+        for rows, K in QUANT_SHAPES:
+            name, q = quantize_line(nv, torch, rows, K, args.steps, args.warmup)
+            print(json.dumps({"workload": name, **q}), flush=True)
+        return
     if args.grouped_only:
         name, g = grouped_line(nv, torch, args.steps, args.warmup)
         print(json.dumps({"workload": name, **g}), flush=True)
@@ -379,6 +430,10 @@ def main():
         torch.cuda.empty_cache()
         name, g = grouped_line(nv, torch, args.steps, args.warmup)
         per[name] = g
+        for rows, K in QUANT_SHAPES:
+            torch.cuda.empty_cache()
+            name, q = quantize_line(nv, torch, rows, K, args.steps, args.warmup)
+            per[name] = q
         for c in synth.CONFIGS:
             if c.index == cfg.index:
                 continue

@@ -37,7 +37,7 @@ PATH_GEMV = 4
 
 EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_pack",
            "nvfp4_unpack", "nvfp4_init", "nvfp4_shutdown", "nvfp4_gemm",
-           "nvfp4_gemm_with_path", "nvfp4_plan", "nvfp4_grouped_gemm"]
+           "nvfp4_gemm_with_path", "nvfp4_plan", "nvfp4_grouped_gemm", "nvfp4_quantize"]
 
 
 class Nvfp4Error(RuntimeError):
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemm_with_path.restype = ctypes.c_int
         L.nvfp4_gemm_with_path.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
                                            _i64, ctypes.c_int, ctypes.c_int, _vp]
+        L.nvfp4_quantize.restype = ctypes.c_int
+        L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
         L.nvfp4_grouped_gemm.restype = ctypes.c_int
         L.nvfp4_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float, _vp, _i64,
                                          _i64, _i64, _vp]
@@ -290,4 +292,26 @@ def grouped_gemm(a: PackedOperand, b: PackedGroups, row_offsets, alpha: float = 
                                   float(alpha), out.data_ptr(), M, N, K, _stream_handle(stream))
     if st:
         raise Nvfp4Error(st, f"nvfp4_grouped_gemm(G={b.groups}, M={M}, N={N}, K={K})")
+    return out
+
+
+def quantize(x, out: PackedOperand | None = None, stream=None) -> PackedOperand:
+    """Quantise a 2-D fp32 device tensor (rows x K, unit stride along K, row
+    stride a multiple of 4 elements) to NVFP4 in the packed layout
+    (nvfp4_quantize); returns the PackedOperand (or fills ``out``)."""
+    import torch
+    if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 tensor with unit stride along K")
+    rows, K = x.shape
+    if out is None:
+        cb, sb = packed_size(rows, K)
+        out = PackedOperand(torch.empty(cb, dtype=torch.uint8, device=x.device),
+                            torch.empty(sb, dtype=torch.uint8, device=x.device), rows, K)
+    elif out.rows != rows or out.K != K:
+        raise ValueError("out has the wrong shape")
+    out.check("out")
+    st = lib().nvfp4_quantize(x.data_ptr(), rows, K, x.stride(0), out.codes.data_ptr(),
+                              out.scales.data_ptr(), _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_quantize(rows={rows}, K={K}, ld={x.stride(0)})")
     return out

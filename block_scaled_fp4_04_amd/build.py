@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4.so")
 SOURCES = [os.path.join(CSRC, "nvfp4_api.cpp"), os.path.join(CSRC, "nvfp4_kernels.hip"),
-           os.path.join(CSRC, "nvfp4_grouped.hip")]
+           os.path.join(CSRC, "nvfp4_grouped.hip"), os.path.join(CSRC, "nvfp4_quantize.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -364,6 +364,32 @@ int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void*
                     stream);
 }
 
+int nvfp4_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
+                   void* packed_scales, void* stream) {
+    if (!x || !packed_codes || !packed_scales || !valid_rows_k(rows, K) || ld < K || ld % 4 != 0)
+        return NVFP4_ERR_INVALID_VALUE;
+    if (!aligned16(x) || !aligned16(packed_codes) || !aligned16(packed_scales))
+        return NVFP4_ERR_MISALIGNED;
+    const int64_t Rp = round_up(rows, kRowPad);
+    const int64_t P = num_panels(K);
+    if (Rp * 16 > INT32_MAX || P > 65535) return NVFP4_ERR_INVALID_VALUE;  // grid size
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return NVFP4_ERR_HIP;
+    const int dst = check_device(device);
+    if (dst != NVFP4_OK) return dst;
+    QuantArgs a{};
+    a.x = x;
+    a.codes = static_cast<uint8_t*>(packed_codes);
+    a.scales = static_cast<uint8_t*>(packed_scales);
+    a.ld = ld;
+    a.rows = (int)rows;
+    a.K = (int)K;
+    a.Rp = (int)Rp;
+    a.P = (int)P;
+    const hipError_t e = launch_quantize(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 int nvfp4_grouped_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
                        const void* b_scales, const int32_t* row_offsets, int64_t groups,
                        float alpha, void* out, int64_t M, int64_t N, int64_t K, void* stream) {

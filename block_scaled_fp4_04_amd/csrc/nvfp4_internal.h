@@ -87,4 +87,15 @@ struct GroupedArgs {
 };
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);
 
+// NVFP4 quantisation of fp32 rows into the packed operand layout.
+struct QuantArgs {
+    const float* x;   // rows x K values, row stride ld elements
+    uint8_t* codes;   // packed codes  [P][Rp][32]
+    uint8_t* scales;  // packed scales [P][Rp][4]
+    int64_t ld;
+    int rows, K;
+    int Rp, P;        // padded rows, 64-element panels
+};
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
 }  // namespace nvfp4

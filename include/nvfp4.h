@@ -126,6 +126,27 @@ int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void*
                          const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
                          int64_t K, int path, int split_k, void* stream);
 
+/* NVFP4 quantisation of fp32 rows straight into the packed layout (the step
+ * before the GEMM for activations; "Peeling the Kernel Onion", section "The
+ * Benchmark Design", for the format).  Per 16-element block of a row:
+ *   scale = E4M3 value nearest to fp32(amax / 6), ties to the even byte,
+ *           saturating at 448;
+ *   code  = E2M1 magnitude nearest to fp32(x / scale), ties to the even code,
+ *           saturating at 6, with the sign bit of x (a block whose scale is 0
+ *           keeps only the sign bits).
+ *   x             : DEVICE fp32, rows x K values, row stride ld elements
+ *                   (ld >= K, ld % 4 == 0); the buffer holds at least
+ *                   (rows - 1) * ld + K values
+ *   packed_codes,
+ *   packed_scales : DEVICE, nvfp4_packed_size(rows, K) bytes each; every byte
+ *                   is written (padding rows and panels as zeros), ready for
+ *                   nvfp4_gemm as A (rows = M) or B (rows = N)
+ * Same size rules as nvfp4_pack; 16-byte aligned pointers (else
+ * NVFP4_ERR_MISALIGNED); non-finite inputs are outside the contract
+ * (infinities saturate).  Asynchronous on `stream`; no allocation. */
+int nvfp4_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
+                   void* packed_scales, void* stream);
+
 /* Grouped GEMM for mixture-of-experts layers: `groups` weight operands B_g
  * (each N x K) share one launch; group g owns rows
  * row_offsets[g] .. row_offsets[g+1]-1 of A and of C:

@@ -137,6 +137,17 @@ def test_pack_groups_concatenates_per_group_packing():
         assert np.array_equal(ps[i * sb:(i + 1) * sb], s1)
 
 
+def test_quantize_rejects_bad_arguments_before_launch():
+    q = nv.lib().nvfp4_quantize
+    assert q(None, 4, 64, 64, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE
+    assert q(0x3000, 0, 64, 64, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE
+    assert q(0x3000, 4, 24, 24, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE   # K % 16
+    assert q(0x3000, 4, 64, 32, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE   # ld < K
+    assert q(0x3000, 4, 64, 66, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE   # ld % 4
+    assert q(0x3004, 4, 64, 64, 0x1000, 0x2000, None) == nv.ERR_MISALIGNED
+    assert q(0x3000, 4, 64, 64, 0x1008, 0x2000, None) == nv.ERR_MISALIGNED
+
+
 def test_python_gemm_rejects_k_mismatch():
     a = nv.PackedOperand(None, None, 4, 128)
     b = nv.PackedOperand(None, None, 4, 256)
