@@ -27,12 +27,17 @@ __device__ __forceinline__ h2 e4m3x2_hi(uint32_t w) {
 }
 
 // Eight E2M1 codes (element 2j in bits 3:0 of byte j) times one fp16 scale.
+// The four converts are kept apart from the four multiplies (the empty asm
+// stops the scheduler from pairing each multiply right after its convert,
+// which made every multiply wait on the result just produced).
 __device__ __forceinline__ h8 decode8(uint32_t w, _Float16 s) {
     const h2 ss = {s, s};
-    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
-    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
-    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
-    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+    h2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    h2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    h2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    h2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+    asm("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
+    const h2 p0 = c0 * ss, p1 = c1 * ss, p2 = c2 * ss, p3 = c3 * ss;
     return h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
