@@ -47,6 +47,8 @@ def parse():
                     help="time only the grouped (all experts in one launch) workload")
     ap.add_argument("--quantize-only", action="store_true",
                     help="time only the fp32 -> NVFP4 quantisation shapes")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode step: eager calls against one recorded sequence")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--cold", action="store_true",
@@ -341,6 +343,73 @@ def quantize_line(nv, torch, rows, K, steps, warmup):
         "path": "quantize"}
 
 
+DECODE_LAYERS = 8
+
+
+def decode_sequence_line(nv, torch, steps, warmup):
+    """A decode step of DECODE_LAYERS layers, each quantising the fp32
+    activations and running the attention projection (1 x 768 x 6144) and
+    the MoE up-projection share (16 x 256 x 6144) with its own weights:
+    4 calls per layer.  Timed as eager calls from Python (host launch gaps
+    included: the device waits for them) and as one recorded sequence
+    (nvfp4_sequence_launch) per step, both between HIP events."""
+    K = 6144
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(2026)
+    x1 = torch.randn((1, K), generator=g, device=dev)
+    x16 = torch.randn((16, K), generator=g, device=dev)
+    a1 = nv.quantize(x1)
+    a16 = nv.quantize(x16)
+    layers = []
+    for _ in range(DECODE_LAYERS):
+        w_attn = nv.quantize(torch.randn((768, K), generator=g, device=dev) * 0.02)
+        w_up = nv.quantize(torch.randn((256, K), generator=g, device=dev) * 0.02)
+        layers.append((w_attn, w_up, torch.empty((1, 768), dtype=torch.bfloat16, device=dev),
+                       torch.empty((16, 256), dtype=torch.bfloat16, device=dev)))
+    stream = torch.cuda.Stream()
+
+    def eager_step():
+        for w_attn, w_up, o1, o16 in layers:
+            nv.quantize(x1, out=a1, stream=stream)
+            nv.gemm(a1, w_attn, 0.5, out=o1, stream=stream)
+            nv.quantize(x16, out=a16, stream=stream)
+            nv.gemm(a16, w_up, 1.0, out=o16, stream=stream)
+
+    seq = nv.Sequence()
+    for w_attn, w_up, o1, o16 in layers:
+        seq.add_quantize(x1, a1)
+        seq.add_gemm(a1, w_attn, o1, 0.5)
+        seq.add_quantize(x16, a16)
+        seq.add_gemm(a16, w_up, o16, 1.0)
+    seq.finalize()
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, warmup)):
+                fn()
+        stream.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            for _ in range(steps):
+                fn()
+            stop.record(stream)
+        stop.synchronize()
+        return start.elapsed_time(stop) * 1000.0 / steps   # us per step
+
+    eager_us = timed(eager_step)
+    seq_us = timed(lambda: seq.launch(stream))
+    calls = seq.calls
+    seq.close()
+    return "decode_step_sequence", {
+        "layers": DECODE_LAYERS, "calls_per_step": calls,
+        "calls": "per layer: quantize 1x6144, GEMM 1x768x6144, quantize 16x6144, GEMM 16x256x6144",
+        "us_per_step_eager": eager_us, "us_per_step_sequence": seq_us,
+        "us_per_call_eager": eager_us / calls, "us_per_call_sequence": seq_us / calls,
+        "speedup": eager_us / seq_us, "path": "sequence (one HIP graph launch per step)"}
+
+
 def cpu_baseline(cfg, ops, budget_s):
     from oracle import oracle as orc
     o = orc.load()
@@ -390,6 +459,10 @@ def main():
             name, q = quantize_line(nv, torch, rows, K, args.steps, args.warmup)
             print(json.dumps({"workload": name, **q}), flush=True)
         return
+    if args.decode_only:
+        name, d = decode_sequence_line(nv, torch, args.steps, args.warmup)
+        print(json.dumps({"workload": name, **d}), flush=True)
+        return
     if args.grouped_only:
         name, g = grouped_line(nv, torch, args.steps, args.warmup)
         print(json.dumps({"workload": name, **g}), flush=True)
@@ -430,6 +503,9 @@ def main():
         torch.cuda.empty_cache()
         name, g = grouped_line(nv, torch, args.steps, args.warmup)
         per[name] = g
+        torch.cuda.empty_cache()
+        name, d = decode_sequence_line(nv, torch, args.steps, args.warmup)
+        per[name] = d
         for rows, K in QUANT_SHAPES:
             torch.cuda.empty_cache()
             name, q = quantize_line(nv, torch, rows, K, args.steps, args.warmup)

@@ -5,6 +5,11 @@ behind the C ABI of ``include/nvfp4.h``; PyTorch supplies device memory and
 the current stream.  There is no fallback: if the library is missing, every
 call raises.
 
+On first use the library is given the tuned plan table shipped beside it
+(``plan_table_gfx950.json``, written by ``python -m
+block_scaled_fp4_04_amd.tune``); the environment variable NVFP4_PLAN_TABLE
+names another table file, or ``off`` for the library's own rules only.
+
     C = alpha * (A . B^T)
 A is M x K and B is N x K, both E2M1 codes packed two per byte with one
 E4M3 scale per 16 elements, alpha is FP32 and C is bfloat16 M x N ("Peeling
@@ -15,12 +20,14 @@ from __future__ import annotations
 
 import ctypes
 import os
+import warnings
 from dataclasses import dataclass
 
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+PLAN_TABLE_PATH = os.path.join(_PKG, "plan_table_gfx950.json")
 
 OK = 0
 ERR_INVALID_VALUE = 1
@@ -28,16 +35,31 @@ ERR_MISALIGNED = 2
 ERR_UNSUPPORTED = 3
 ERR_HIP = 4
 ERR_ALLOC = 5
+ERR_CAPTURE = 6
+ERR_STATE = 7
 
 PATH_AUTO = 0
 PATH_TILE = 1
 PATH_SKINNY = 2
 PATH_WSPLIT = 3
 PATH_GEMV = 4
+PATH_NAMES = {PATH_TILE: "tile", PATH_SKINNY: "skinny", PATH_WSPLIT: "wsplit", PATH_GEMV: "gemv"}
+
+PLAN_HEURISTIC = 0
+PLAN_TABLE = 1
 
 EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_pack",
            "nvfp4_unpack", "nvfp4_init", "nvfp4_shutdown", "nvfp4_gemm",
-           "nvfp4_gemm_with_path", "nvfp4_plan", "nvfp4_grouped_gemm", "nvfp4_quantize"]
+           "nvfp4_gemm_with_plan", "nvfp4_plan", "nvfp4_plan_table_load",
+           "nvfp4_plan_table_clear", "nvfp4_build_id", "nvfp4_grouped_gemm", "nvfp4_quantize",
+           "nvfp4_sequence_create", "nvfp4_sequence_add_gemm", "nvfp4_sequence_add_grouped_gemm",
+           "nvfp4_sequence_add_quantize", "nvfp4_sequence_finalize", "nvfp4_sequence_launch",
+           "nvfp4_sequence_destroy"]
+
+
+class _PlanT(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("split_k", ctypes.c_int32), ("source", ctypes.c_int32)]
 
 
 class Nvfp4Error(RuntimeError):
@@ -75,19 +97,52 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_shutdown.restype = None
         L.nvfp4_gemm.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i64, _vp]
-        L.nvfp4_gemm_with_path.restype = ctypes.c_int
-        L.nvfp4_gemm_with_path.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
-                                           _i64, ctypes.c_int, ctypes.c_int, _vp]
+        L.nvfp4_gemm_with_plan.restype = ctypes.c_int
+        L.nvfp4_gemm_with_plan.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
+                                           _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
         L.nvfp4_quantize.restype = ctypes.c_int
         L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
         L.nvfp4_grouped_gemm.restype = ctypes.c_int
         L.nvfp4_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float, _vp, _i64,
                                          _i64, _i64, _vp]
-        ip = ctypes.POINTER(ctypes.c_int)
         L.nvfp4_plan.restype = ctypes.c_int
-        L.nvfp4_plan.argtypes = [_i64, _i64, _i64, ip, ip, ip, ip]
+        L.nvfp4_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_PlanT)]
+        L.nvfp4_plan_table_load.restype = ctypes.c_int
+        L.nvfp4_plan_table_load.argtypes = [ctypes.c_char_p, ctypes.POINTER(_i64),
+                                            ctypes.POINTER(ctypes.c_int)]
+        L.nvfp4_plan_table_clear.restype = None
+        L.nvfp4_build_id.restype = ctypes.c_char_p
+        L.nvfp4_sequence_create.restype = ctypes.c_int
+        L.nvfp4_sequence_create.argtypes = [ctypes.POINTER(_vp)]
+        L.nvfp4_sequence_add_gemm.restype = ctypes.c_int
+        L.nvfp4_sequence_add_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64,
+                                              _i64, _i64]
+        L.nvfp4_sequence_add_grouped_gemm.restype = ctypes.c_int
+        L.nvfp4_sequence_add_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                                      ctypes.c_float, _vp, _i64, _i64, _i64]
+        L.nvfp4_sequence_add_quantize.restype = ctypes.c_int
+        L.nvfp4_sequence_add_quantize.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp]
+        for f in ("nvfp4_sequence_finalize", "nvfp4_sequence_destroy"):
+            getattr(L, f).restype = ctypes.c_int
+            getattr(L, f).argtypes = [_vp]
+        L.nvfp4_sequence_launch.restype = ctypes.c_int
+        L.nvfp4_sequence_launch.argtypes = [_vp, _vp]
         _lib = L
+        load_default_plan_table()
     return _lib
+
+
+def load_default_plan_table() -> int:
+    """Give the library the table named by NVFP4_PLAN_TABLE, else the one
+    shipped beside it (if present); ``off`` loads none.  Returns the number
+    of entries loaded."""
+    table = os.environ.get("NVFP4_PLAN_TABLE", "")
+    if table.lower() == "off":
+        return 0
+    path = table or PLAN_TABLE_PATH
+    if not table and not os.path.exists(path):
+        return 0
+    return load_plan_table(path)[0]
 
 
 def status_string(status: int) -> str:
@@ -149,12 +204,36 @@ def unpack(packed_codes: np.ndarray, packed_scales: np.ndarray, rows: int, K: in
 
 
 def plan(M: int, N: int, K: int) -> dict:
-    p, s, tm, tn = (ctypes.c_int() for _ in range(4))
-    st = lib().nvfp4_plan(M, N, K, ctypes.byref(p), ctypes.byref(s), ctypes.byref(tm),
-                          ctypes.byref(tn))
+    """The plan nvfp4_gemm uses for the shape (path, tile, split-K, and
+    whether it came from the tuned table)."""
+    p = _PlanT()
+    st = lib().nvfp4_plan(M, N, K, ctypes.byref(p))
     if st:
         raise Nvfp4Error(st, "nvfp4_plan")
-    return {"path": p.value, "split_k": s.value, "tile_m": tm.value, "tile_n": tn.value}
+    return {"path": p.path, "split_k": p.split_k, "tile_m": p.tile_m, "tile_n": p.tile_n,
+            "source": p.source}
+
+
+def build_id() -> str:
+    return lib().nvfp4_build_id().decode()
+
+
+def load_plan_table(path: str) -> tuple[int, bool]:
+    """Load a tuned plan table (JSON) into the library; returns (entries,
+    same_build).  Warns when the table was timed on other kernels."""
+    n, same = _i64(), ctypes.c_int()
+    st = lib().nvfp4_plan_table_load(os.fsencode(path), ctypes.byref(n), ctypes.byref(same))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_plan_table_load({path})")
+    if not same.value:
+        warnings.warn(f"plan table {path} was timed on other kernels than build "
+                      f"{build_id()}; its choices are valid but may not be the fastest",
+                      stacklevel=2)
+    return n.value, bool(same.value)
+
+
+def clear_plan_table() -> None:
+    lib().nvfp4_plan_table_clear()
 
 
 def init(device: int = 0) -> None:
@@ -201,10 +280,12 @@ def _stream_handle(stream) -> int | None:
 
 
 def gemm(a: PackedOperand, b: PackedOperand, alpha: float = 1.0, out=None,
-         path: int = PATH_AUTO, split_k: int = 0, stream=None):
+         path: int = PATH_AUTO, split_k: int = 0, stream=None, tile: int = 0):
     """C = alpha * (A . B^T) as an M x N bfloat16 tensor on A's device.
-    Raises ValueError when A and B do not share K (a mismatch is an error,
-    not a silent result)."""
+    ``path``, ``tile`` and ``split_k`` force a launch plan as
+    nvfp4_gemm_with_plan does (0 = the library's choice).  Raises ValueError
+    when A and B do not share K (a mismatch is an error, not a silent
+    result)."""
     import torch
     if a.K != b.K:
         raise ValueError(f"K dimension mismatch: A has K={a.K}, B has K={b.K}")
@@ -215,9 +296,9 @@ def gemm(a: PackedOperand, b: PackedOperand, alpha: float = 1.0, out=None,
         raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
     a.check("a")
     b.check("b")
-    st = lib().nvfp4_gemm_with_path(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+    st = lib().nvfp4_gemm_with_plan(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
                                     b.scales.data_ptr(), float(alpha), out.data_ptr(), M, N, K,
-                                    int(path), int(split_k), _stream_handle(stream))
+                                    int(path), int(tile), int(split_k), _stream_handle(stream))
     if st:
         raise Nvfp4Error(st, f"nvfp4_gemm(M={M}, N={N}, K={K})")
     return out
@@ -315,3 +396,93 @@ def quantize(x, out: PackedOperand | None = None, stream=None) -> PackedOperand:
     if st:
         raise Nvfp4Error(st, f"nvfp4_quantize(rows={rows}, K={K}, ld={x.stride(0)})")
     return out
+
+
+class Sequence:
+    """A recorded sequence of NVFP4 calls replayed with one graph launch
+    (nvfp4_sequence_*): record with the add_* methods (fixed buffers; the
+    plans are chosen then), ``finalize()`` once, then ``launch()`` per step.
+    The tensors passed in are kept referenced for the sequence's lifetime."""
+
+    def __init__(self):
+        h = _vp()
+        st = lib().nvfp4_sequence_create(ctypes.byref(h))
+        if st:
+            raise Nvfp4Error(st, "nvfp4_sequence_create")
+        self._h = h
+        self._keep = []
+        self.calls = 0
+
+    def _check(self, st, what):
+        if st:
+            raise Nvfp4Error(st, what)
+        self.calls += 1
+
+    def add_gemm(self, a: PackedOperand, b: PackedOperand, out, alpha: float = 1.0) -> None:
+        import torch
+        if a.K != b.K:
+            raise ValueError(f"K dimension mismatch: A has K={a.K}, B has K={b.K}")
+        M, N = a.rows, b.rows
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
+        a.check("a")
+        b.check("b")
+        self._keep += [a, b, out]
+        self._check(lib().nvfp4_sequence_add_gemm(
+            self._h, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+            b.scales.data_ptr(), float(alpha), out.data_ptr(), M, N, a.K),
+            f"nvfp4_sequence_add_gemm(M={M}, N={N}, K={a.K})")
+
+    def add_grouped_gemm(self, a: PackedOperand, b: "PackedGroups", row_offsets, out,
+                         alpha: float = 1.0) -> None:
+        import torch
+        if a.K != b.K:
+            raise ValueError(f"K dimension mismatch: A has K={a.K}, B has K={b.K}")
+        M, N = a.rows, b.rows
+        if row_offsets.dtype != torch.int32 or row_offsets.numel() != b.groups + 1:
+            raise ValueError(f"row_offsets must be an int32 tensor of {b.groups + 1} entries")
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
+        a.check("a")
+        b.check("b")
+        self._keep += [a, b, row_offsets, out]
+        self._check(lib().nvfp4_sequence_add_grouped_gemm(
+            self._h, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+            b.scales.data_ptr(), row_offsets.data_ptr(), b.groups, float(alpha), out.data_ptr(),
+            M, N, a.K), f"nvfp4_sequence_add_grouped_gemm(G={b.groups}, M={M}, N={N})")
+
+    def add_quantize(self, x, out: PackedOperand) -> None:
+        import torch
+        if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
+            raise ValueError("x must be a 2-D float32 tensor with unit stride along K")
+        rows, K = x.shape
+        if out.rows != rows or out.K != K:
+            raise ValueError("out has the wrong shape")
+        out.check("out")
+        self._keep += [x, out]
+        self._check(lib().nvfp4_sequence_add_quantize(
+            self._h, x.data_ptr(), rows, K, x.stride(0), out.codes.data_ptr(),
+            out.scales.data_ptr()), f"nvfp4_sequence_add_quantize(rows={rows}, K={K})")
+
+    def finalize(self) -> None:
+        st = lib().nvfp4_sequence_finalize(self._h)
+        if st:
+            raise Nvfp4Error(st, "nvfp4_sequence_finalize")
+
+    def launch(self, stream=None) -> None:
+        st = lib().nvfp4_sequence_launch(self._h, _stream_handle(stream))
+        if st:
+            raise Nvfp4Error(st, "nvfp4_sequence_launch")
+
+    def close(self) -> None:
+        """Frees the graph and workspace (launches must have completed)."""
+        if self._h is not None:
+            lib().nvfp4_sequence_destroy(self._h)
+            self._h = None
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

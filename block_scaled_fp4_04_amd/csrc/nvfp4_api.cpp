@@ -1,6 +1,7 @@
 // nvfp4_api.cpp -- host side of the NVFP4 block-scaled GEMM library:
-// argument validation, the canonical <-> packed layout transform, path and
-// split-K planning, the per-(device, stream) split-K workspace, and launch.
+// argument validation, the canonical <-> packed layout transform, the
+// per-(device, stream) split-K workspace, and launch (planning is in
+// nvfp4_plan.cpp).
 //
 // The operation and its argument rules are those of include/nvfp4.h: C =
 // alpha * (A . B^T) on E2M1 codes with one E4M3 scale per 16 elements and a
@@ -18,7 +19,7 @@
 #include <utility>
 
 #include "nvfp4.h"
-#include "nvfp4_internal.h"
+#include "nvfp4_host.h"
 
 using namespace nvfp4;
 
@@ -66,13 +67,23 @@ struct Workspace {
 
 std::map<std::pair<int, void*>, Workspace> g_ws;
 
+bool capturing(void* stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) == hipSuccess &&
+           cs != hipStreamCaptureStatusNone;
+}
+
 // Makes sure the workspace of (device, stream) can hold the request.  Growing
 // it frees the old buffers (hipFree waits for work that may still use them)
 // and zero-fills the new counters; this happens only when a larger shape is
-// seen for the first time on that stream.
+// seen for the first time on that stream, and never while the stream is
+// being captured into a graph (NVFP4_ERR_CAPTURE: allocation and the
+// synchronous fill are not allowed there).
 int get_workspace(int device, void* stream, size_t floats, size_t counters, Workspace** out) {
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace& ws = g_ws[{device, stream}];
+    if ((floats > ws.partial_floats || counters > ws.counter_count) && capturing(stream))
+        return NVFP4_ERR_CAPTURE;
     if (floats > ws.partial_floats) {
         if (ws.partials) (void)hipFree(ws.partials);
         ws.partials = nullptr;
@@ -92,103 +103,38 @@ int get_workspace(int device, void* stream, size_t floats, size_t counters, Work
     return NVFP4_OK;
 }
 
-// ---- planning ---------------------------------------------------------------
-
-struct Plan {
-    int path;
-    int cfg;      // tile configuration (tile path)
-    int split_k;
-    int tiles_m, tiles_n;
-};
-
-constexpr int kCUs = 256;
-
-Plan make_plan(int64_t M, int64_t N, int64_t K, int path, int split_req) {
-    Plan p{};
-    const int64_t P = num_panels(K);
-    const int steps = (int)(P / 2);
-    if (path == NVFP4_PATH_AUTO && M <= 4) path = NVFP4_PATH_GEMV;
-    if (path == NVFP4_PATH_AUTO && M <= 16) path = NVFP4_PATH_SKINNY;
-    p.path = path;
-    if (path == NVFP4_PATH_GEMV) {
-        p.split_k = 1;
-        p.tiles_m = 1;
-        p.tiles_n = (int)(round_up(N, kRowPad) / 4);
-        return p;
+// Runs a prepared job eagerly on `stream` with that stream's workspace.
+int run_job(const Job& job, void* stream) {
+    int device = 0;
+    const int dst = current_device(&device);
+    if (dst != NVFP4_OK || job.empty) return dst;
+    float* partials = nullptr;
+    uint32_t* counters = nullptr;
+    if (job.floats || job.counters) {
+        Workspace* ws = nullptr;
+        const int wst = get_workspace(device, stream, job.floats, job.counters, &ws);
+        if (wst != NVFP4_OK) return wst;
+        partials = ws->partials;
+        counters = ws->counters;
     }
-    if (path == NVFP4_PATH_SKINNY) {
-        // One workgroup of kSkinnyWaves waves per 16 output columns covers the
-        // whole K range: the split-K hand-off costs more than it saves once
-        // there are 8 or more column groups (measured at 1x768x6144 and
-        // 16x256x6144).  Fewer groups split K (each wave keeps at least one
-        // 128-element work unit).
-        const int64_t groups = round_up(N, kRowPad) / 16;
-        int s = split_req;
-        if (s <= 0) {
-            s = (int)((8 + groups - 1) / groups);
-            const int cap = steps / kSkinnyWaves;
-            if (s > cap) s = cap;
-        }
-        if (s > steps) s = steps;
-        p.split_k = s < 1 ? 1 : s;
-        p.tiles_m = 1;
-        p.tiles_n = (int)groups;
-        return p;
-    }
-    if (path == NVFP4_PATH_AUTO) {
-        // Large shapes whose 256 x 256 tiles nearly fill the machine use the
-        // LDS-fed tile kernel; the rest use the kernel whose waves split K.
-        const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-        path = t256 >= (3 * kCUs) / 4 ? NVFP4_PATH_TILE : NVFP4_PATH_WSPLIT;
-        p.path = path;
-    }
-    if (path == NVFP4_PATH_WSPLIT) {
-        const int cfg = WSPLIT_64x64;
-        const TileShape s = wsplit_shape(cfg);
-        p.cfg = cfg;
-        p.tiles_m = (int)((M + s.bm - 1) / s.bm);
-        p.tiles_n = (int)((N + s.bn - 1) / s.bn);
-        const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-        int sk = split_req;
-        if (sk <= 0) {
-            // A workgroup (8 waves, ~236 VGPRs each) occupies a whole CU, so
-            // split K across workgroups only while every workgroup still has
-            // a CU of its own (a second round of workgroups costs more than
-            // the split saves), keeping at least one panel per wave.
-            sk = 1;
-            while (tiles * (sk + 1) <= kCUs && (int64_t)(sk + 1) * 8 <= 2 * steps) ++sk;
-        }
-        if (sk > steps) sk = steps;
-        p.split_k = sk < 1 ? 1 : sk;
-        return p;
-    }
-    // Tile path: largest tile that still gives a reasonably full machine,
-    // then split K until there are about two workgroups per CU.
-    int cfg = TILE_256x256;
-    for (int c : {TILE_256x256, TILE_128x128, TILE_64x64}) {
-        const TileShape s = tile_shape(c);
-        const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
-        cfg = c;
-        if (tiles >= kCUs) break;
-    }
-    const TileShape s = tile_shape(cfg);
-    p.cfg = cfg;
-    p.tiles_m = (int)((M + s.bm - 1) / s.bm);
-    p.tiles_n = (int)((N + s.bn - 1) / s.bn);
-    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-    int sk = split_req;
-    if (sk <= 0) {
-        sk = 1;
-        while (tiles * sk < kCUs && sk * 2 <= steps / 2) sk *= 2;
-    }
-    if (sk > steps) sk = steps;
-    p.split_k = sk < 1 ? 1 : sk;
-    return p;
+    const hipError_t e = launch_job(job, device, partials, counters, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
-             const void* b_scales, float alpha, void* out, int64_t M, int64_t N, int64_t K,
-             int path, int split_k, void* stream) {
+}  // namespace
+
+// ---- jobs ---------------------------------------------------------------------
+
+namespace nvfp4 {
+
+int current_device(int* device) {
+    if (hipGetDevice(device) != hipSuccess) return NVFP4_ERR_HIP;
+    return check_device(*device);
+}
+
+int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
+                 const void* b_scales, float alpha, void* out, int64_t M, int64_t N, int64_t K,
+                 int path, int tile, int split_k, Job* job) {
     if (!a_packed || !a_scales || !b_packed || !b_scales || !out) return NVFP4_ERR_INVALID_VALUE;
     if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim) return NVFP4_ERR_INVALID_VALUE;
     if (!valid_rows_k(1, K)) return NVFP4_ERR_INVALID_VALUE;
@@ -200,12 +146,11 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     if (path == NVFP4_PATH_SKINNY && M > 16) return NVFP4_ERR_UNSUPPORTED;
     if (path == NVFP4_PATH_GEMV && M > 4) return NVFP4_ERR_UNSUPPORTED;
 
-    int device = 0;
-    if (hipGetDevice(&device) != hipSuccess) return NVFP4_ERR_HIP;
-    const int dst = check_device(device);
-    if (dst != NVFP4_OK) return dst;
-
-    const Plan plan = make_plan(M, N, K, path, split_k);
+    *job = Job{};
+    job->kind = JOB_GEMM;
+    Plan& plan = job->plan;
+    const int pst = make_plan(M, N, K, path, tile, split_k, &plan);
+    if (pst != NVFP4_OK) return pst;
     if (plan.path == NVFP4_PATH_TILE) {
         // the tile kernel addresses each packed operand with 32-bit offsets
         const int64_t P = num_panels(K);
@@ -214,7 +159,7 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
             P * round_up(N, kRowPad) * kPanelCodeBytes >= limit)
             return NVFP4_ERR_UNSUPPORTED;
     }
-    GemmArgs a{};
+    GemmArgs& a = job->gemm;
     a.a_codes = static_cast<const uint8_t*>(a_packed);
     a.a_scales = static_cast<const uint8_t*>(a_scales);
     a.b_codes = static_cast<const uint8_t*>(b_packed);
@@ -229,30 +174,87 @@ int run_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
     a.split_k = plan.split_k;
     a.tiles_m = plan.tiles_m;
     a.tiles_n = plan.tiles_n;
-
-    const size_t floats = plan.path == NVFP4_PATH_GEMV     ? 0
-                          : plan.path == NVFP4_PATH_SKINNY ? skinny_partial_floats(a)
-                          : plan.path == NVFP4_PATH_WSPLIT ? wsplit_partial_floats(plan.cfg, a)
-                                                           : tile_partial_floats(plan.cfg, a);
-    const size_t counters = plan.path == NVFP4_PATH_GEMV     ? 0
-                            : plan.path == NVFP4_PATH_SKINNY ? skinny_counters(a)
-                                                             : tile_counters(plan.cfg, a);
-    if (floats || counters) {
-        Workspace* ws = nullptr;
-        const int wst = get_workspace(device, stream, floats, counters, &ws);
-        if (wst != NVFP4_OK) return wst;
-        a.partials = ws->partials;
-        a.counters = ws->counters;
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = plan.path == NVFP4_PATH_GEMV     ? launch_gemv(a, s)
-                         : plan.path == NVFP4_PATH_SKINNY ? launch_skinny(a, s)
-                         : plan.path == NVFP4_PATH_WSPLIT ? launch_wsplit(plan.cfg, a, s)
-                                                          : launch_tile(plan.cfg, a, device, s);
-    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    job->floats = plan.path == NVFP4_PATH_GEMV     ? 0
+                  : plan.path == NVFP4_PATH_SKINNY ? skinny_partial_floats(a)
+                  : plan.path == NVFP4_PATH_WSPLIT ? wsplit_partial_floats(plan.cfg, a)
+                                                   : tile_partial_floats(plan.cfg, a);
+    job->counters = plan.path == NVFP4_PATH_GEMV     ? 0
+                    : plan.path == NVFP4_PATH_SKINNY ? skinny_counters(a)
+                                                     : tile_counters(plan.cfg, a);
+    return NVFP4_OK;
 }
 
-}  // namespace
+int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_packed,
+                    const void* b_scales, const int32_t* row_offsets, int64_t groups, float alpha,
+                    void* out, int64_t M, int64_t N, int64_t K, Job* job) {
+    if (!a_packed || !a_scales || !b_packed || !b_scales || !row_offsets || !out)
+        return NVFP4_ERR_INVALID_VALUE;
+    if (M < 0 || N < 1 || M > kMaxDim || N > kMaxDim || groups < 1 || !valid_rows_k(1, K))
+        return NVFP4_ERR_INVALID_VALUE;
+    const int64_t Np = round_up(N, kRowPad);
+    if (groups * (Np / 16) > INT32_MAX) return NVFP4_ERR_INVALID_VALUE;
+    if (!aligned16(a_packed) || !aligned16(a_scales) || !aligned16(b_packed) ||
+        !aligned16(b_scales) || !aligned16(out) || (reinterpret_cast<uintptr_t>(row_offsets) & 3u))
+        return NVFP4_ERR_MISALIGNED;
+    *job = Job{};
+    job->kind = JOB_GROUPED;
+    job->empty = M == 0;  // no rows: nothing to compute or write
+    GroupedArgs& a = job->grouped;
+    a.a_codes = static_cast<const uint8_t*>(a_packed);
+    a.a_scales = static_cast<const uint8_t*>(a_scales);
+    a.b_codes = static_cast<const uint8_t*>(b_packed);
+    a.b_scales = static_cast<const uint8_t*>(b_scales);
+    a.offsets = row_offsets;
+    a.out = static_cast<uint16_t*>(out);
+    a.alpha = alpha;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.Mp = (int)round_up(M, kRowPad);
+    a.Np = (int)Np;
+    a.P = (int)num_panels(K);
+    a.G = (int)groups;
+    return NVFP4_OK;
+}
+
+int prepare_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
+                     void* packed_scales, Job* job) {
+    if (!x || !packed_codes || !packed_scales || !valid_rows_k(rows, K) || ld < K || ld % 4 != 0)
+        return NVFP4_ERR_INVALID_VALUE;
+    if (!aligned16(x) || !aligned16(packed_codes) || !aligned16(packed_scales))
+        return NVFP4_ERR_MISALIGNED;
+    const int64_t Rp = round_up(rows, kRowPad);
+    const int64_t P = num_panels(K);
+    if (Rp * 16 > INT32_MAX || P > 65535) return NVFP4_ERR_INVALID_VALUE;  // grid size
+    *job = Job{};
+    job->kind = JOB_QUANTIZE;
+    QuantArgs& a = job->quant;
+    a.x = x;
+    a.codes = static_cast<uint8_t*>(packed_codes);
+    a.scales = static_cast<uint8_t*>(packed_scales);
+    a.ld = ld;
+    a.rows = (int)rows;
+    a.K = (int)K;
+    a.Rp = (int)Rp;
+    a.P = (int)P;
+    return NVFP4_OK;
+}
+
+hipError_t launch_job(const Job& job, int device, float* partials, uint32_t* counters,
+                      hipStream_t s) {
+    if (job.empty) return hipSuccess;
+    if (job.kind == JOB_GROUPED) return launch_grouped(job.grouped, s);
+    if (job.kind == JOB_QUANTIZE) return launch_quantize(job.quant, s);
+    GemmArgs a = job.gemm;
+    a.partials = partials;
+    a.counters = counters;
+    const Plan& plan = job.plan;
+    return plan.path == NVFP4_PATH_GEMV     ? launch_gemv(a, s)
+           : plan.path == NVFP4_PATH_SKINNY ? launch_skinny(a, s)
+           : plan.path == NVFP4_PATH_WSPLIT ? launch_wsplit(plan.cfg, a, s)
+                                            : launch_tile(plan.cfg, a, device, s);
+}
+
+}  // namespace nvfp4
 
 extern "C" {
 
@@ -264,6 +266,8 @@ const char* nvfp4_status_string(int status) {
         case NVFP4_ERR_UNSUPPORTED: return "unsupported device or path for this shape";
         case NVFP4_ERR_HIP: return "HIP runtime error";
         case NVFP4_ERR_ALLOC: return "workspace allocation failed";
+        case NVFP4_ERR_CAPTURE: return "workspace needed while the stream is being captured";
+        case NVFP4_ERR_STATE: return "call not allowed in the object's current state";
         default: return "unknown status";
     }
 }
@@ -353,93 +357,33 @@ void nvfp4_shutdown(void) {
 int nvfp4_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
                const void* b_scales, float alpha, void* out, int64_t M, int64_t N, int64_t K,
                void* stream) {
-    return run_gemm(a_packed, a_scales, b_packed, b_scales, alpha, out, M, N, K,
-                    NVFP4_PATH_AUTO, 0, stream);
+    return nvfp4_gemm_with_plan(a_packed, a_scales, b_packed, b_scales, alpha, out, M, N, K,
+                                NVFP4_PATH_AUTO, 0, 0, stream);
 }
 
-int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void* b_packed,
+int nvfp4_gemm_with_plan(const void* a_packed, const void* a_scales, const void* b_packed,
                          const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
-                         int64_t K, int path, int split_k, void* stream) {
-    return run_gemm(a_packed, a_scales, b_packed, b_scales, alpha, out, M, N, K, path, split_k,
-                    stream);
+                         int64_t K, int path, int tile, int split_k, void* stream) {
+    Job job;
+    const int st = prepare_gemm(a_packed, a_scales, b_packed, b_scales, alpha, out, M, N, K, path,
+                                tile, split_k, &job);
+    return st != NVFP4_OK ? st : run_job(job, stream);
 }
 
 int nvfp4_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
                    void* packed_scales, void* stream) {
-    if (!x || !packed_codes || !packed_scales || !valid_rows_k(rows, K) || ld < K || ld % 4 != 0)
-        return NVFP4_ERR_INVALID_VALUE;
-    if (!aligned16(x) || !aligned16(packed_codes) || !aligned16(packed_scales))
-        return NVFP4_ERR_MISALIGNED;
-    const int64_t Rp = round_up(rows, kRowPad);
-    const int64_t P = num_panels(K);
-    if (Rp * 16 > INT32_MAX || P > 65535) return NVFP4_ERR_INVALID_VALUE;  // grid size
-    int device = 0;
-    if (hipGetDevice(&device) != hipSuccess) return NVFP4_ERR_HIP;
-    const int dst = check_device(device);
-    if (dst != NVFP4_OK) return dst;
-    QuantArgs a{};
-    a.x = x;
-    a.codes = static_cast<uint8_t*>(packed_codes);
-    a.scales = static_cast<uint8_t*>(packed_scales);
-    a.ld = ld;
-    a.rows = (int)rows;
-    a.K = (int)K;
-    a.Rp = (int)Rp;
-    a.P = (int)P;
-    const hipError_t e = launch_quantize(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    Job job;
+    const int st = prepare_quantize(x, rows, K, ld, packed_codes, packed_scales, &job);
+    return st != NVFP4_OK ? st : run_job(job, stream);
 }
 
 int nvfp4_grouped_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
                        const void* b_scales, const int32_t* row_offsets, int64_t groups,
                        float alpha, void* out, int64_t M, int64_t N, int64_t K, void* stream) {
-    if (!a_packed || !a_scales || !b_packed || !b_scales || !row_offsets || !out)
-        return NVFP4_ERR_INVALID_VALUE;
-    if (M < 0 || N < 1 || M > kMaxDim || N > kMaxDim || groups < 1 || !valid_rows_k(1, K))
-        return NVFP4_ERR_INVALID_VALUE;
-    const int64_t Np = round_up(N, kRowPad);
-    if (groups * (Np / 16) > INT32_MAX) return NVFP4_ERR_INVALID_VALUE;
-    if (!aligned16(a_packed) || !aligned16(a_scales) || !aligned16(b_packed) ||
-        !aligned16(b_scales) || !aligned16(out) || (reinterpret_cast<uintptr_t>(row_offsets) & 3u))
-        return NVFP4_ERR_MISALIGNED;
-    int device = 0;
-    if (hipGetDevice(&device) != hipSuccess) return NVFP4_ERR_HIP;
-    const int dst = check_device(device);
-    if (dst != NVFP4_OK) return dst;
-    if (M == 0) return NVFP4_OK;  // no rows: nothing to compute or write
-
-    GroupedArgs a{};
-    a.a_codes = static_cast<const uint8_t*>(a_packed);
-    a.a_scales = static_cast<const uint8_t*>(a_scales);
-    a.b_codes = static_cast<const uint8_t*>(b_packed);
-    a.b_scales = static_cast<const uint8_t*>(b_scales);
-    a.offsets = row_offsets;
-    a.out = static_cast<uint16_t*>(out);
-    a.alpha = alpha;
-    a.M = (int)M;
-    a.N = (int)N;
-    a.Mp = (int)round_up(M, kRowPad);
-    a.Np = (int)Np;
-    a.P = (int)num_panels(K);
-    a.G = (int)groups;
-    const hipError_t e = launch_grouped(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
-}
-
-int nvfp4_plan(int64_t M, int64_t N, int64_t K, int* path, int* split_k, int* tile_m,
-               int* tile_n) {
-    if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim || !valid_rows_k(1, K))
-        return NVFP4_ERR_INVALID_VALUE;
-    const Plan p = make_plan(M, N, K, NVFP4_PATH_AUTO, 0);
-    if (path) *path = p.path;
-    if (split_k) *split_k = p.split_k;
-    const TileShape s = p.path == NVFP4_PATH_GEMV     ? TileShape{4, 1}
-                        : p.path == NVFP4_PATH_SKINNY ? TileShape{16, 16}
-                        : p.path == NVFP4_PATH_WSPLIT ? wsplit_shape(p.cfg)
-                                                      : tile_shape(p.cfg);
-    if (tile_m) *tile_m = s.bm;
-    if (tile_n) *tile_n = s.bn;
-    return NVFP4_OK;
+    Job job;
+    const int st = prepare_grouped(a_packed, a_scales, b_packed, b_scales, row_offsets, groups,
+                                   alpha, out, M, N, K, &job);
+    return st != NVFP4_OK ? st : run_job(job, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,46 @@
+// nvfp4_host.h -- host-side pieces shared by the eager entry points and the
+// recorded sequences (not part of the public ABI): a validated and planned
+// launch ("job"), the device check, and the launch of a job.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "nvfp4_internal.h"
+#include "nvfp4_plan.h"
+
+namespace nvfp4 {
+
+enum JobKind { JOB_GEMM = 0, JOB_GROUPED = 1, JOB_QUANTIZE = 2 };
+
+struct Job {
+    int kind = JOB_GEMM;
+    Plan plan{};                 // JOB_GEMM
+    GemmArgs gemm{};             // JOB_GEMM (workspace pointers set at launch)
+    size_t floats = 0;           // split-K partial floats the job needs
+    size_t counters = 0;         // split-K arrival counters the job needs
+    GroupedArgs grouped{};       // JOB_GROUPED
+    QuantArgs quant{};           // JOB_QUANTIZE
+    bool empty = false;          // nothing to launch (a grouped GEMM with no rows)
+};
+
+// Argument checks and planning, host-only (no device call).  Return an
+// NVFP4_* status; on NVFP4_OK the job is ready to launch.
+int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
+                 const void* b_scales, float alpha, void* out, int64_t M, int64_t N, int64_t K,
+                 int path, int tile, int split_k, Job* job);
+int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_packed,
+                    const void* b_scales, const int32_t* row_offsets, int64_t groups, float alpha,
+                    void* out, int64_t M, int64_t N, int64_t K, Job* job);
+int prepare_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
+                     void* packed_scales, Job* job);
+
+// The current device, checked to be a gfx950 GPU (status).
+int current_device(int* device);
+
+// Enqueues a prepared job on `stream`, with the split-K workspace given
+// (null when the job needs none).
+hipError_t launch_job(const Job& job, int device, float* partials, uint32_t* counters,
+                      hipStream_t stream);
+
+}  // namespace nvfp4

@@ -60,6 +60,10 @@ inline TileShape wsplit_shape(int cfg) {
 }
 size_t wsplit_partial_floats(int cfg, const GemmArgs& a);
 
+// Workgroups of a tile configuration resident on `device` at once (queried
+// once per device and configuration; 0 if the query fails).
+int resident_tiles(int cfg, int device);
+
 hipError_t launch_tile(int cfg, const GemmArgs& a, int device, hipStream_t stream);
 hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);

@@ -1,0 +1,180 @@
+// nvfp4_sequence.cpp -- recorded sequences of NVFP4 calls, replayed with one
+// HIP graph launch (include/nvfp4.h, "Recorded sequences").
+//
+// Decode steps run the same few small GEMMs for every token, each worth a
+// few microseconds of device time; launching them one by one costs about as
+// much again ("Peeling the Kernel Onion", section "Knowledge Created and Its
+// Impact": graphs to cut launch overhead for small GEMMs).  A sequence keeps
+// the validated, planned calls; finalize captures them, in order, on a
+// private stream into a graph that owns nothing but kernel nodes (the
+// workspace's counters are zeroed once with a synchronous fill before the
+// capture and reset themselves in the kernels, so no memset node is ever
+// recorded), and launch replays that graph.
+#include <hip/hip_runtime.h>
+
+#include <new>
+#include <vector>
+
+#include "nvfp4.h"
+#include "nvfp4_host.h"
+
+using namespace nvfp4;
+
+struct nvfp4_sequence {
+    std::vector<Job> jobs;
+    bool finalized = false;
+    int device = -1;
+    float* partials = nullptr;
+    uint32_t* counters = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+int add_job(nvfp4_sequence* seq, int status, const Job& job) {
+    if (status != NVFP4_OK) return status;
+    seq->jobs.push_back(job);
+    return NVFP4_OK;
+}
+
+void release(nvfp4_sequence* seq) {
+    if (seq->exec) (void)hipGraphExecDestroy(seq->exec);
+    if (seq->partials) (void)hipFree(seq->partials);
+    if (seq->counters) (void)hipFree(seq->counters);
+    seq->exec = nullptr;
+    seq->partials = nullptr;
+    seq->counters = nullptr;
+}
+
+// Captures the jobs on a private stream and instantiates the graph.
+int capture(nvfp4_sequence* seq) {
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return NVFP4_ERR_HIP;
+    int st = NVFP4_OK;
+    hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        st = NVFP4_ERR_HIP;
+    } else {
+        for (const Job& job : seq->jobs) {
+            const bool ws = job.floats || job.counters;
+            if (launch_job(job, seq->device, ws ? seq->partials : nullptr,
+                           ws ? seq->counters : nullptr, cs) != hipSuccess) {
+                st = NVFP4_ERR_HIP;
+                break;
+            }
+        }
+        // always end the capture, so the stream can be destroyed
+        if (hipStreamEndCapture(cs, &graph) != hipSuccess) st = NVFP4_ERR_HIP;
+    }
+    if (st == NVFP4_OK && hipGraphInstantiate(&seq->exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+        seq->exec = nullptr;
+        st = NVFP4_ERR_HIP;
+    }
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(cs);
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_sequence_create(nvfp4_sequence_t* seq) {
+    if (!seq) return NVFP4_ERR_INVALID_VALUE;
+    *seq = new (std::nothrow) nvfp4_sequence();
+    return *seq ? NVFP4_OK : NVFP4_ERR_ALLOC;
+}
+
+int nvfp4_sequence_add_gemm(nvfp4_sequence_t seq, const void* a_packed, const void* a_scales,
+                            const void* b_packed, const void* b_scales, float alpha, void* out,
+                            int64_t M, int64_t N, int64_t K) {
+    if (!seq) return NVFP4_ERR_INVALID_VALUE;
+    if (seq->finalized) return NVFP4_ERR_STATE;
+    Job job;
+    const int st = prepare_gemm(a_packed, a_scales, b_packed, b_scales, alpha, out, M, N, K,
+                                NVFP4_PATH_AUTO, 0, 0, &job);
+    return add_job(seq, st, job);
+}
+
+int nvfp4_sequence_add_grouped_gemm(nvfp4_sequence_t seq, const void* a_packed,
+                                    const void* a_scales, const void* b_packed,
+                                    const void* b_scales, const int32_t* row_offsets,
+                                    int64_t groups, float alpha, void* out, int64_t M, int64_t N,
+                                    int64_t K) {
+    if (!seq) return NVFP4_ERR_INVALID_VALUE;
+    if (seq->finalized) return NVFP4_ERR_STATE;
+    Job job;
+    const int st = prepare_grouped(a_packed, a_scales, b_packed, b_scales, row_offsets, groups,
+                                   alpha, out, M, N, K, &job);
+    return add_job(seq, st, job);
+}
+
+int nvfp4_sequence_add_quantize(nvfp4_sequence_t seq, const float* x, int64_t rows, int64_t K,
+                                int64_t ld, void* packed_codes, void* packed_scales) {
+    if (!seq) return NVFP4_ERR_INVALID_VALUE;
+    if (seq->finalized) return NVFP4_ERR_STATE;
+    Job job;
+    const int st = prepare_quantize(x, rows, K, ld, packed_codes, packed_scales, &job);
+    return add_job(seq, st, job);
+}
+
+int nvfp4_sequence_finalize(nvfp4_sequence_t seq) {
+    if (!seq) return NVFP4_ERR_INVALID_VALUE;
+    if (seq->finalized) return NVFP4_ERR_STATE;
+    if (seq->jobs.empty()) return NVFP4_ERR_INVALID_VALUE;
+    int device = 0;
+    int st = current_device(&device);
+    if (st != NVFP4_OK) return st;
+    seq->device = device;
+    // one workspace serves every call: they run one after another
+    size_t floats = 0, counters = 0;
+    for (const Job& job : seq->jobs) {
+        floats = job.floats > floats ? job.floats : floats;
+        counters = job.counters > counters ? job.counters : counters;
+        // resolve every device query the launch makes before the capture
+        if (job.kind == JOB_GEMM && job.plan.path == NVFP4_PATH_TILE &&
+            resident_tiles(job.plan.cfg, device) <= 0)
+            return NVFP4_ERR_HIP;
+    }
+    if (floats && hipMalloc(&seq->partials, floats * sizeof(float)) != hipSuccess) {
+        release(seq);
+        return NVFP4_ERR_ALLOC;
+    }
+    if (counters) {
+        if (hipMalloc(&seq->counters, counters * sizeof(uint32_t)) != hipSuccess) {
+            release(seq);
+            return NVFP4_ERR_ALLOC;
+        }
+        if (hipMemset(seq->counters, 0, counters * sizeof(uint32_t)) != hipSuccess) {
+            release(seq);
+            return NVFP4_ERR_HIP;
+        }
+    }
+    st = capture(seq);
+    if (st != NVFP4_OK) {
+        release(seq);
+        return st;
+    }
+    seq->finalized = true;
+    return NVFP4_OK;
+}
+
+int nvfp4_sequence_launch(nvfp4_sequence_t seq, void* stream) {
+    if (!seq) return NVFP4_ERR_INVALID_VALUE;
+    if (!seq->finalized) return NVFP4_ERR_STATE;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return NVFP4_ERR_HIP;
+    if (device != seq->device) return NVFP4_ERR_INVALID_VALUE;
+    return hipGraphLaunch(seq->exec, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? NVFP4_OK
+               : NVFP4_ERR_HIP;
+}
+
+int nvfp4_sequence_destroy(nvfp4_sequence_t seq) {
+    if (!seq) return NVFP4_OK;
+    release(seq);
+    delete seq;
+    return NVFP4_OK;
+}
+
+}  // extern "C"

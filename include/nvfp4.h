@@ -51,10 +51,13 @@ typedef enum nvfp4_status {
     NVFP4_ERR_MISALIGNED = 2,    /* a device pointer is not 16-byte aligned */
     NVFP4_ERR_UNSUPPORTED = 3,   /* no gfx950 device / forced path cannot run */
     NVFP4_ERR_HIP = 4,           /* a HIP runtime call failed */
-    NVFP4_ERR_ALLOC = 5          /* workspace allocation failed */
+    NVFP4_ERR_ALLOC = 5,         /* workspace allocation failed */
+    NVFP4_ERR_CAPTURE = 6,       /* a split-K workspace would have to be created or
+                                    grown while the stream is being captured */
+    NVFP4_ERR_STATE = 7          /* call not allowed in the object's current state */
 } nvfp4_status;
 
-/* Kernel paths for nvfp4_gemm_with_path. */
+/* Kernel paths for nvfp4_gemm_with_plan and nvfp4_plan. */
 enum {
     NVFP4_PATH_AUTO = 0,   /* library's choice from M, N, K */
     NVFP4_PATH_TILE = 1,   /* large shapes: MFMA tiles fed through an LDS ring */
@@ -112,19 +115,30 @@ void nvfp4_shutdown(void);
  * library-owned workspace per
  * (device, stream) pair, allocated on the first call that needs it (the
  * only allocation the library makes); calls on one stream are ordered, calls
- * on different streams use different workspaces.  Launch failures return
+ * on different streams use different workspaces.  Under stream capture the
+ * workspace must already be large enough (make one call of the same shape
+ * on that stream first), else NVFP4_ERR_CAPTURE.  Launch failures return
  * NVFP4_ERR_HIP. */
 int nvfp4_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
                const void* b_scales, float alpha, void* out, int64_t M, int64_t N, int64_t K,
                void* stream);
 
-/* nvfp4_gemm with an explicit kernel path (NVFP4_PATH_*) and split-K factor
- * (0 = library's choice, else the number of K slices, clamped to the number
- * of K steps).  Same contract as nvfp4_gemm; NVFP4_ERR_UNSUPPORTED if the
- * forced path cannot run the shape (skinny needs M <= 16, gemv M <= 4). */
-int nvfp4_gemm_with_path(const void* a_packed, const void* a_scales, const void* b_packed,
+/* nvfp4_gemm with a forced launch plan, for tuning and tests:
+ *   path    : NVFP4_PATH_* (NVFP4_PATH_AUTO = library's choice, then tile
+ *             must be 0)
+ *   tile    : 0 = library's choice; else the workgroup's output tile edge:
+ *             256, 128 or 64 for NVFP4_PATH_TILE (square tiles), 64 or 128
+ *             rows (of 64 columns) for NVFP4_PATH_WSPLIT; must be 0 for the
+ *             skinny and gemv paths (fixed tiles)
+ *   split_k : 0 = library's choice, else the number of K slices, clamped to
+ *             the number of 128-element K steps
+ * Same contract as nvfp4_gemm.  A bad path or tile is NVFP4_ERR_INVALID_VALUE;
+ * NVFP4_ERR_UNSUPPORTED if the forced path cannot run the shape (skinny needs
+ * M <= 16, gemv M <= 4).  Every plan gives the same result up to the order of
+ * the FP32 additions (see nvfp4_gemm); a given plan is deterministic. */
+int nvfp4_gemm_with_plan(const void* a_packed, const void* a_scales, const void* b_packed,
                          const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
-                         int64_t K, int path, int split_k, void* stream);
+                         int64_t K, int path, int tile, int split_k, void* stream);
 
 /* NVFP4 quantisation of fp32 rows straight into the packed layout (the step
  * before the GEMM for activations; "Peeling the Kernel Onion", section "The
@@ -175,11 +189,110 @@ int nvfp4_grouped_gemm(const void* a_packed, const void* a_scales, const void* b
                        const void* b_scales, const int32_t* row_offsets, int64_t groups,
                        float alpha, void* out, int64_t M, int64_t N, int64_t K, void* stream);
 
-/* The path (NVFP4_PATH_TILE / _SKINNY / _WSPLIT / _GEMV) and split-K factor that
- * nvfp4_gemm would use for a shape; also the tile sizes.  Any output pointer
- * may be NULL.  Host-only, no device work. */
-int nvfp4_plan(int64_t M, int64_t N, int64_t K, int* path, int* split_k, int* tile_m,
-               int* tile_n);
+/* Where a plan came from. */
+enum {
+    NVFP4_PLAN_HEURISTIC = 0, /* the library's rules from M, N, K */
+    NVFP4_PLAN_TABLE = 1      /* an entry of the loaded plan table */
+};
+
+/* A launch plan: the kernel path, the output tile of one workgroup, the
+ * split-K factor, and its source. */
+typedef struct nvfp4_plan_t {
+    int32_t path;    /* NVFP4_PATH_TILE / _SKINNY / _WSPLIT / _GEMV */
+    int32_t tile_m;  /* output rows of one workgroup's tile */
+    int32_t tile_n;  /* output columns of one workgroup's tile */
+    int32_t split_k; /* number of K slices (>= 1) */
+    int32_t source;  /* NVFP4_PLAN_HEURISTIC or NVFP4_PLAN_TABLE */
+} nvfp4_plan_t;
+
+/* The plan nvfp4_gemm would use for a shape.  Host-only, no device work.
+ * NVFP4_ERR_INVALID_VALUE for sizes nvfp4_gemm rejects or a NULL `plan`. */
+int nvfp4_plan(int64_t M, int64_t N, int64_t K, nvfp4_plan_t* plan);
+
+/* Tuned plan table.  The GEMM library on the pages picks a tile
+ * configuration per shape by autotuning; that search lost its best tactics
+ * ("The SM120 FP4 Kernel Disaster", Finding 3) and its results were never
+ * saved ("The Multi-Pronged Investigation", Task 2).  Here the choices are
+ * measured once, offline, and persisted as a JSON file:
+ *   { "format": "nvfp4-plan-table", "version": 1, "arch": "gfx950",
+ *     "build": "<nvfp4_build_id() of the library that was timed>",
+ *     "entries": [ { "M": 4096, "N": 2048, "K": 6144, "path": "tile",
+ *                    "tile": 128, "split_k": 1 }, ... ] }
+ * "path" is "tile", "skinny", "wsplit" or "gemv"; "tile" and "split_k" follow
+ * nvfp4_gemm_with_plan (tile 0 = the path's default; split_k >= 1); other
+ * keys are ignored.  Every entry is checked: sizes as for nvfp4_gemm, the
+ * tile allowed for the path, skinny only for M <= 16 and gemv for M <= 4.
+ * A later entry for the same (M, N, K) replaces an earlier one.
+ * nvfp4_gemm (NVFP4_PATH_AUTO, nothing forced) then uses, for (M, N, K): the
+ * entry for exactly that shape, else the entry with the same N and K and the
+ * smallest M' >= M, if M' <= 2 M; else its own rules.  Which plan runs
+ * changes only the order of FP32 additions, never the contract.
+ * nvfp4_plan_table_load replaces the loaded table with the file's, or keeps
+ * the old one if the file cannot be read or parsed or an entry is invalid
+ * (NVFP4_ERR_INVALID_VALUE), or the arch is not gfx950
+ * (NVFP4_ERR_UNSUPPORTED).  `entries` (may be NULL) receives the number of
+ * entries loaded; `same_build` (may be NULL) is set to 1 if the table's
+ * "build" equals nvfp4_build_id(), else 0 (the table was timed on other
+ * kernels: still valid, perhaps no longer the fastest choice).
+ * Thread-safe; calls that plan concurrently see the old or the new table. */
+int nvfp4_plan_table_load(const char* json_path, int64_t* entries, int* same_build);
+
+/* Drops the loaded table: plans come from the library's rules again. */
+void nvfp4_plan_table_clear(void);
+
+/* Identifier of the kernels this library was built from (a hash of their
+ * sources; static string, never NULL). */
+const char* nvfp4_build_id(void);
+
+/* Recorded sequences: launch amortisation for decode steps.
+ * A decode step of a served model runs the same short list of small GEMMs
+ * for every token, and at batch 1-16 each GEMM's own work takes a few
+ * microseconds, so launching them one by one from the host costs about as
+ * much as the work; the pages' serving stack captures such steps into
+ * graphs for that reason ("Peeling the Kernel Onion", section "Knowledge
+ * Created and Its Impact").  A sequence records GEMMs, grouped GEMMs and
+ * quantisations with fixed buffers once, and replays all of them with one
+ * graph launch per step.
+ *   nvfp4_sequence_create   : an empty sequence (host object, caller-owned)
+ *   nvfp4_sequence_add_*    : append one call; arguments and checks as for
+ *                             nvfp4_gemm / nvfp4_grouped_gemm / nvfp4_quantize
+ *                             (minus the stream); the plan is fixed here.
+ *                             Buffers are used by address at every launch:
+ *                             they must stay allocated for the sequence's
+ *                             lifetime, and their contents are read when the
+ *                             sequence runs, not when it is recorded
+ *   nvfp4_sequence_finalize : on the current device (gfx950), allocates the
+ *                             sequence's own split-K workspace, captures the
+ *                             calls in order into a HIP graph and
+ *                             instantiates it; no further adds
+ *   nvfp4_sequence_launch   : enqueues the whole sequence on `stream` (one
+ *                             graph launch; asynchronous like nvfp4_gemm);
+ *                             the current device must be the finalising one
+ *   nvfp4_sequence_destroy  : frees the graph and the workspace; launches
+ *                             must have completed (NULL is a no-op)
+ * The calls of one launch run in recorded order.  Launches of one sequence
+ * share its workspace: they must not run concurrently (launch on one stream,
+ * or order the streams).  A sequence is not thread-safe; different
+ * sequences are independent.  Results equal those of the same eager calls
+ * in the same order, bit for bit.  Adding after finalize, finalizing twice,
+ * or launching before finalize is NVFP4_ERR_STATE; finalizing an empty
+ * sequence is NVFP4_ERR_INVALID_VALUE. */
+typedef struct nvfp4_sequence* nvfp4_sequence_t;
+
+int nvfp4_sequence_create(nvfp4_sequence_t* seq);
+int nvfp4_sequence_add_gemm(nvfp4_sequence_t seq, const void* a_packed, const void* a_scales,
+                            const void* b_packed, const void* b_scales, float alpha, void* out,
+                            int64_t M, int64_t N, int64_t K);
+int nvfp4_sequence_add_grouped_gemm(nvfp4_sequence_t seq, const void* a_packed,
+                                    const void* a_scales, const void* b_packed,
+                                    const void* b_scales, const int32_t* row_offsets,
+                                    int64_t groups, float alpha, void* out, int64_t M, int64_t N,
+                                    int64_t K);
+int nvfp4_sequence_add_quantize(nvfp4_sequence_t seq, const float* x, int64_t rows, int64_t K,
+                                int64_t ld, void* packed_codes, void* packed_scales);
+int nvfp4_sequence_finalize(nvfp4_sequence_t seq);
+int nvfp4_sequence_launch(nvfp4_sequence_t seq, void* stream);
+int nvfp4_sequence_destroy(nvfp4_sequence_t seq);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,18 @@
+"""Launch plans (path, tile, split-K) that the GPU parity tests force, so the
+tuned table can be checked to choose only among them."""
+import block_scaled_fp4_04_amd as nv
+
+TILED = [(nv.PATH_TILE, 256), (nv.PATH_TILE, 128), (nv.PATH_TILE, 64), (nv.PATH_WSPLIT, 64),
+         (nv.PATH_WSPLIT, 128)]
+TILED_SPLITS = [1, 2, 3, 4, 6, 8]
+SKINNY_SPLITS = [1, 2, 3, 4, 5, 8, 16]   # forced in the split-K and forced-plan tests
+
+
+def tested(path_name: str, tile: int, split_k: int) -> bool:
+    path = {v: k for k, v in nv.PATH_NAMES.items()}[path_name]
+    if path == nv.PATH_GEMV:
+        return split_k == 1
+    if path == nv.PATH_SKINNY:
+        return split_k in SKINNY_SPLITS
+    default = 256 if path == nv.PATH_TILE else 64
+    return (path, tile or default) in TILED and split_k in TILED_SPLITS

@@ -29,8 +29,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for st in range(6):
-        assert nv.status_string(st)
+    names = {nv.status_string(st) for st in range(8)}
+    assert len(names) == 8 and "unknown status" not in names
     assert nv.status_string(99) == "unknown status"
     assert nv.version() >= 100
 
@@ -96,14 +96,20 @@ def test_gemm_rejects_bad_arguments_before_launch():
     assert _raw(out=0x5002) == nv.ERR_MISALIGNED
     lib = nv.lib()
     # a forced skinny path needs M <= 16
-    assert lib.nvfp4_gemm_with_path(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 17, 4, 64,
-                                    nv.PATH_SKINNY, 0, None) == nv.ERR_UNSUPPORTED
-    assert lib.nvfp4_gemm_with_path(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 5, 4, 64,
-                                    nv.PATH_GEMV, 0, None) == nv.ERR_UNSUPPORTED
-    assert lib.nvfp4_gemm_with_path(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64,
-                                    7, 0, None) == nv.ERR_INVALID_VALUE
-    assert lib.nvfp4_gemm_with_path(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64,
-                                    0, -1, None) == nv.ERR_INVALID_VALUE
+    assert _wp(17, 4, 64, nv.PATH_SKINNY) == nv.ERR_UNSUPPORTED
+    assert _wp(5, 4, 64, nv.PATH_GEMV) == nv.ERR_UNSUPPORTED
+    assert _wp(4, 4, 64, 7) == nv.ERR_INVALID_VALUE
+    assert _wp(4, 4, 64, 0, split_k=-1) == nv.ERR_INVALID_VALUE
+    # tiles the path does not have
+    for path, tile in [(nv.PATH_AUTO, 128), (nv.PATH_TILE, 96), (nv.PATH_TILE, 32),
+                       (nv.PATH_WSPLIT, 256), (nv.PATH_SKINNY, 16), (nv.PATH_GEMV, 4),
+                       (nv.PATH_TILE, -1)]:
+        assert _wp(4, 32, 64, path, tile) == nv.ERR_INVALID_VALUE, (path, tile)
+
+
+def _wp(M, N, K, path, tile=0, split_k=0):
+    return nv.lib().nvfp4_gemm_with_plan(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, M, N, K,
+                                         path, tile, split_k, None)
 
 
 def _graw(a=0x1000, sa=0x2000, b=0x3000, sb=0x4000, off=0x6000, G=4, out=0x5000, M=4, N=4,
@@ -155,16 +161,72 @@ def test_python_gemm_rejects_k_mismatch():
         nv.gemm(a, b)
 
 
-def test_plan():
-    assert nv.plan(1, 768, 6144)["path"] == nv.PATH_GEMV
-    assert nv.plan(4, 768, 6144)["path"] == nv.PATH_GEMV
-    assert nv.plan(5, 768, 6144)["path"] == nv.PATH_SKINNY
-    assert nv.plan(16, 256, 6144)["path"] == nv.PATH_SKINNY
-    p = nv.plan(16384, 8192, 8192)
-    assert p["path"] == nv.PATH_TILE and p["split_k"] == 1 and p["tile_m"] == 256
-    for M, N, K in [(512, 768, 6144), (512, 2048, 6144), (17, 8, 16), (300, 5000, 64)]:
+def test_plan(no_table):
+    """The library's own rules (no tuned table loaded)."""
+    def key(M, N, K):
         p = nv.plan(M, N, K)
-        assert p["path"] == nv.PATH_WSPLIT and p["split_k"] >= 1
+        return nv.PATH_NAMES[p["path"]], p["tile_m"], p["split_k"]
+    # dot products only for at most 2048 outputs of one or two rows
+    assert key(1, 768, 6144)[0] == "gemv"
+    assert key(1, 2048, 6144)[0] == "gemv"
+    assert key(2, 768, 6144)[0] == "gemv"
+    assert key(1, 6144, 6144)[0] == "skinny"
+    assert key(2, 2048, 6144)[0] == "skinny"
+    assert key(4, 256, 6144)[0] == "skinny"
+    assert key(16, 256, 6144)[0] == "skinny"
+    # 256 x 256 tiles once they give 3/4 of a workgroup per CU
+    assert key(16384, 8192, 8192) == ("tile", 256, 1)
+    assert key(2048, 6144, 6144) == ("tile", 256, 1)          # 192 tiles
+    # else 128 x 128 tiles, split in two below two tiles per CU
+    assert key(4096, 2048, 6144) == ("tile", 128, 1)          # 512 tiles
+    assert key(1024, 6144, 6144) == ("tile", 128, 2)          # 384 tiles
+    assert key(2048, 2048, 6144) == ("tile", 128, 2)          # 256 tiles
+    # else waves split K; 128-row tiles once they alone fill 3/4 of the CUs
+    assert key(1024, 2048, 6144) == ("wsplit", 128, 1)        # 256 tiles of 128 x 64
+    assert key(512, 2048, 6144) == ("wsplit", 64, 1)
+    assert key(512, 768, 6144) == ("wsplit", 64, 2)
+    assert key(32, 256, 6144) == ("wsplit", 64, 3)            # at most 3 slices
+    for M, N, K in [(512, 768, 6144), (512, 2048, 6144), (17, 8, 16), (300, 5000, 64),
+                    (64, 64, 4096)]:
+        p = nv.plan(M, N, K)
+        assert p["path"] == nv.PATH_WSPLIT and 1 <= p["split_k"] <= 3
         # split K only while every workgroup keeps a CU to itself
         tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
         assert p["split_k"] == 1 or tiles * p["split_k"] <= 256
+    assert all(nv.plan(M, N, K)["source"] == nv.PLAN_HEURISTIC
+               for M, N, K in [(1, 768, 6144), (4096, 2048, 6144), (16384, 8192, 8192)])
+
+
+def test_sequence_state_and_validation():
+    """Host-side rules of recorded sequences (no device needed): argument
+    checks at add time, nothing to finalize when empty, no launch before
+    finalize, NULL handles."""
+    lib = nv.lib()
+    h = nv._vp()
+    assert lib.nvfp4_sequence_create(None) == nv.ERR_INVALID_VALUE
+    assert lib.nvfp4_sequence_create(ctypes.byref(h)) == nv.OK and h.value
+    try:
+        add = lib.nvfp4_sequence_add_gemm
+        assert add(h, 0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 24) == nv.ERR_INVALID_VALUE
+        assert add(h, 0x1004, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64) == nv.ERR_MISALIGNED
+        assert add(h, None, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64) == nv.ERR_INVALID_VALUE
+        g = lib.nvfp4_sequence_add_grouped_gemm
+        assert g(h, 0x1000, 0x2000, 0x3000, 0x4000, 0x6002, 2, 1.0, 0x5000, 4, 4, 64) \
+            == nv.ERR_MISALIGNED
+        q = lib.nvfp4_sequence_add_quantize
+        assert q(h, 0x3000, 4, 64, 32, 0x1000, 0x2000) == nv.ERR_INVALID_VALUE
+        # nothing recorded: nothing to finalize; not finalized: no launch
+        assert lib.nvfp4_sequence_finalize(h) == nv.ERR_INVALID_VALUE
+        assert lib.nvfp4_sequence_launch(h, None) == nv.ERR_STATE
+        assert add(h, 0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64) == nv.OK
+        assert q(h, 0x3000, 4, 64, 64, 0x1000, 0x2000) == nv.OK
+        assert g(h, 0x1000, 0x2000, 0x3000, 0x4000, 0x6000, 2, 1.0, 0x5000, 0, 4, 64) == nv.OK
+    finally:
+        assert lib.nvfp4_sequence_destroy(h) == nv.OK
+    for f in ("nvfp4_sequence_finalize", "nvfp4_sequence_launch"):
+        args = (None,) if f.endswith("finalize") else (None, None)
+        assert getattr(lib, f)(*args) == nv.ERR_INVALID_VALUE
+    assert lib.nvfp4_sequence_destroy(None) == nv.OK
+    assert lib.nvfp4_sequence_add_gemm(None, 0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4,
+                                       64) == nv.ERR_INVALID_VALUE
+

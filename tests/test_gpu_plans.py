@@ -1,0 +1,104 @@
+"""GPU parity of forced launch plans (nvfp4_gemm_with_plan): every tiled
+path and tile size with several split-K factors on a ragged shape, and the
+persistent tile grid (more tiles than resident workgroups) for each tile
+size, against the oracle element by element."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import oracle as orc
+from parity import compare
+from plan_cases import TILED, TILED_SPLITS
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_04_amd as nv  # noqa: E402
+
+DEV = "cuda"
+
+
+def say(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return orc.load()
+
+
+@pytest.fixture(scope="module")
+def ragged(o):
+    """300 x 200 x 2192: ragged in M and N for every tile, K not a multiple
+    of 128 (zero panels at the end), 18 K steps."""
+    ops = synth.random_operands(4242, 300, 200, 2192, alpha=-0.75)
+    ref = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha)
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    return ops, ref, a, b
+
+
+@pytest.mark.parametrize("split_k", TILED_SPLITS)
+@pytest.mark.parametrize("path,tile", TILED)
+def test_forced_plan(ragged, path, tile, split_k):
+    ops, (bits, exact, mag), a, b = ragged
+    say(f"forced plan {nv.PATH_NAMES[path]} tile {tile} split {split_k}: "
+        f"{ops.M}x{ops.N}x{ops.K}")
+    out = nv.gemm(a, b, ops.alpha, path=path, tile=tile, split_k=split_k)
+    torch.cuda.synchronize()
+    g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
+    r = compare(g, bits, exact, mag, ops.alpha)
+    say(f"  {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 4, 8])
+def test_forced_skinny(o, split_k):
+    ops = synth.random_operands(4343, 9, 200, 2192, alpha=0.5)
+    say(f"forced skinny split {split_k}: {ops.M}x{ops.N}x{ops.K}")
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    out = nv.gemm(a, b, ops.alpha, path=nv.PATH_SKINNY, split_k=split_k)
+    torch.cuda.synchronize()
+    g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
+    bits, exact, mag = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha)
+    r = compare(g, bits, exact, mag, ops.alpha)
+    say(f"  {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
+
+
+@pytest.mark.parametrize("tile", [256, 128, 64])
+def test_persistent_grid_each_tile(o, tile):
+    """5100 x 5100 x 576: 400, 1600 and 6400 tiles of 256, 128 and 64, more
+    than the workgroups resident on the GPU, so each workgroup walks several
+    tiles; sampled elements (edge rows and columns, random ones)."""
+    M = N = 5100
+    K = 576
+    ops = synth.random_operands(977 + tile, M, N, K, alpha=1.5)
+    say(f"persistent tile {tile}: {M}x{N}x{K}")
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    out = nv.gemm(a, b, ops.alpha, path=nv.PATH_TILE, tile=tile, split_k=1)
+    torch.cuda.synchronize()
+    g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
+    rng = np.random.Generator(np.random.PCG64(tile))
+    edges = np.array([0, tile - 1, tile, M - 1 - (M % tile), M - (M % tile), M - 1])
+    ms = np.concatenate([np.repeat(edges, 256), rng.integers(0, M, 2048)])
+    ns = np.concatenate([rng.integers(0, N, 256 * len(edges)), rng.integers(0, N, 2048)])
+    ms = np.concatenate([ms, rng.integers(0, M, 256 * len(edges))])
+    ns = np.concatenate([ns, np.repeat(edges, 256)])
+    pb, pe, pm = o.gemm_points(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha,
+                               ms, ns)
+    r = compare(g[ms, ns], pb, pe, pm, ops.alpha)
+    say(f"  {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
+    gf = orc.bf16_bits_to_float(g)
+    assert np.all(np.isfinite(gf)) and np.count_nonzero(g & 0x7FFF) > 0.99 * g.size

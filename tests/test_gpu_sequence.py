@@ -1,0 +1,184 @@
+"""Recorded sequences (nvfp4_sequence_*): a decode step's calls replayed with
+one graph launch give, on every replay, the results of the same eager calls
+bit for bit, with the program's own eager work and new inputs between the
+replays; plus the state rules that need a device, and the capture guard of
+the eager entry points."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import oracle as orc
+from parity import compare
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_04_amd as nv  # noqa: E402
+
+DEV = "cuda"
+
+
+def say(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bits(t):
+    return t.view(torch.int16).cpu().numpy().astype(np.uint16)
+
+
+class Step:
+    """One decode step: quantise the fp32 activations of 16 tokens and of 1
+    token, an MoE up-projection share (16 x 256 x 6144, skinny), an
+    attention projection (1 x 768 x 6144, dot products), a 32-row GEMM whose
+    plan splits K across workgroups (workspace), and a grouped GEMM of the
+    16 tokens routed to 2 of 8 experts."""
+
+    def __init__(self, seed):
+        g = torch.Generator(device=DEV).manual_seed(seed)
+        K = 6144
+        self.x16 = torch.randn((16, K), generator=g, device=DEV)
+        self.x1 = torch.randn((1, K), generator=g, device=DEV)
+        self.x32 = torch.randn((32, K), generator=g, device=DEV)
+        self.w_up = nv.quantize(torch.randn((256, K), generator=g, device=DEV))
+        self.w_attn = nv.quantize(torch.randn((768, K), generator=g, device=DEV) * 0.02)
+        self.w_mid = nv.quantize(torch.randn((200, K), generator=g, device=DEV))
+        gops = synth.grouped_operands(seed, 16, 8, 2, 64, K, alpha=0.75)
+        self.experts = nv.groups_to_device(gops.b_codes, gops.b_scales, DEV)
+        self.offsets = torch.from_numpy(gops.offsets).to(DEV)
+        self.tok = gops.M                       # 32 routed rows
+        self.xg = torch.randn((self.tok, K), generator=g, device=DEV)
+        mk = lambda r: nv.PackedOperand(*(torch.empty(n, dtype=torch.uint8, device=DEV)
+                                          for n in nv.packed_size(r, K)), r, K)
+        self.a16, self.a1, self.a32, self.ag = mk(16), mk(1), mk(32), mk(self.tok)
+        self.out = {
+            "up": torch.empty((16, 256), dtype=torch.bfloat16, device=DEV),
+            "attn": torch.empty((1, 768), dtype=torch.bfloat16, device=DEV),
+            "mid": torch.empty((32, 200), dtype=torch.bfloat16, device=DEV),
+            "moe": torch.empty((self.tok, 64), dtype=torch.bfloat16, device=DEV),
+        }
+
+    def eager(self, stream=None):
+        nv.quantize(self.x16, out=self.a16, stream=stream)
+        nv.quantize(self.x1, out=self.a1, stream=stream)
+        nv.quantize(self.x32, out=self.a32, stream=stream)
+        nv.quantize(self.xg, out=self.ag, stream=stream)
+        nv.gemm(self.a16, self.w_up, 1.0, out=self.out["up"], stream=stream)
+        nv.gemm(self.a1, self.w_attn, 0.5, out=self.out["attn"], stream=stream)
+        nv.gemm(self.a32, self.w_mid, -1.25, out=self.out["mid"], stream=stream)
+        nv.grouped_gemm(self.ag, self.experts, self.offsets, 0.75, out=self.out["moe"],
+                        stream=stream)
+
+    def record(self) -> nv.Sequence:
+        s = nv.Sequence()
+        s.add_quantize(self.x16, self.a16)
+        s.add_quantize(self.x1, self.a1)
+        s.add_quantize(self.x32, self.a32)
+        s.add_quantize(self.xg, self.ag)
+        s.add_gemm(self.a16, self.w_up, self.out["up"], 1.0)
+        s.add_gemm(self.a1, self.w_attn, self.out["attn"], 0.5)
+        s.add_gemm(self.a32, self.w_mid, self.out["mid"], -1.25)
+        s.add_grouped_gemm(self.ag, self.experts, self.offsets, self.out["moe"], 0.75)
+        return s
+
+    def results(self):
+        torch.cuda.synchronize()
+        return {k: bits(v) for k, v in self.out.items()}
+
+    def clear(self):
+        for v in self.out.values():
+            v.fill_(float("nan"))
+
+
+def test_sequence_replays_match_eager_calls():
+    step = Step(31)
+    plans = {k: nv.plan(*shape) for k, shape in
+             [("up", (16, 256, 6144)), ("attn", (1, 768, 6144)), ("mid", (32, 200, 6144))]}
+    say(f"sequence plans {plans}")
+    assert plans["mid"]["split_k"] > 1          # the sequence's own workspace is used
+    seq = step.record()
+    seq.finalize()
+    assert seq.calls == 8
+    stream = torch.cuda.Stream()
+    for replay in range(4):
+        # new activations, written by the program's own eager work
+        with torch.no_grad():
+            for x in (step.x16, step.x1, step.x32, step.xg):
+                x.normal_()
+                x.mul_(1.0 + replay)
+        torch.cuda.synchronize()
+        step.clear()
+        step.eager()
+        want = step.results()
+        step.clear()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            seq.launch(stream)
+        stream.synchronize()
+        got = step.results()
+        for k in want:
+            same = np.array_equal(got[k], want[k])
+            say(f"replay {replay} {k}: identical to eager = {same}")
+            assert same, k
+        assert not np.all(want["up"] == 0)
+    # one replay against the oracle: quantise on the host, GEMM in fp64
+    o = orc.load()
+    ac, as_ = o.quantize(step.x16.cpu().numpy())
+    wc, ws = nv.unpack(step.w_up.codes.cpu().numpy(), step.w_up.scales.cpu().numpy(), 256, 6144)
+    ob, oe, om = o.gemm(ac, as_, wc, ws, 1.0)
+    r = compare(got["up"], ob, oe, om, 1.0)
+    say(f"sequence vs oracle (up-projection): {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999
+    seq.close()
+
+
+def test_sequence_state_on_device():
+    step = Step(7)
+    seq = nv.Sequence()
+    seq.add_gemm(step.a16, step.w_up, step.out["up"])
+    seq.finalize()
+    with pytest.raises(nv.Nvfp4Error) as e:
+        seq.finalize()
+    assert e.value.status == nv.ERR_STATE
+    with pytest.raises(nv.Nvfp4Error) as e:
+        seq.add_gemm(step.a16, step.w_up, step.out["up"])
+    assert e.value.status == nv.ERR_STATE
+    seq.launch()
+    torch.cuda.synchronize()
+    seq.close()
+
+
+def test_eager_call_under_capture_needs_its_workspace_first():
+    """Under stream capture the split-K workspace cannot be created: the call
+    reports NVFP4_ERR_CAPTURE and enqueues nothing; after one eager call on
+    that stream the same call captures and replays correctly."""
+    step = Step(5)
+    nv.quantize(step.x32, out=step.a32)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    assert nv.plan(32, 200, 6144)["split_k"] > 1
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(nv.Nvfp4Error) as e:
+        with torch.cuda.graph(g, stream=s):
+            nv.gemm(step.a32, step.w_mid, 1.0, out=step.out["mid"], stream=s)
+    assert e.value.status == nv.ERR_CAPTURE
+    with torch.cuda.stream(s):
+        nv.gemm(step.a32, step.w_mid, 1.0, out=step.out["mid"], stream=s)
+    s.synchronize()
+    want = bits(step.out["mid"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        nv.gemm(step.a32, step.w_mid, 1.0, out=step.out["mid"], stream=s)
+    for _ in range(3):
+        step.clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(step.out["mid"]), want)
