@@ -59,7 +59,8 @@ EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_p
 
 class _PlanT(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-                ("split_k", ctypes.c_int32), ("source", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("tail_tiles", ctypes.c_int32),
+                ("tail_split", ctypes.c_int32), ("source", ctypes.c_int32)]
 
 
 class Nvfp4Error(RuntimeError):
@@ -211,7 +212,7 @@ def plan(M: int, N: int, K: int) -> dict:
     if st:
         raise Nvfp4Error(st, "nvfp4_plan")
     return {"path": p.path, "split_k": p.split_k, "tile_m": p.tile_m, "tile_n": p.tile_n,
-            "source": p.source}
+            "tail_tiles": p.tail_tiles, "tail_split": p.tail_split, "source": p.source}
 
 
 def build_id() -> str:

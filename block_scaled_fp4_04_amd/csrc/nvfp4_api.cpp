@@ -174,6 +174,10 @@ int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packe
     a.split_k = plan.split_k;
     a.tiles_m = plan.tiles_m;
     a.tiles_n = plan.tiles_n;
+    a.tile_begin = 0;
+    a.tile_count = plan.tiles_m * plan.tiles_n;
+    a.tail_tiles = plan.tail_tiles;
+    a.tail_split = plan.tail_split;
     job->floats = plan.path == NVFP4_PATH_GEMV     ? 0
                   : plan.path == NVFP4_PATH_SKINNY ? skinny_partial_floats(a)
                   : plan.path == NVFP4_PATH_WSPLIT ? wsplit_partial_floats(plan.cfg, a)

@@ -32,6 +32,10 @@ struct GemmArgs {
     int P;                    // number of 64-element K panels (even)
     int split_k;              // number of K slices (>= 1)
     int tiles_m, tiles_n;     // output tiles along M and N (tile kernel)
+    int tile_begin, tile_count;  // tiles [tile_begin, tile_begin + tile_count) of the
+                                 // tiles_m x tiles_n grid this launch computes (tile kernel)
+    int tail_tiles, tail_split;  // tile kernel without split-K: the last tail_tiles tiles
+                                 // run in a second launch split tail_split ways along K
 };
 
 // Tile configurations of the large-M kernel.

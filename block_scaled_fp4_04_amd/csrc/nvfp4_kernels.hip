@@ -88,6 +88,12 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     static_assert(NS >= 3 && NS <= 8 && (NS - 2) * LPS < 64, "pipeline depth");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+    // 256 x 256 tiles: per wave, a 32 x 64 bf16 staging block for the
+    // epilogue (the ring keeps loading the next tile meanwhile, so the
+    // epilogue cannot borrow ring buffers; this brings the workgroup to the
+    // 160 KB of LDS).
+    constexpr bool STAGED_OUT = BM == 256 && BN == 256;
+    __shared__ __attribute__((aligned(16))) uint8_t out_stage[STAGED_OUT ? 4 * 4096 : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -102,7 +108,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     // the single (tile, K range) pair w.  Consecutive ids are dealt to the
     // eight XCDs in turn; the id is remapped so that each XCD works on a
     // contiguous range of tiles, walked in groups of 8 along M for L2 reuse.
-    const int T = a.tiles_m * a.tiles_n;
+    const int T = a.tile_count;
     const int S = SPLIT ? a.split_k : 1;
     const int G = SPLIT ? 1 : (int)gridDim.x;
     const int n_items = SPLIT ? 1 : (T - (int)blockIdx.x + G - 1) / G;
@@ -113,8 +119,9 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
         z = bid % S;
         t = bid / S;
     };
-    auto origin_of = [&](int t, int& m0, int& n0) {
+    auto origin_of = [&](int t, int& m0, int& n0) {  // t: tile of this launch's range
         constexpr int GROUP_M = 8;
+        t += a.tile_begin;
         const int in_group = GROUP_M * a.tiles_n;
         const int first_m = (t / in_group) * GROUP_M;
         const int gsize = min(a.tiles_m - first_m, GROUP_M);
@@ -330,47 +337,106 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     // rows 8 * (v / 4) + 4 * (l / 32) + v % 4 in lane l; the blocks hold C
     // transposed, so lane l has row l % 32 of C and, for each v / 4, four
     // consecutive columns, stored as one 8-byte write when N % 4 == 0.
-    auto store_tile = [&](int m0, int n0) {
+    // One 32 x 32 block (i, j) of the wave's part of the tile; val(v) gives
+    // the lane's v-th value of the block.  Lane coordinates are recomputed
+    // here (cheap, and no VGPR has to stay live across the main loop for
+    // them); the block is stored through a uniform base address plus a
+    // 32-bit lane offset (32 * N * 2 bytes < 4 GiB: the packed-size limit
+    // of this path keeps N below 2^25).
+    auto store_block = [&](int m0, int n0, int i, int j, auto&& val) {
         const bool vec = (a.N & 3) == 0;
-        // Lane coordinates recomputed here (cheap, and no VGPR has to stay
-        // live across the main loop for them); each 32 x 32 block is stored
-        // through a uniform base address plus a 32-bit lane offset
-        // (32 * N * 2 bytes < 4 GiB: the packed-size limit of this path
-        // keeps N below 2^25).
         const uint32_t ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
         const int lq = (int)(ln & 31u), lh = (int)(ln >> 5);
         const uint32_t lane_off = (uint32_t)lq * (uint32_t)a.N * 2u + (uint32_t)lh * 8u;
+        const int row0 = m0 + wm * (BM / 2) + i * 32;
+        const int col0 = n0 + wn * (BN / 2) + j * 32;
+        uint8_t* base = reinterpret_cast<uint8_t*>(a.out + (int64_t)row0 * a.N + col0);
+        if (row0 + lq < a.M) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int col = col0 + 8 * u + 4 * lh;
+                const uint16_t e0 = to_bf16(a.alpha * val(4 * u + 0));
+                const uint16_t e1 = to_bf16(a.alpha * val(4 * u + 1));
+                const uint16_t e2 = to_bf16(a.alpha * val(4 * u + 2));
+                const uint16_t e3 = to_bf16(a.alpha * val(4 * u + 3));
+                uint8_t* p = base + lane_off + 16u * u;
+                if (vec) {
+                    if (col < a.N)
+                        *reinterpret_cast<uint2*>(p) =
+                            uint2{(uint32_t)e0 | ((uint32_t)e1 << 16), (uint32_t)e2 | ((uint32_t)e3 << 16)};
+                } else {
+                    uint16_t* o = reinterpret_cast<uint16_t*>(p);
+                    if (col + 0 < a.N) o[0] = e0;
+                    if (col + 1 < a.N) o[1] = e1;
+                    if (col + 2 < a.N) o[2] = e2;
+                    if (col + 3 < a.N) o[3] = e3;
+                }
+            }
+        }
+    };
+    // Epilogue through the wave's LDS staging block (256 x 256 tiles, N % 8
+    // == 0): for each row of 32 x 32 blocks and each pair of blocks, the
+    // lanes write their bf16 values (row l % 32, four columns per 8-byte
+    // write) into a 32 x 128-byte block, then read it back 16 bytes per lane
+    // along rows, so that every store instruction writes eight whole
+    // 128-byte lines of C.  Partial lines (the direct form writes 16 bytes
+    // of 32 rows per instruction) left L2 incomplete for tall, narrow C and
+    // were written back to memory several times over.  The 16-byte column
+    // chunks of a staged row are XOR-swizzled by the row (mod 8) to spread
+    // the writes over the LDS banks.  The block is private to the wave and
+    // LDS instructions of one wave complete in order, so no barrier is
+    // needed between the writes and the reads.
+    auto store_tile_staged = [&](int m0, int n0) {
+        uint8_t* st = out_stage + wave * 4096;
+        const uint32_t ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int lq = (int)(ln & 31u), lh = (int)(ln >> 5);
+        const int wsw = (lq & 7) * 16;                 // swizzle of the row this lane writes
+        const int rrow = (int)(ln >> 3), rch = (int)(ln & 7u);  // row / chunk this lane reads
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int jj = 0; jj < NI / 2; ++jj) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jl = 0; jl < 2; ++jl)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const f16v& c = acc[i][2 * jj + jl];
+                        const uint16_t e0 = to_bf16(a.alpha * acc_read(c[4 * u + 0]));
+                        const uint16_t e1 = to_bf16(a.alpha * acc_read(c[4 * u + 1]));
+                        const uint16_t e2 = to_bf16(a.alpha * acc_read(c[4 * u + 2]));
+                        const uint16_t e3 = to_bf16(a.alpha * acc_read(c[4 * u + 3]));
+                        const int cb = jl * 64 + u * 16 + lh * 8;  // byte column in the staged row
+                        *reinterpret_cast<uint2*>(st + lq * 128 + (cb ^ wsw)) =
+                            uint2{(uint32_t)e0 | ((uint32_t)e1 << 16), (uint32_t)e2 | ((uint32_t)e3 << 16)};
+                    }
+                const int col = n0 + wn * (BN / 2) + jj * 64 + rch * 8;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int r = k * 8 + rrow;
+                    const uint4 v = *reinterpret_cast<const uint4*>(st + r * 128 + ((rch * 16) ^ ((r & 7) * 16)));
+                    const int row = m0 + wm * (BM / 2) + i * 32 + r;
+                    if (row < a.M && col < a.N)
+                        *reinterpret_cast<uint4*>(a.out + (int64_t)row * a.N + col) = v;
+                }
+            }
+    };
+    // Epilogue of a tile without split-K, straight from the accumulators
+    // (read one at a time from AGPRs), one block at a time so that few
+    // values sit in VGPRs.
+    auto store_tile = [&](int m0, int n0) {
+        if constexpr (STAGED_OUT) {
+            if ((a.N & 7) == 0) {
+                store_tile_staged(m0, n0);
+                return;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-                // one 32 x 32 block at a time keeps few values in VGPRs
                 __builtin_amdgcn_sched_barrier(0);
-                const int row0 = m0 + wm * (BM / 2) + i * 32;
-                const int col0 = n0 + wn * (BN / 2) + j * 32;
-                uint8_t* base = reinterpret_cast<uint8_t*>(a.out + (int64_t)row0 * a.N + col0);
-                if (row0 + lq < a.M) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int col = col0 + 8 * u + 4 * lh;
-                        const uint16_t e0 = to_bf16(a.alpha * (SPLIT ? acc[i][j][4 * u + 0] : acc_read(acc[i][j][4 * u + 0])));
-                        const uint16_t e1 = to_bf16(a.alpha * (SPLIT ? acc[i][j][4 * u + 1] : acc_read(acc[i][j][4 * u + 1])));
-                        const uint16_t e2 = to_bf16(a.alpha * (SPLIT ? acc[i][j][4 * u + 2] : acc_read(acc[i][j][4 * u + 2])));
-                        const uint16_t e3 = to_bf16(a.alpha * (SPLIT ? acc[i][j][4 * u + 3] : acc_read(acc[i][j][4 * u + 3])));
-                        uint8_t* p = base + lane_off + 16u * u;
-                        if (vec) {
-                            if (col < a.N)
-                                *reinterpret_cast<uint2*>(p) =
-                                    uint2{(uint32_t)e0 | ((uint32_t)e1 << 16), (uint32_t)e2 | ((uint32_t)e3 << 16)};
-                        } else {
-                            uint16_t* o = reinterpret_cast<uint16_t*>(p);
-                            if (col + 0 < a.N) o[0] = e0;
-                            if (col + 1 < a.N) o[1] = e1;
-                            if (col + 2 < a.N) o[2] = e2;
-                            if (col + 3 < a.N) o[3] = e3;
-                        }
-                    }
-                }
+                store_block(m0, n0, i, j, [&](int v) { return acc_read(acc[i][j][v]); });
             }
     };
 
@@ -392,7 +458,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     ready_scales(r0);
     decode(r0, 0, av[0], bv[0]);
 
-    if (!SPLIT) {
+    if constexpr (!SPLIT) {
         // The tiles of this workgroup in turn; a tile's result is stored
         // right after its last panel, while the loads of the next tile's
         // first panels are in flight.
@@ -437,24 +503,33 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
         }
         __syncthreads();
         if (!s_last) return;
+        // Add the S partial tiles in split order, one row of 32 x 32 blocks
+        // at a time: its NI * 16 values of every split are loaded together
+        // (the accumulators are dead by now, so the registers are free; one
+        // value at a time would wait a full memory round trip per value).
         const float* all = a.partials + (int64_t)t0 * S * (BM * BN);
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i) {
+            float sum[NI][16];
 #pragma unroll
             for (int j = 0; j < NI; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-        for (int zz = 0; zz < S; ++zz) {
-            const float* pz = all + (int64_t)zz * (BM * BN);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
+                for (int v = 0; v < 16; ++v) sum[j][v] = 0.0f;
+            for (int zz = 0; zz < S; ++zz) {
+                const float* pz = all + (int64_t)zz * (BM * BN) + (i * NI) * 16 * 256 + tid;
+                float part[NI][16];
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        acc[i][j][v] += fetch(pz + ((i * NI + j) * 16 + v) * 256 + tid);
+                    for (int v = 0; v < 16; ++v) part[j][v] = fetch(pz + (j * 16 + v) * 256);
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sum[j][v] += part[j][v];
+            }
+#pragma unroll
+            for (int j = 0; j < NI; ++j) store_block(m0, n0, i, j, [&](int v) { return sum[j][v]; });
         }
-        store_tile(m0, n0);
     }
     wait_vmcnt<0>();  // drain the look-ahead loads before the LDS is released
 }
@@ -876,13 +951,16 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs a) {
 }  // namespace
 
 size_t tile_partial_floats(int cfg, const GemmArgs& a) {
-    if (a.split_k <= 1) return 0;
     const TileShape s = tile_shape(cfg);
-    return (size_t)a.tiles_m * a.tiles_n * a.split_k * s.bm * s.bn;
+    if (a.split_k > 1) return (size_t)a.tile_count * a.split_k * s.bm * s.bn;
+    if (a.tail_tiles > 0) return (size_t)a.tail_tiles * a.tail_split * s.bm * s.bn;
+    return 0;
 }
 size_t tile_counters(int cfg, const GemmArgs& a) {
     (void)cfg;
-    return a.split_k <= 1 ? 0 : (size_t)a.tiles_m * a.tiles_n;
+    if (a.split_k > 1) return (size_t)a.tile_count;
+    if (a.tail_tiles > 0) return (size_t)a.tail_tiles;
+    return 0;
 }
 size_t skinny_partial_floats(const GemmArgs& a) {
     return a.split_k <= 1 ? 0 : (size_t)(a.Np / 16) * a.split_k * 256;
@@ -912,8 +990,33 @@ int resident_tiles(int cfg, int device) {
     return r;
 }
 
+namespace {
+hipError_t launch_tile_range(int cfg, const GemmArgs& a, int device, hipStream_t stream);
+}  // namespace
+
 hipError_t launch_tile(int cfg, const GemmArgs& a, int device, hipStream_t stream) {
-    const int tiles = a.tiles_m * a.tiles_n;
+    if (a.split_k > 1 || a.tail_tiles <= 0) return launch_tile_range(cfg, a, device, stream);
+    // Tail: the full rounds of tiles first (persistent, whole K range), then
+    // the last tail_tiles tiles with K split tail_split ways, so that they
+    // occupy the CUs a last partial round would leave idle.  The launches
+    // are ordered on the stream; the second one's workgroups reduce their
+    // partial tiles through the workspace as any split-K launch does.
+    GemmArgs head = a;
+    head.tile_count = a.tile_count - a.tail_tiles;
+    head.tail_tiles = 0;
+    const hipError_t e = launch_tile_range(cfg, head, device, stream);
+    if (e != hipSuccess) return e;
+    GemmArgs tail = a;
+    tail.tile_begin = a.tile_begin + head.tile_count;
+    tail.tile_count = a.tail_tiles;
+    tail.split_k = a.tail_split;
+    tail.tail_tiles = 0;
+    return launch_tile_range(cfg, tail, device, stream);
+}
+
+namespace {
+hipError_t launch_tile_range(int cfg, const GemmArgs& a, int device, hipStream_t stream) {
+    const int tiles = a.tile_count;
     const bool split = a.split_k > 1;
     int blocks = tiles * a.split_k;
     if (!split && a.P >= 8) {
@@ -943,6 +1046,7 @@ hipError_t launch_tile(int cfg, const GemmArgs& a, int device, hipStream_t strea
     }
     return hipGetLastError();
 }
+}  // namespace
 
 size_t wsplit_partial_floats(int cfg, const GemmArgs& a) {
     if (a.split_k <= 1) return 0;

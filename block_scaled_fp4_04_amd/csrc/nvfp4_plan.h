@@ -10,6 +10,7 @@ struct Plan {
     int cfg;      // TileConfig (tile path) or WsplitConfig (wsplit path)
     int split_k;  // number of K slices (>= 1)
     int tiles_m, tiles_n;
+    int tail_tiles, tail_split;  // tile path without split-K: last tiles split along K
     int source;   // NVFP4_PLAN_HEURISTIC or NVFP4_PLAN_TABLE
 };
 

@@ -202,6 +202,8 @@ typedef struct nvfp4_plan_t {
     int32_t tile_m;  /* output rows of one workgroup's tile */
     int32_t tile_n;  /* output columns of one workgroup's tile */
     int32_t split_k; /* number of K slices (>= 1) */
+    int32_t tail_tiles; /* tile path, split_k 1: the last tail_tiles tiles run in a */
+    int32_t tail_split; /* second launch with K split tail_split ways (0 if none)  */
     int32_t source;  /* NVFP4_PLAN_HEURISTIC or NVFP4_PLAN_TABLE */
 } nvfp4_plan_t;
 

@@ -77,10 +77,11 @@ def test_forced_skinny(o, split_k):
 
 @pytest.mark.parametrize("tile", [256, 128, 64])
 def test_persistent_grid_each_tile(o, tile):
-    """5100 x 5100 x 576: 400, 1600 and 6400 tiles of 256, 128 and 64, more
+    """5100 x 5104 x 576: 400, 1600 and 6400 tiles of 256, 128 and 64, more
     than the workgroups resident on the GPU, so each workgroup walks several
-    tiles; sampled elements (edge rows and columns, random ones)."""
-    M = N = 5100
+    tiles (N % 8 == 0: the 256 x 256 tiles store through the LDS staging
+    block); sampled elements (edge rows and columns, random ones)."""
+    M, N = 5100, 5104
     K = 576
     ops = synth.random_operands(977 + tile, M, N, K, alpha=1.5)
     say(f"persistent tile {tile}: {M}x{N}x{K}")
@@ -90,11 +91,12 @@ def test_persistent_grid_each_tile(o, tile):
     torch.cuda.synchronize()
     g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
     rng = np.random.Generator(np.random.PCG64(tile))
-    edges = np.array([0, tile - 1, tile, M - 1 - (M % tile), M - (M % tile), M - 1])
-    ms = np.concatenate([np.repeat(edges, 256), rng.integers(0, M, 2048)])
-    ns = np.concatenate([rng.integers(0, N, 256 * len(edges)), rng.integers(0, N, 2048)])
-    ms = np.concatenate([ms, rng.integers(0, M, 256 * len(edges))])
-    ns = np.concatenate([ns, np.repeat(edges, 256)])
+    edges_m = np.array([0, tile - 1, tile, M - 1 - (M % tile), M - (M % tile), M - 1])
+    edges_n = np.array([0, tile - 1, tile, N - 1 - (N % tile), N - (N % tile), N - 1])
+    ms = np.concatenate([np.repeat(edges_m, 256), rng.integers(0, M, 2048)])
+    ns = np.concatenate([rng.integers(0, N, 256 * len(edges_m)), rng.integers(0, N, 2048)])
+    ms = np.concatenate([ms, rng.integers(0, M, 256 * len(edges_n))])
+    ns = np.concatenate([ns, np.repeat(edges_n, 256)])
     pb, pe, pm = o.gemm_points(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha,
                                ms, ns)
     r = compare(g[ms, ns], pb, pe, pm, ops.alpha)
@@ -102,3 +104,32 @@ def test_persistent_grid_each_tile(o, tile):
     assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
     gf = orc.bf16_bits_to_float(g)
     assert np.all(np.isfinite(gf)) and np.count_nonzero(g & 0x7FFF) > 0.99 * g.size
+
+
+@pytest.mark.parametrize("M,N,K,tail,split", [(4096, 6144, 512, 128, 2), (4352, 4352, 1024, 33, 4)])
+def test_tail_split_launch(o, M, N, K, tail, split):
+    """256 x 256 tiles whose last round would be at most half full: the
+    full rounds run as one launch and the last tiles as a second launch
+    with K split (384 tiles: 128 split 2 ways; 289 tiles: 33 split 4 ways);
+    sampled elements all over C, a third of them in the tail's tiles."""
+    p = nv.plan(M, N, K)
+    assert (p["path"], p["tile_m"], p["split_k"], p["tail_tiles"], p["tail_split"]) == \
+        (nv.PATH_TILE, 256, 1, tail, split), p
+    ops = synth.random_operands(31 * M + K, M, N, K, alpha=0.875)
+    say(f"tail split {tail}x{split}: {M}x{N}x{K}")
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    out = nv.gemm(a, b, ops.alpha)
+    torch.cuda.synchronize()
+    g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
+    rng = np.random.Generator(np.random.PCG64(M + N))
+    ms = np.concatenate([rng.integers(0, M, 4096), np.full(256, M - 1), np.arange(256)])
+    ns = np.concatenate([rng.integers(0, N, 4096), rng.integers(0, N, 256), np.full(256, N - 1)])
+    pb, pe, pm = o.gemm_points(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha,
+                               ms, ns)
+    r = compare(g[ms, ns], pb, pe, pm, ops.alpha)
+    say(f"  {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
+    gf = orc.bf16_bits_to_float(g)
+    assert np.all(np.isfinite(gf)) and np.count_nonzero(g & 0x7FFF) > 0.99 * g.size
+
