@@ -143,7 +143,7 @@ int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packe
     if (!aligned16(a_packed) || !aligned16(a_scales) || !aligned16(b_packed) ||
         !aligned16(b_scales) || !aligned16(out))
         return NVFP4_ERR_MISALIGNED;
-    if (path == NVFP4_PATH_SKINNY && M > 16) return NVFP4_ERR_UNSUPPORTED;
+    if (path == NVFP4_PATH_SKINNY && M > 64) return NVFP4_ERR_UNSUPPORTED;
     if (path == NVFP4_PATH_GEMV && M > 4) return NVFP4_ERR_UNSUPPORTED;
 
     *job = Job{};

@@ -535,14 +535,15 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny-M kernel (M <= 16), for decode-sized GEMMs that are bound by
+// Skinny-M kernel (M <= 64), for decode-sized GEMMs that are bound by
 // streaming B from HBM and by latency.
 //
-// v_mfma_f32_16x16x32_f16 with the (zero-padded) 16 rows of A as the MFMA A
-// operand and 16 rows of B as the B operand.  Work unit: 16 B rows x 128 K
-// (two panels).  Lane l holds row l % 16 and, with g = l / 16, the 16-byte
-// half (g % 2) of panel (g / 2): one 16-byte load of codes and one 2-byte
-// load of scales per operand, straight from HBM (B is used once, so it does
+// v_mfma_f32_16x16x32_f16 with a 16-row block of A (zero-padded) as the MFMA
+// A operand and 16 rows of B as the B operand; MB = ceil(M / 16) blocks of A
+// share each decoded B fragment.  Work unit: 16 B rows x 128 K (two
+// panels).  Lane l holds row l % 16 and, with g = l / 16, the 16-byte half
+// (g % 2) of panel (g / 2): one 16-byte load of codes and one 2-byte load of
+// scales per operand block, straight from HBM (B is used once, so it does
 // not pass through LDS).  Each MFMA sub-step s takes word s of every lane.
 // Lanes whose A row is at or beyond M skip their A loads (zeros).
 //
@@ -553,9 +554,9 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 // are added in LDS in wave order; with split_k > 1 the workgroup partials
 // are added by the last arrival in split order (deterministic).
 // ---------------------------------------------------------------------------
-template <int WAVES>
+template <int WAVES, int MB>
 __global__ void __launch_bounds__(WAVES * 64) skinny_kernel(GemmArgs a) {
-    constexpr int UNITS = 4;
+    constexpr int UNITS = MB <= 2 ? 4 : 2;   // (registers: 128 VGPRs at 16 waves)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -569,78 +570,101 @@ __global__ void __launch_bounds__(WAVES * 64) skinny_kernel(GemmArgs a) {
     const int grp = lane >> 4;
     const int pl = grp >> 1, half = grp & 1;
     const int nrow = g * 16 + r16;
-    const bool a_row = r16 < a.M;
 
-    f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f4v acc[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[b] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
     for (int base = c0 + wave; base < c1; base += WAVES * UNITS) {
-        uint4 bw[UNITS], aw[UNITS];
-        uint32_t bs[UNITS], as[UNITS];
+        uint4 bw[UNITS], aw[UNITS][MB];
+        uint32_t bs[UNITS], as[UNITS][MB];
 #pragma unroll
         for (int u = 0; u < UNITS; ++u) {
             const int c = base + WAVES * u;
             const int panel = 2 * c + pl;
             bw[u] = uint4{0u, 0u, 0u, 0u};
-            aw[u] = uint4{0u, 0u, 0u, 0u};
             bs[u] = 0u;
-            as[u] = 0u;
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                aw[u][b] = uint4{0u, 0u, 0u, 0u};
+                as[u][b] = 0u;
+            }
             if (c < c1 && panel < a.P) {
                 const int64_t bo = (int64_t)panel * a.Np + nrow;
                 bw[u] = *reinterpret_cast<const uint4*>(a.b_codes + bo * 32 + half * 16);
                 bs[u] = *reinterpret_cast<const uint16_t*>(a.b_scales + bo * 4 + half * 2);
-                if (a_row) {
-                    const int64_t ao = (int64_t)panel * a.Mp + r16;
-                    aw[u] = *reinterpret_cast<const uint4*>(a.a_codes + ao * 32 + half * 16);
-                    as[u] = *reinterpret_cast<const uint16_t*>(a.a_scales + ao * 4 + half * 2);
+#pragma unroll
+                for (int b = 0; b < MB; ++b) {
+                    if (16 * b + r16 < a.M) {
+                        const int64_t ao = (int64_t)panel * a.Mp + 16 * b + r16;
+                        aw[u][b] = *reinterpret_cast<const uint4*>(a.a_codes + ao * 32 + half * 16);
+                        as[u][b] = *reinterpret_cast<const uint16_t*>(a.a_scales + ao * 4 + half * 2);
+                    }
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < UNITS; ++u) {
             const h2 sbh = e4m3x2_lo(bs[u]);
-            const h2 sah = e4m3x2_lo(as[u]);
+            h2 sah[MB];
+#pragma unroll
+            for (int b = 0; b < MB; ++b) sah[b] = e4m3x2_lo(as[u][b]);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const h8 av = decode8(word_of(aw[u], s), scale_of(sah, s));
                 const h8 bv = decode8(word_of(bw[u], s), scale_of(sbh, s));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < MB; ++b) {
+                    const h8 av = decode8(word_of(aw[u][b], s), scale_of(sah[b], s));
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[b], 0, 0, 0);
+                }
             }
         }
     }
 
-    __shared__ f4v red[WAVES][64];
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave != 0) return;
-    f4v sum = red[0][lane];
+    __shared__ f4v red[WAVES][MB][64];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+    for (int b = 0; b < MB; ++b) red[wave][b][lane] = acc[b];
+    __syncthreads();
+    // wave b < MB adds the wave partials of A block b (in wave order); every
+    // wave stays until the split-K hand-off is decided (barriers below)
+    const int blk = wave < MB ? wave : 0;
+    const bool reducer = wave < MB;
+    f4v sum = red[0][blk][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += red[w][blk][lane];
 
     if (S > 1) {
-        float* mine = a.partials + ((int64_t)g * S + z) * 256;
+        float* mine = a.partials + (((int64_t)g * S + z) * MB + blk) * 256;
+        if (reducer) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) publish(mine + v * 64 + lane, sum[v]);
-        uint32_t old = 0;
-        if (lane == 0) old = arrive(a.counters + g);
-        old = __shfl(old, 0);
-        if (old != (uint32_t)(S - 1)) return;
-        if (lane == 0) reset_counter(a.counters + g);  // all splits arrived
-        const float* all = a.partials + (int64_t)g * S * 256;
+            for (int v = 0; v < 4; ++v) publish(mine + v * 64 + lane, sum[v]);
+        }
+        // one arrival per workgroup, after every block's partials are out
+        __shared__ uint32_t s_old;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) s_old = arrive(a.counters + g);
+        __syncthreads();
+        if (s_old != (uint32_t)(S - 1)) return;       // (uniform in the workgroup)
+        if (tid == 0) reset_counter(a.counters + g);  // all splits arrived
+        if (!reducer) return;
         f4v t = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int zz = 0; zz < S; ++zz) {
+            const float* pz = a.partials + (((int64_t)g * S + zz) * MB + blk) * 256;
             f4v p;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) p[v] = fetch(all + zz * 256 + v * 64 + lane);
+            for (int v = 0; v < 4; ++v) p[v] = fetch(pz + v * 64 + lane);
             t += p;
         }
         sum = t;
     }
+    if (!reducer) return;
 
     // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + v.
     const int col = g * 16 + r16;
     if (col < a.N) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int row = 4 * grp + v;
+            const int row = 16 * blk + 4 * grp + v;
             if (row < a.M) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * sum[v]);
         }
     }
@@ -963,7 +987,8 @@ size_t tile_counters(int cfg, const GemmArgs& a) {
     return 0;
 }
 size_t skinny_partial_floats(const GemmArgs& a) {
-    return a.split_k <= 1 ? 0 : (size_t)(a.Np / 16) * a.split_k * 256;
+    const int mb = (a.M + 15) / 16;
+    return a.split_k <= 1 ? 0 : (size_t)(a.Np / 16) * a.split_k * mb * 256;
 }
 size_t skinny_counters(const GemmArgs& a) {
     return a.split_k <= 1 ? 0 : (size_t)(a.Np / 16);
@@ -1080,7 +1105,11 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
 
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.Np / 16) * a.split_k));
-    hipLaunchKernelGGL(skinny_kernel<kSkinnyWaves>, grid, dim3(kSkinnyWaves * 64), 0, stream, a);
+    const dim3 block(kSkinnyWaves * 64);
+    if (a.M <= 16) hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, 1>), grid, block, 0, stream, a);
+    else if (a.M <= 32) hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, 2>), grid, block, 0, stream, a);
+    else if (a.M <= 48) hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, 3>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, 4>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -300,7 +300,7 @@ bool parse_entry(const JValue& e, int64_t* M, int64_t* N, int64_t* K, Choice* c)
     if (e.get("tile") && !get_int(e, "tile", 0, 256, &tile)) return false;
     if (!get_int(e, "split_k", 1, 1 << 20, &split)) return false;
     if (!tile_allowed(c->path, (int)tile)) return false;
-    if (c->path == NVFP4_PATH_SKINNY && *M > 16) return false;
+    if (c->path == NVFP4_PATH_SKINNY && *M > 64) return false;
     if (c->path == NVFP4_PATH_GEMV && *M > 4) return false;
     c->tile = (int)tile;
     c->split_k = (int)split;
@@ -309,16 +309,18 @@ bool parse_entry(const JValue& e, int64_t* M, int64_t* N, int64_t* K, Choice* c)
 
 // ---- the library's rules ----------------------------------------------------
 
-void plan_skinny(int64_t N, int steps, int split_req, Plan* p) {
+void plan_skinny(int64_t M, int64_t N, int steps, int split_req, Plan* p) {
     // One workgroup of kSkinnyWaves waves per 16 output columns covers the
     // whole K range: the split-K hand-off costs more than it saves once
     // there are 8 or more column groups (measured at 1x768x6144 and
     // 16x256x6144).  Fewer groups split K (each wave keeps at least one
-    // 128-element work unit).
+    // 128-element work unit); with three or four blocks of 16 rows of A,
+    // two K slices (measured at 64 x 256..2048 x 6144).
     const int64_t groups = round_up(N, kRowPad) / 16;
     int s = split_req;
     if (s <= 0) {
         s = (int)((8 + groups - 1) / groups);
+        if (M > 32 && s < 2) s = 2;
         const int cap = steps / kSkinnyWaves;
         if (s > cap) s = cap;
     }
@@ -411,7 +413,9 @@ int make_plan(int64_t M, int64_t N, int64_t K, int path, int tile, int split_req
         // 6144 .. 8192 (device time per call):
         //  * the dot-product kernel wins only while the whole output is at
         //    most 2048 elements of one or two rows; beyond that the skinny
-        //    kernel's 16-row MFMA blocks are faster;
+        //    kernel's 16-row MFMA blocks are faster, up to 64 rows while
+        //    N <= 2048 (one workgroup per CU and 16 columns: more columns
+        //    than that make more than one round);
         //  * the LDS-fed tile kernel wins once its tiles give about 3/4 of
         //    a workgroup per CU: 256 x 256 tiles, else 128 x 128 tiles
         //    (with two K slices below two tiles per CU);
@@ -421,7 +425,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int path, int tile, int split_req
         const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
         if (M <= 2 && M * N <= 2048) {
             path = NVFP4_PATH_GEMV;
-        } else if (M <= 16) {
+        } else if (M <= 16 || (M <= 64 && N <= 2048)) {
             path = NVFP4_PATH_SKINNY;
         } else if (t256 >= (3 * kCUs) / 4) {
             path = NVFP4_PATH_TILE;
@@ -444,7 +448,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int path, int tile, int split_req
             p->tiles_m = 1;
             p->tiles_n = (int)(round_up(N, kRowPad) / 4);
             break;
-        case NVFP4_PATH_SKINNY: plan_skinny(N, steps, split_req, p); break;
+        case NVFP4_PATH_SKINNY: plan_skinny(M, N, steps, split_req, p); break;
         case NVFP4_PATH_WSPLIT: plan_wsplit(M, N, steps, tile, split_req, p); break;
         default: plan_tile(M, N, steps, tile, split_req, p); break;
     }

@@ -50,7 +50,7 @@ def candidates(M: int, N: int, K: int) -> list[tuple[int, int, int]]:
     out = []
     if M <= 4:
         out.append((nv.PATH_GEMV, 0, 1))
-    if M <= 16:
+    if M <= 64:
         groups = cdiv(N, 16)
         for s in (1, 2, 4, 8, 16):
             if s <= max(1, steps // SKINNY_WAVES) and groups * s <= 4096:

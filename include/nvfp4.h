@@ -61,7 +61,7 @@ typedef enum nvfp4_status {
 enum {
     NVFP4_PATH_AUTO = 0,   /* library's choice from M, N, K */
     NVFP4_PATH_TILE = 1,   /* large shapes: MFMA tiles fed through an LDS ring */
-    NVFP4_PATH_SKINNY = 2, /* M <= 16: decode shapes, one wave per K range */
+    NVFP4_PATH_SKINNY = 2, /* M <= 64: decode shapes, waves share a column group's K range */
     NVFP4_PATH_WSPLIT = 3, /* mid-size shapes: the waves of a workgroup split K */
     NVFP4_PATH_GEMV = 4    /* M <= 4: one wave per column of C, dot products */
 };
@@ -134,7 +134,7 @@ int nvfp4_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
  *             the number of 128-element K steps
  * Same contract as nvfp4_gemm.  A bad path or tile is NVFP4_ERR_INVALID_VALUE;
  * NVFP4_ERR_UNSUPPORTED if the forced path cannot run the shape (skinny needs
- * M <= 16, gemv M <= 4).  Every plan gives the same result up to the order of
+ * M <= 64, gemv M <= 4).  Every plan gives the same result up to the order of
  * the FP32 additions (see nvfp4_gemm); a given plan is deterministic. */
 int nvfp4_gemm_with_plan(const void* a_packed, const void* a_scales, const void* b_packed,
                          const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
@@ -223,7 +223,7 @@ int nvfp4_plan(int64_t M, int64_t N, int64_t K, nvfp4_plan_t* plan);
  * "path" is "tile", "skinny", "wsplit" or "gemv"; "tile" and "split_k" follow
  * nvfp4_gemm_with_plan (tile 0 = the path's default; split_k >= 1); other
  * keys are ignored.  Every entry is checked: sizes as for nvfp4_gemm, the
- * tile allowed for the path, skinny only for M <= 16 and gemv for M <= 4.
+ * tile allowed for the path, skinny only for M <= 64 and gemv for M <= 4.
  * A later entry for the same (M, N, K) replaces an earlier one.
  * nvfp4_gemm (NVFP4_PATH_AUTO, nothing forced) then uses, for (M, N, K): the
  * entry for exactly that shape, else the entry with the same N and K and the

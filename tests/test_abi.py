@@ -95,8 +95,8 @@ def test_gemm_rejects_bad_arguments_before_launch():
     assert _raw(a=0x1004) == nv.ERR_MISALIGNED
     assert _raw(out=0x5002) == nv.ERR_MISALIGNED
     lib = nv.lib()
-    # a forced skinny path needs M <= 16
-    assert _wp(17, 4, 64, nv.PATH_SKINNY) == nv.ERR_UNSUPPORTED
+    # a forced skinny path needs M <= 64
+    assert _wp(65, 4, 64, nv.PATH_SKINNY) == nv.ERR_UNSUPPORTED
     assert _wp(5, 4, 64, nv.PATH_GEMV) == nv.ERR_UNSUPPORTED
     assert _wp(4, 4, 64, 7) == nv.ERR_INVALID_VALUE
     assert _wp(4, 4, 64, 0, split_k=-1) == nv.ERR_INVALID_VALUE
@@ -185,9 +185,12 @@ def test_plan(no_table):
     assert key(1024, 2048, 6144) == ("wsplit", 128, 1)        # 256 tiles of 128 x 64
     assert key(512, 2048, 6144) == ("wsplit", 64, 1)
     assert key(512, 768, 6144) == ("wsplit", 64, 2)
-    assert key(32, 256, 6144) == ("wsplit", 64, 3)            # at most 3 slices
-    for M, N, K in [(512, 768, 6144), (512, 2048, 6144), (17, 8, 16), (300, 5000, 64),
-                    (64, 64, 4096)]:
+    # skinny up to 64 rows while N <= 2048, two K slices from 33 rows on
+    assert key(32, 256, 6144)[0] == "skinny" and nv.plan(32, 256, 6144)["split_k"] == 1
+    assert key(64, 2048, 6144)[0] == "skinny" and nv.plan(64, 2048, 6144)["split_k"] == 2
+    assert key(64, 6144, 6144)[0] == "wsplit"
+    assert key(65, 256, 6144) == ("wsplit", 64, 3)            # at most 3 slices
+    for M, N, K in [(512, 768, 6144), (512, 2048, 6144), (300, 5000, 64), (128, 64, 4096)]:
         p = nv.plan(M, N, K)
         assert p["path"] == nv.PATH_WSPLIT and 1 <= p["split_k"] <= 3
         # split K only while every workgroup keeps a CU to itself

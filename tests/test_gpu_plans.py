@@ -75,6 +75,24 @@ def test_forced_skinny(o, split_k):
     assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
 
 
+@pytest.mark.parametrize("split_k", [1, 3])
+@pytest.mark.parametrize("M", [17, 32, 33, 48, 49, 64])
+def test_skinny_several_row_blocks(o, M, split_k):
+    """The skinny kernel with 2-4 blocks of 16 rows of A sharing each decoded
+    B fragment (ragged last block), with and without split-K."""
+    ops = synth.random_operands(4444 + M, M, 200, 2192, alpha=-1.5)
+    say(f"skinny {M} rows split {split_k}: {ops.M}x{ops.N}x{ops.K}")
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    out = nv.gemm(a, b, ops.alpha, path=nv.PATH_SKINNY, split_k=split_k)
+    torch.cuda.synchronize()
+    g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
+    bits, exact, mag = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha)
+    r = compare(g, bits, exact, mag, ops.alpha)
+    say(f"  {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
+
+
 @pytest.mark.parametrize("tile", [256, 128, 64])
 def test_persistent_grid_each_tile(o, tile):
     """5100 x 5104 x 576: 400, 1600 and 6400 tiles of 256, 128 and 64, more

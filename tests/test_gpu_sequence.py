@@ -37,7 +37,7 @@ def bits(t):
 class Step:
     """One decode step: quantise the fp32 activations of 16 tokens and of 1
     token, an MoE up-projection share (16 x 256 x 6144, skinny), an
-    attention projection (1 x 768 x 6144, dot products), a 32-row GEMM whose
+    attention projection (1 x 768 x 6144, dot products), a 48-row GEMM whose
     plan splits K across workgroups (workspace), and a grouped GEMM of the
     16 tokens routed to 2 of 8 experts."""
 
@@ -46,7 +46,7 @@ class Step:
         K = 6144
         self.x16 = torch.randn((16, K), generator=g, device=DEV)
         self.x1 = torch.randn((1, K), generator=g, device=DEV)
-        self.x32 = torch.randn((32, K), generator=g, device=DEV)
+        self.x48 = torch.randn((48, K), generator=g, device=DEV)
         self.w_up = nv.quantize(torch.randn((256, K), generator=g, device=DEV))
         self.w_attn = nv.quantize(torch.randn((768, K), generator=g, device=DEV) * 0.02)
         self.w_mid = nv.quantize(torch.randn((200, K), generator=g, device=DEV))
@@ -57,22 +57,22 @@ class Step:
         self.xg = torch.randn((self.tok, K), generator=g, device=DEV)
         mk = lambda r: nv.PackedOperand(*(torch.empty(n, dtype=torch.uint8, device=DEV)
                                           for n in nv.packed_size(r, K)), r, K)
-        self.a16, self.a1, self.a32, self.ag = mk(16), mk(1), mk(32), mk(self.tok)
+        self.a16, self.a1, self.a48, self.ag = mk(16), mk(1), mk(48), mk(self.tok)
         self.out = {
             "up": torch.empty((16, 256), dtype=torch.bfloat16, device=DEV),
             "attn": torch.empty((1, 768), dtype=torch.bfloat16, device=DEV),
-            "mid": torch.empty((32, 200), dtype=torch.bfloat16, device=DEV),
+            "mid": torch.empty((48, 200), dtype=torch.bfloat16, device=DEV),
             "moe": torch.empty((self.tok, 64), dtype=torch.bfloat16, device=DEV),
         }
 
     def eager(self, stream=None):
         nv.quantize(self.x16, out=self.a16, stream=stream)
         nv.quantize(self.x1, out=self.a1, stream=stream)
-        nv.quantize(self.x32, out=self.a32, stream=stream)
+        nv.quantize(self.x48, out=self.a48, stream=stream)
         nv.quantize(self.xg, out=self.ag, stream=stream)
         nv.gemm(self.a16, self.w_up, 1.0, out=self.out["up"], stream=stream)
         nv.gemm(self.a1, self.w_attn, 0.5, out=self.out["attn"], stream=stream)
-        nv.gemm(self.a32, self.w_mid, -1.25, out=self.out["mid"], stream=stream)
+        nv.gemm(self.a48, self.w_mid, -1.25, out=self.out["mid"], stream=stream)
         nv.grouped_gemm(self.ag, self.experts, self.offsets, 0.75, out=self.out["moe"],
                         stream=stream)
 
@@ -80,11 +80,11 @@ class Step:
         s = nv.Sequence()
         s.add_quantize(self.x16, self.a16)
         s.add_quantize(self.x1, self.a1)
-        s.add_quantize(self.x32, self.a32)
+        s.add_quantize(self.x48, self.a48)
         s.add_quantize(self.xg, self.ag)
         s.add_gemm(self.a16, self.w_up, self.out["up"], 1.0)
         s.add_gemm(self.a1, self.w_attn, self.out["attn"], 0.5)
-        s.add_gemm(self.a32, self.w_mid, self.out["mid"], -1.25)
+        s.add_gemm(self.a48, self.w_mid, self.out["mid"], -1.25)
         s.add_grouped_gemm(self.ag, self.experts, self.offsets, self.out["moe"], 0.75)
         return s
 
@@ -100,7 +100,7 @@ class Step:
 def test_sequence_replays_match_eager_calls():
     step = Step(31)
     plans = {k: nv.plan(*shape) for k, shape in
-             [("up", (16, 256, 6144)), ("attn", (1, 768, 6144)), ("mid", (32, 200, 6144))]}
+             [("up", (16, 256, 6144)), ("attn", (1, 768, 6144)), ("mid", (48, 200, 6144))]}
     say(f"sequence plans {plans}")
     assert plans["mid"]["split_k"] > 1          # the sequence's own workspace is used
     seq = step.record()
@@ -110,7 +110,7 @@ def test_sequence_replays_match_eager_calls():
     for replay in range(4):
         # new activations, written by the program's own eager work
         with torch.no_grad():
-            for x in (step.x16, step.x1, step.x32, step.xg):
+            for x in (step.x16, step.x1, step.x48, step.xg):
                 x.normal_()
                 x.mul_(1.0 + replay)
         torch.cuda.synchronize()
@@ -160,22 +160,22 @@ def test_eager_call_under_capture_needs_its_workspace_first():
     reports NVFP4_ERR_CAPTURE and enqueues nothing; after one eager call on
     that stream the same call captures and replays correctly."""
     step = Step(5)
-    nv.quantize(step.x32, out=step.a32)
+    nv.quantize(step.x48, out=step.a48)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
-    assert nv.plan(32, 200, 6144)["split_k"] > 1
+    assert nv.plan(48, 200, 6144)["split_k"] > 1
     g = torch.cuda.CUDAGraph()
     with pytest.raises(nv.Nvfp4Error) as e:
         with torch.cuda.graph(g, stream=s):
-            nv.gemm(step.a32, step.w_mid, 1.0, out=step.out["mid"], stream=s)
+            nv.gemm(step.a48, step.w_mid, 1.0, out=step.out["mid"], stream=s)
     assert e.value.status == nv.ERR_CAPTURE
     with torch.cuda.stream(s):
-        nv.gemm(step.a32, step.w_mid, 1.0, out=step.out["mid"], stream=s)
+        nv.gemm(step.a48, step.w_mid, 1.0, out=step.out["mid"], stream=s)
     s.synchronize()
     want = bits(step.out["mid"])
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        nv.gemm(step.a32, step.w_mid, 1.0, out=step.out["mid"], stream=s)
+        nv.gemm(step.a48, step.w_mid, 1.0, out=step.out["mid"], stream=s)
     for _ in range(3):
         step.clear()
         torch.cuda.synchronize()

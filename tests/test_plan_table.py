@@ -133,7 +133,7 @@ BAD_TABLES = {
     "tile the path lacks": [entry(64, 64, 128, "tile", 96)],
     "wsplit tile 256": [entry(64, 64, 128, "wsplit", 256)],
     "skinny tile": [entry(8, 64, 128, "skinny", 16)],
-    "skinny above 16 rows": [entry(17, 64, 128, "skinny")],
+    "skinny above 64 rows": [entry(65, 64, 128, "skinny")],
     "gemv above 4 rows": [entry(5, 64, 128, "gemv")],
     "split_k 0": [entry(64, 64, 128, "tile", 64, 0)],
     "split_k missing": [{"M": 64, "N": 64, "K": 128, "path": "tile", "tile": 64}],
