@@ -182,3 +182,32 @@ def test_eager_call_under_capture_needs_its_workspace_first():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits(step.out["mid"]), want)
+
+
+def test_sequence_with_two_launch_tile_call():
+    """A call whose plan runs as two launches (256 x 256 tiles, the last
+    round split along K: 384 tiles) inside a recorded sequence: replays equal
+    the eager call bit for bit."""
+    M, N, K = 4096, 6144, 512
+    p = nv.plan(M, N, K)
+    assert p["tail_tiles"] > 0, p
+    g = torch.Generator(device=DEV).manual_seed(99)
+    x = torch.randn((M, K), generator=g, device=DEV)
+    a = nv.quantize(x)
+    b = nv.quantize(torch.randn((N, K), generator=g, device=DEV))
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    nv.gemm(a, b, 0.5, out=out)
+    torch.cuda.synchronize()
+    want = bits(out)
+    seq = nv.Sequence()
+    seq.add_gemm(a, b, out, 0.5)
+    seq.finalize()
+    for replay in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        seq.launch()
+        torch.cuda.synchronize()
+        same = np.array_equal(bits(out), want)
+        say(f"two-launch call in a sequence, replay {replay}: identical = {same}")
+        assert same
+    seq.close()
