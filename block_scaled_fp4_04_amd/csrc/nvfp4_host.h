@@ -11,12 +11,12 @@
 
 namespace nvfp4 {
 
-enum JobKind { JOB_GEMM = 0, JOB_GROUPED = 1, JOB_QUANTIZE = 2 };
+enum JobKind { JOB_GEMM = 0, JOB_GROUPED = 1, JOB_QUANTIZE = 2, JOB_GROUPED_TILE = 3 };
 
 struct Job {
     int kind = JOB_GEMM;
-    Plan plan{};                 // JOB_GEMM
-    GemmArgs gemm{};             // JOB_GEMM (workspace pointers set at launch)
+    Plan plan{};                 // JOB_GEMM (JOB_GROUPED_TILE: plan.cfg)
+    GemmArgs gemm{};             // JOB_GEMM, JOB_GROUPED_TILE (workspace pointers set at launch)
     size_t floats = 0;           // split-K partial floats the job needs
     size_t counters = 0;         // split-K arrival counters the job needs
     GroupedArgs grouped{};       // JOB_GROUPED

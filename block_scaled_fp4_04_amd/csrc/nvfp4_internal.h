@@ -36,6 +36,8 @@ struct GemmArgs {
                                  // tiles_m x tiles_n grid this launch computes (tile kernel)
     int tail_tiles, tail_split;  // tile kernel without split-K: the last tail_tiles tiles
                                  // run in a second launch split tail_split ways along K
+    const int32_t* offsets;   // grouped tile launch: [groups + 1] row offsets (device), else null
+    int groups;               // grouped tile launch: number of groups (B holds one N x K operand each)
 };
 
 // Tile configurations of the large-M kernel.
@@ -79,6 +81,7 @@ constexpr int kGroupedWaves = 8;   // waves per workgroup (split K)
 constexpr int kGroupedChunks = 2;  // 16-row chunks of A per pass over B
 constexpr int kGroupedUnits = 1;   // 128-element K units of loads in flight per wave
 constexpr int kGroupedBlocks = 4;  // 16-row blocks of B per workgroup (share A's decode)
+constexpr int kGroupedTileRows = 256;  // groups this large on average use the tile kernel
 
 struct GroupedArgs {
     const uint8_t* a_codes;   // [P][Mp][32], all M rows
@@ -94,6 +97,11 @@ struct GroupedArgs {
     int G;                    // number of groups
 };
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);
+
+// Grouped GEMM with large groups on the tile kernel (256 x 256 tiles): one
+// workgroup per (row block of a group, column block) of an upper bound of
+// tiles_m = ceil(M / 256) + groups row blocks.
+hipError_t launch_grouped_tile(const GemmArgs& a, hipStream_t stream);
 
 // NVFP4 quantisation of fp32 rows into the packed operand layout.
 struct QuantArgs {

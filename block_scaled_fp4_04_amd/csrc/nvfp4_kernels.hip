@@ -70,7 +70,7 @@ namespace {
 // last of a tile's workgroups to arrive adds the partial tiles in split order
 // (deterministic) and runs the epilogue.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NS, bool SPLIT>
+template <int BM, int BN, int NS, bool SPLIT, bool GROUPED = false>
 __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     constexpr int MI = BM / 64;  // 32-row blocks per wave
     constexpr int NI = BN / 64;  // 32-column blocks per wave
@@ -93,7 +93,8 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     // epilogue cannot borrow ring buffers; this brings the workgroup to the
     // 160 KB of LDS).
     constexpr bool STAGED_OUT = BM == 256 && BN == 256;
-    __shared__ __attribute__((aligned(16))) uint8_t out_stage[STAGED_OUT ? 4 * 4096 : 16];
+    // (also the grouped mode's scheduling scratch, before the main loop)
+    __shared__ __attribute__((aligned(16))) uint8_t out_stage[STAGED_OUT ? 4 * 4096 : 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -111,7 +112,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     const int T = a.tile_count;
     const int S = SPLIT ? a.split_k : 1;
     const int G = SPLIT ? 1 : (int)gridDim.x;
-    const int n_items = SPLIT ? 1 : (T - (int)blockIdx.x + G - 1) / G;
+    const int n_items = (SPLIT || GROUPED) ? 1 : (T - (int)blockIdx.x + G - 1) / G;
     auto item_of = [&](int it, int& t, int& z) {
         int bid = (int)blockIdx.x + it * G;
         const int total = T * S;
@@ -130,6 +131,66 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     };
     int t0, z0;
     item_of(0, t0, z0);
+
+    // Grouped mode (a mixture-of-experts layer with large groups): group g
+    // owns rows [offsets[g], offsets[g+1]) of A and C and its own B operand.
+    // The row blocks of all groups are numbered in group order (group g has
+    // ceil(rows_g / BM) of them); tile t0 is row block t0 / tiles_n, column
+    // block t0 % tiles_n, and the grid is an upper bound on the tiles.  Each
+    // thread counts the row blocks of a contiguous range of groups, a
+    // workgroup-wide prefix sum places the ranges, and the thread whose range
+    // holds the row block publishes (group, first row, end row); a workgroup
+    // past the last row block exits.  Offsets are clamped to [0, M] as in the
+    // grouped skinny kernel.  Scratch: the epilogue's staging block.
+    int grp = 0, grp_row0 = 0, row_end = a.M;
+    if constexpr (GROUPED) {
+        int* sch = reinterpret_cast<int*>(out_stage);  // [0..3] wave totals, [4..7] result
+        const int vm = t0 / a.tiles_n;
+        const int per = (a.groups + 255) / 256;
+        const int g_lo = min(tid * per, a.groups), g_hi = min(g_lo + per, a.groups);
+        auto rows_of = [&](int g, int& r0, int& r1) {
+            r0 = min(max(a.offsets[g], 0), a.M);
+            r1 = min(max(a.offsets[g + 1], r0), a.M);
+        };
+        int cnt = 0;
+        for (int g = g_lo; g < g_hi; ++g) {
+            int r0, r1;
+            rows_of(g, r0, r1);
+            cnt += (r1 - r0 + BM - 1) / BM;
+        }
+        int incl = cnt;  // inclusive prefix sum over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (tid == 0) sch[7] = 0;
+        if (lane == 63) sch[wave] = incl;
+        __syncthreads();
+        int excl = incl - cnt;
+        for (int w = 0; w < wave; ++w) excl += sch[w];
+        if (vm >= excl && vm < excl + cnt) {
+            int v = vm - excl;
+            for (int g = g_lo; g < g_hi; ++g) {
+                int r0, r1;
+                rows_of(g, r0, r1);
+                const int c = (r1 - r0 + BM - 1) / BM;
+                if (v < c) {
+                    sch[4] = g;
+                    sch[5] = r0 + v * BM;
+                    sch[6] = r1;
+                    sch[7] = 1;
+                    break;
+                }
+                v -= c;
+            }
+        }
+        __syncthreads();
+        if (sch[7] == 0) return;  // no tile: the whole workgroup leaves
+        grp = __builtin_amdgcn_readfirstlane(sch[4]);
+        grp_row0 = __builtin_amdgcn_readfirstlane(sch[5]);
+        row_end = __builtin_amdgcn_readfirstlane(sch[6]);
+    }
     const int nst = a.P / 2;
     const int p0 = 2 * (int)((int64_t)z0 * nst / S);
     const int p1 = 2 * (int)((int64_t)(z0 + 1) * nst / S);
@@ -168,9 +229,10 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
         s_lane[i] = (uint32_t)(half * (R / 2) + (sr % G2) * 32 + sr / G2) * 4u;
     }
     const __amdgpu_buffer_rsrc_t rac = make_rsrc(a.a_codes, (uint32_t)a.P * a.Mp * 32u);
-    const __amdgpu_buffer_rsrc_t rbc = make_rsrc(a.b_codes, (uint32_t)a.P * a.Np * 32u);
+    const int64_t b_rows = GROUPED ? (int64_t)grp * a.P * a.Np : 0;  // B rows of the groups before
+    const __amdgpu_buffer_rsrc_t rbc = make_rsrc(a.b_codes + b_rows * 32, (uint32_t)a.P * a.Np * 32u);
     const __amdgpu_buffer_rsrc_t ras = make_rsrc(a.a_scales, (uint32_t)a.P * a.Mp * 4u);
-    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(a.b_scales, (uint32_t)a.P * a.Np * 4u);
+    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(a.b_scales + b_rows * 4, (uint32_t)a.P * a.Np * 4u);
     // Tile whose panels are being loaded: byte offsets of its first A and B
     // rows inside a code panel (inside a scale panel: / 8).
     uint32_t base_a = 0, base_b = 0;
@@ -306,7 +368,12 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
     auto start_item = [&](int it, int& m0, int& n0) {
         int t, z;
         item_of(it, t, z);
-        origin_of(t, m0, n0);
+        if constexpr (GROUPED) {
+            m0 = grp_row0;
+            n0 = (t % a.tiles_n) * BN;
+        } else {
+            origin_of(t, m0, n0);
+        }
         cur_it = it;
         if (it + 1 < n_items) {
             item_of(it + 1, t, z);
@@ -351,7 +418,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
         const int row0 = m0 + wm * (BM / 2) + i * 32;
         const int col0 = n0 + wn * (BN / 2) + j * 32;
         uint8_t* base = reinterpret_cast<uint8_t*>(a.out + (int64_t)row0 * a.N + col0);
-        if (row0 + lq < a.M) {
+        if (row0 + lq < row_end) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int col = col0 + 8 * u + 4 * lh;
@@ -416,7 +483,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
                     const int r = k * 8 + rrow;
                     const uint4 v = *reinterpret_cast<const uint4*>(st + r * 128 + ((rch * 16) ^ ((r & 7) * 16)));
                     const int row = m0 + wm * (BM / 2) + i * 32 + r;
-                    if (row < a.M && col < a.N)
+                    if (row < row_end && col < a.N)
                         *reinterpret_cast<uint4*>(a.out + (int64_t)row * a.N + col) = v;
                 }
             }
@@ -1074,6 +1141,12 @@ hipError_t launch_tile_range(int cfg, const GemmArgs& a, int device, hipStream_t
     return hipGetLastError();
 }
 }  // namespace
+
+hipError_t launch_grouped_tile(const GemmArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((tile_kernel<256, 256, 8, false, true>), dim3((unsigned)a.tile_count), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
 
 size_t wsplit_partial_floats(int cfg, const GemmArgs& a) {
     if (a.split_k <= 1) return 0;

@@ -183,6 +183,11 @@ int nvfp4_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* pa
  *                        group are overwritten, rows outside every group are
  *                        left untouched
  *   M                  : total rows (0 is allowed: nothing is launched)
+ * Groups of about 16-250 rows (M / groups < 256) run on a skinny kernel
+ * built for the memory-bound decode regime; larger groups (prefill) run on
+ * the MFMA tile kernel with 256 x 256 tiles, one workgroup per row block of
+ * a group and column block.  Either way the result is the same GEMM, up to
+ * the order of the FP32 additions.
  * Same alignment (row_offsets: 4 bytes), status and stream rules as
  * nvfp4_gemm; no workspace, no allocation. */
 int nvfp4_grouped_gemm(const void* a_packed, const void* a_scales, const void* b_packed,

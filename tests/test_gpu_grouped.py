@@ -123,3 +123,40 @@ def test_grouped_no_rows():
     st = nv.lib().nvfp4_grouped_gemm(0x1000, 0x2000, 0x3000, 0x4000, 0x6000, 4, 1.0, 0x5000,
                                      0, 16, 128, None)
     assert st == nv.OK
+
+
+# Groups of 256 rows or more on average run on the tile kernel (256 x 256
+# tiles: row blocks of each group, with a partial block at every group's
+# end); the first case stays on the grouped skinny kernel (about 100 rows
+# per group, several passes over B per workgroup).
+@pytest.mark.parametrize("sizes,N,K", [
+    ([0, 70, 130, 1, 257, 64, 200], 200, 640),      # skinny path, empty and 1-row groups
+    ([300, 512, 0, 700, 259], 264, 1040),            # tile path, K not a multiple of 128
+    ([256] * 4 + [512], 256, 2048),                  # tile path, whole blocks only
+    ([1, 1000, 3, 300], 136, 384),                   # tile path, tiny and large groups
+])
+def test_grouped_tile_path(o, sizes, N, K):
+    ops = random_grouped(sum(sizes) * 3 + N + K, sizes, N, K, alpha=-0.625)
+    g = run_grouped(ops, label="grouped (tile path)")
+    check(o, ops, g, f"grouped tile path sizes={sizes} N={N} K={K}")
+
+
+def test_grouped_tile_path_clamps_and_leaves_other_rows(o):
+    """Tile path with a malformed table (entries outside [0, M] are clamped)
+    and a table that ends before M (the rows after it keep their contents)."""
+    sizes = [400, 260, 300]
+    ops = random_grouped(77, sizes, 136, 512, alpha=1.5)
+    M, N = ops.M, ops.N
+    bad = np.array([0, -9, 400, 10 ** 6], np.int32)           # acts as [0, 0, 400, M]
+    eff = synth.GroupedOperands(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales,
+                                np.array([0, 0, 400, M], np.int32), ops.alpha, M, N, ops.K, 3)
+    g = run_grouped(ops, offsets=bad, label="tile path, clamped offsets")
+    check(o, eff, g, "tile path, clamped offsets")
+    short = np.array([0, 400, 660, M - 70], np.int32)
+    out = torch.full((M, N), 3.0, dtype=torch.bfloat16, device=DEV)
+    g2 = run_grouped(ops, offsets=short, out=out, label="tile path, short table")
+    eff2 = synth.GroupedOperands(ops.a_codes[:M - 70], ops.a_scales[:M - 70], ops.b_codes,
+                                 ops.b_scales, short, ops.alpha, M - 70, N, ops.K, 3)
+    check(o, eff2, g2[:M - 70], "tile path, short table")
+    three = int(torch.tensor([3.0], dtype=torch.bfloat16).view(torch.int16).item()) & 0xFFFF
+    assert np.all(g2[M - 70:] == three)
