@@ -77,7 +77,7 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream);  // M <= 4
 
 // Grouped (mixture-of-experts) GEMM: G weight operands of N x K, rows of A
 // assigned to groups by a device table of G + 1 offsets.
-constexpr int kGroupedWaves = 8;   // waves per workgroup (split K)
+constexpr int kGroupedWaves = 4;   // waves per workgroup (split K)
 constexpr int kGroupedChunks = 2;  // 16-row chunks of A per pass over B
 constexpr int kGroupedUnits = 1;   // 128-element K units of loads in flight per wave
 constexpr int kGroupedBlocks = 4;  // 16-row blocks of B per workgroup (share A's decode)
