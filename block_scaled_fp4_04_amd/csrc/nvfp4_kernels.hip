@@ -68,7 +68,19 @@ namespace {
 // Split-K (split_k > 1): the K steps are divided into split_k contiguous
 // ranges; each workgroup publishes its FP32 tile to the workspace, and the
 // last of a tile's workgroups to arrive adds the partial tiles in split order
-// (deterministic) and runs the epilogue.
+// (deterministic) and runs the epilogue.  A persistent launch whose last
+// round would be at most half full is issued as two launches (launch_tile):
+// the full rounds, then the remaining tiles with their K range split.
+//
+// Epilogue: 256 x 256 tiles (with N % 8 == 0) pass the output through a
+// per-wave LDS staging block so that every store writes whole 128-byte
+// lines; the other configurations store 8-byte pieces straight from the
+// accumulators.
+//
+// Grouped mode (GROUPED): the experts of a mixture-of-experts layer with
+// large groups; each workgroup finds its group and row block from the
+// device offsets table (see the code), multiplies that group's B, and
+// stores only the group's rows.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int NS, bool SPLIT, bool GROUPED = false>
 __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
