@@ -561,9 +561,60 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
             step(r, r, r0, r1, false);
             step(r + 1, r + 1, r1, r0, false);
         }
-        // Split-K: publish the partial tile; the last arrival reduces in
-        // split order.
         wait_vmcnt<0>();  // drain the look-ahead loads before the LDS is released
+        __shared__ int s_last;
+        if (S == 2) {
+            // Two K slices: the sum of two partial tiles does not depend on
+            // their order, so only the workgroup that finishes first
+            // publishes its tile; the second adds it to its own accumulators.
+            // The tile's counter takes one increment per arrival and one
+            // from the first workgroup once its tile is out, so the second
+            // (ticket 1 or 2) waits until it reads 3.  The first workgroup
+            // never waits, so the wait ends; it is bounded all the same.
+            __syncthreads();
+            if (tid == 0) s_last = (int)arrive(a.counters + t0);
+            __syncthreads();
+            const int64_t slot = (int64_t)t0 * S * (BM * BN);
+            if (s_last == 0) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            publish(a.partials + slot + ((i * NI + j) * 16 + v) * 256 + tid, acc[i][j][v]);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (tid == 0) (void)arrive(a.counters + t0);  // the partial tile is out
+                return;
+            }
+            if (tid == 0) {
+                for (int it = 0; it < (1 << 22); ++it) {
+                    if (__hip_atomic_load(a.counters + t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= 3u) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                reset_counter(a.counters + t0);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const float* po = a.partials + slot + (i * NI) * 16 * 256 + tid;
+                float sum[NI][16];
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sum[j][v] = fetch(po + (j * 16 + v) * 256);
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sum[j][v] += acc[i][j][v];
+#pragma unroll
+                for (int j = 0; j < NI; ++j) store_block(m0, n0, i, j, [&](int v) { return sum[j][v]; });
+            }
+            return;
+        }
+        // More slices: every workgroup publishes its partial tile; the last
+        // arrival adds them in split order.
         float* mine = a.partials + ((int64_t)t0 * S + z0) * (BM * BN);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -572,7 +623,6 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     publish(mine + ((i * NI + j) * 16 + v) * 256 + tid, acc[i][j][v]);
-        __shared__ int s_last;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
