@@ -988,80 +988,97 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // Dot-product kernel for M <= MR (MR <= 4): decode-sized GEMMs with one to
-// four rows of A, bound by streaming B and by latency.
+// four rows of A, bound by streaming B and by memory latency.
 //
-// With so few rows an MFMA would spend half its decode work on the padding
-// rows of A, and one workgroup per 16 columns leaves most CUs idle.  Here
-// each wave owns one row n of B over the whole of K, so 4-wave workgroups
-// cover N/4 CUs' worth of work without any cross-workgroup reduction:
-//   * A (M rows) is decoded once per workgroup into LDS as exact fp16;
-//   * B codes are widened to fp16 without their scale (v_cvt_scalef32_pk_
-//     f16_fp4, scale 1.0) and dotted with A in pairs (v_dot2_f32_f16): within
-//     a 16-element block every term shares one A and one B scale, so the
-//     block sum of (code_b * a') needs at most 12 significant bits and is
-//     exact in FP32; one FMA then applies the block's B scale and adds the
-//     block to the running sum (the only rounding, as in an MFMA
-//     accumulator);
-//   * lane l reads half-panels l, l+64, ... of its row (16 bytes of codes and
-//     2 bytes of scales each), all issued before the wave waits;
-//   * the 64 lane sums are added by a fixed butterfly, lane 0 stores.
-// K is processed in chunks of KC elements so A fits in LDS for any K.
+// With so few rows an MFMA would spend most of its decode work on the
+// padding rows of A, and one workgroup per 16 columns leaves most CUs idle.
+// Here each wave owns one row n of B over the whole of K, so there is no
+// cross-wave or cross-workgroup reduction, and nothing goes through LDS:
+//   * lane l takes half-panels l, l+64, ... of row n of B and the same
+//     half-panels of the MR rows of A (16 bytes of codes and 2 bytes of
+//     scales each, A from the L2 after its first reader); every load of a
+//     batch is issued before the first wait, so one memory round trip
+//     covers K up to 8192, and each half-panel is worked on as soon as its
+//     own loads are in;
+//   * codes of both operands are widened to fp16 without their scales
+//     (v_cvt_scalef32_pk_f16_fp4, scale 1.0) and dotted in pairs
+//     (v_dot2_f32_f16); inside a 16-element block the code products are
+//     multiples of 1/4 below 36, so the block sum is exact in FP32, and
+//     one FMA applies the product of the two block scales (exact: at most
+//     8 significant bits, and the scaled block sum at most 20) while adding
+//     the block to the running sum -- the only rounding, as in an MFMA
+//     accumulator;
+//   * the 64 lane sums are added in a fixed order with DPP moves (within
+//     rows of 16 lanes, then across rows), and lane 63 stores.
 // ---------------------------------------------------------------------------
-template <int MR>
-__global__ void __launch_bounds__(256) gemv_kernel(GemmArgs a) {
-    constexpr int KC = 8192;                 // K elements per chunk (128 panels)
-    constexpr int HPL = KC / 32 / 64;        // half-panels per lane per chunk (4)
-    __shared__ __attribute__((aligned(16))) _Float16 as[MR][KC];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int n = blockIdx.x * 4 + wave;     // B row (< Np: the grid is Np / 4)
-    const int M = a.M;
-    const int Kp = a.P * 64;
+// Source operand of a DPP move with zero fill for lanes it does not cover.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_src(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, true));
+}
+
+// Sum of x over the 64 lanes of the wave, complete in lane 63: windows of
+// 2, 4, 8 and 16 lanes inside each row of 16 (row_shr:1,2,4,8), then row 0
+// into row 1 and row 2 into row 3 (row_bcast:15), then rows 0-1 into rows
+// 2-3 (row_bcast:31).  The order of the additions is fixed.
+__device__ __forceinline__ float wave_sum_lane63(float x) {
+    x += dpp_src<0x111, 0xF>(x);
+    x += dpp_src<0x112, 0xF>(x);
+    x += dpp_src<0x114, 0xF>(x);
+    x += dpp_src<0x118, 0xF>(x);
+    x += dpp_src<0x142, 0xA>(x);
+    x += dpp_src<0x143, 0xC>(x);
+    return x;
+}
+
+// Waves (rows of B) per workgroup.  Measured against 1 and 2 waves with
+// K = 6144-8192: 4 is the fastest from N = 768 up (1.3-1.7x faster than 1
+// wave at N = 6144-8192, and faster with operands beyond the last-level
+// cache); 1 or 2 waves win only at N = 256 (2.2-2.4 against 2.7 us).
+constexpr int kGemvWaves = 4;
+
+template <int MR, int HPL>
+__global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(GemmArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * kGemvWaves + (threadIdx.x >> 6);  // B row (< Np)
+    const int hp_total = a.P * 2;               // 32-element half-panels along K
 
     float acc[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
 
-    for (int k0 = 0; k0 < Kp; k0 += KC) {
-        const int kc = min(KC, Kp - k0);     // elements in this chunk (multiple of 128)
-        const int hp_total = kc / 32;        // half-panels in this chunk
-        // B loads of this chunk first, so their latency overlaps the A decode.
-        uint4 bw[HPL];
-        uint32_t bsc[HPL];
+    // Batches of HPL half-panels per lane.  The loads are unconditional (a
+    // lane past the end reads the last half-panel again and its block sums
+    // are weighted by zero), so the compiler can wait for each half-panel's
+    // loads alone and work on the first while the later ones arrive.
+    for (int base = 0; base < hp_total; base += 64 * HPL) {
+        uint4 bw[HPL], aw[HPL][MR];
+        uint32_t bsc[HPL], asc[HPL][MR];
 #pragma unroll
         for (int i = 0; i < HPL; ++i) {
-            const int hp = lane + 64 * i;
-            bw[i] = uint4{0u, 0u, 0u, 0u};
-            bsc[i] = 0u;
-            if (hp < hp_total) {
-                const int64_t panel = (int64_t)(k0 / 64) + hp / 2;
-                const int64_t row = panel * a.Np + n;
-                bw[i] = *reinterpret_cast<const uint4*>(a.b_codes + row * 32 + (hp & 1) * 16);
-                bsc[i] = *reinterpret_cast<const uint16_t*>(a.b_scales + row * 4 + (hp & 1) * 2);
+            const int hp = min(base + lane + 64 * i, hp_total - 1);
+            const int64_t panel = hp >> 1;
+            const int half = hp & 1;
+            const int64_t brow = panel * a.Np + n;
+            bw[i] = *reinterpret_cast<const uint4*>(a.b_codes + brow * 32 + half * 16);
+            bsc[i] = *reinterpret_cast<const uint16_t*>(a.b_scales + brow * 4 + half * 2);
+            // rows MR-1 < 16 <= Mp: padding rows of A are zeros in memory
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const int64_t arow = panel * a.Mp + m;
+                aw[i][m] = *reinterpret_cast<const uint4*>(a.a_codes + arow * 32 + half * 16);
+                asc[i][m] = *reinterpret_cast<const uint16_t*>(a.a_scales + arow * 4 + half * 2);
             }
         }
-        // A rows of this chunk -> LDS (exact fp16), one 8-element word per item.
-        __syncthreads();  // the previous chunk's A is no longer read
-        const int words = M * (kc / 8);
-        for (int w = tid; w < words; w += 256) {
-            const int m = w / (kc / 8), wk = w % (kc / 8);  // word wk of row m in the chunk
-            const int64_t panel = (int64_t)(k0 / 64) + wk / 8;
-            const int64_t row = panel * a.Mp + m;
-            const uint32_t code = *reinterpret_cast<const uint32_t*>(a.a_codes + row * 32 + (wk & 7) * 4);
-            const uint32_t sw = *reinterpret_cast<const uint32_t*>(a.a_scales + row * 4);
-            const h2 s2 = (wk & 7) < 4 ? e4m3x2_lo(sw) : e4m3x2_hi(sw);
-            const _Float16 sc = ((wk & 7) & 2) ? s2[1] : s2[0];  // block (wk & 7) / 2
-            const h8 v = decode8(code, sc);
-            *reinterpret_cast<h8*>(&as[m][wk * 8]) = v;
-        }
-        __syncthreads();
 #pragma unroll
         for (int i = 0; i < HPL; ++i) {
-            const int hp = lane + 64 * i;
-            if (hp >= hp_total) break;
-            const h2 sb = e4m3x2_lo(bsc[i]);  // scales of blocks 2*(hp&1), 2*(hp&1)+1
+            const bool live = base + lane + 64 * i < hp_total;
+            const h2 sb = e4m3x2_lo(bsc[i]);       // B scales of the half-panel's two blocks
+            h2 sa[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) sa[m] = e4m3x2_lo(asc[i][m]);
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
                 float bs[MR];
@@ -1069,39 +1086,35 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs a) {
                 for (int m = 0; m < MR; ++m) bs[m] = 0.0f;
 #pragma unroll
                 for (int wd = 0; wd < 2; ++wd) {
-                    const uint32_t word = word_of(bw[i], 2 * blk + wd);
-                    const int kk = hp * 32 + (2 * blk + wd) * 8;  // chunk-relative element
+                    const uint32_t w = word_of(bw[i], 2 * blk + wd);
+                    const h2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+                    const h2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+                    const h2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+                    const h2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
 #pragma unroll
                     for (int m = 0; m < MR; ++m) {
-                        if (m >= M) break;
-                        const h8 av = *reinterpret_cast<const h8*>(&as[m][kk]);
-                        bs[m] = __builtin_amdgcn_fdot2(h2{av[0], av[1]}, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0), bs[m], false);
-                        bs[m] = __builtin_amdgcn_fdot2(h2{av[2], av[3]}, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1), bs[m], false);
-                        bs[m] = __builtin_amdgcn_fdot2(h2{av[4], av[5]}, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2), bs[m], false);
-                        bs[m] = __builtin_amdgcn_fdot2(h2{av[6], av[7]}, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3), bs[m], false);
+                        const uint32_t v = word_of(aw[i][m], 2 * blk + wd);
+                        bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0), b0, bs[m], false);
+                        bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1), b1, bs[m], false);
+                        bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2), b2, bs[m], false);
+                        bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3), b3, bs[m], false);
                     }
                 }
-                const float sbf = (float)sb[blk];
+                const float sbf = live ? (float)sb[blk] : 0.0f;
 #pragma unroll
-                for (int m = 0; m < MR; ++m) acc[m] = __builtin_fmaf(bs[m], sbf, acc[m]);
+                for (int m = 0; m < MR; ++m)
+                    acc[m] = __builtin_fmaf(bs[m], live ? (float)sa[m][blk] * sbf : 0.0f, acc[m]);
             }
         }
     }
-    // Fixed butterfly over the 64 lanes of the wave.
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-        float x = acc[m];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-        acc[m] = x;
-    }
-    if (lane == 0 && n < a.N) {
+    for (int m = 0; m < MR; ++m) acc[m] = wave_sum_lane63(acc[m]);
+    if (lane == 63 && n < a.N) {
 #pragma unroll
         for (int m = 0; m < MR; ++m)
-            if (m < M) a.out[(int64_t)m * a.N + n] = to_bf16(a.alpha * acc[m]);
+            if (m < a.M) a.out[(int64_t)m * a.N + n] = to_bf16(a.alpha * acc[m]);
     }
 }
-
 
 }  // namespace
 
@@ -1233,10 +1246,21 @@ hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.Np / 4));
-    if (a.M <= 1) hipLaunchKernelGGL(gemv_kernel<1>, grid, dim3(256), 0, stream, a);
-    else if (a.M <= 2) hipLaunchKernelGGL(gemv_kernel<2>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(gemv_kernel<4>, grid, dim3(256), 0, stream, a);
+    // Np is a multiple of 16, so whole workgroups cover it.  One batch of
+    // loads covers K up to 8192 (256 half-panels); a shorter K takes as
+    // few half-panels per lane as it needs.
+    const dim3 grid((unsigned)(a.Np / kGemvWaves)), block(64 * kGemvWaves);
+    const int hpl = (int)std::min<int64_t>(4, (2 * (int64_t)a.P + 63) / 64);
+    const int mr = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
+    switch (mr * 8 + hpl) {
+#define NVFP4_GEMV_CASE(MR, HPL) \
+        case MR * 8 + HPL: hipLaunchKernelGGL((gemv_kernel<MR, HPL>), grid, block, 0, stream, a); break;
+        NVFP4_GEMV_CASE(1, 1) NVFP4_GEMV_CASE(1, 2) NVFP4_GEMV_CASE(1, 3) NVFP4_GEMV_CASE(1, 4)
+        NVFP4_GEMV_CASE(2, 1) NVFP4_GEMV_CASE(2, 2) NVFP4_GEMV_CASE(2, 3) NVFP4_GEMV_CASE(2, 4)
+        NVFP4_GEMV_CASE(4, 1) NVFP4_GEMV_CASE(4, 2) NVFP4_GEMV_CASE(4, 3) NVFP4_GEMV_CASE(4, 4)
+#undef NVFP4_GEMV_CASE
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

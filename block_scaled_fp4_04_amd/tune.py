@@ -132,6 +132,8 @@ def tune_shape(M, N, K, device, stream, log) -> dict:
         f"{times[heur]:.2f} us; chosen {nv.PATH_NAMES[best[0]]}/{best[1]}/{best[2]} "
         f"{times[best]:.2f} us ({flops / times[best] / 1e6:.1f} TFLOPS, "
         f"{len(times)} plans timed)")
+    log("    " + ", ".join(f"{nv.PATH_NAMES[c[0]]}/{c[1]}/{c[2]} {t:.2f}"
+                          for c, t in sorted(times.items(), key=lambda kv: kv[1])))
     del a, b, out
     return {"M": M, "N": N, "K": K, "path": nv.PATH_NAMES[best[0]], "tile": best[1],
             "split_k": best[2], "us": round(times[best], 3),
