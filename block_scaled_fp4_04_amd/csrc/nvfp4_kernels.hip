@@ -674,7 +674,7 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 // (g % 2) of panel (g / 2): one 16-byte load of codes and one 2-byte load of
 // scales per operand block, straight from HBM (B is used once, so it does
 // not pass through LDS).  Each MFMA sub-step s takes word s of every lane.
-// Lanes whose A row is at or beyond M skip their A loads (zeros).
+// Rows of A at or beyond M come from the packed operand's zero padding.
 //
 // Grid: (N / 16 row groups) x split_k workgroups of WAVES waves; a
 // workgroup owns one row group and a contiguous range of work units, dealt
@@ -683,9 +683,8 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 // are added in LDS in wave order; with split_k > 1 the workgroup partials
 // are added by the last arrival in split order (deterministic).
 // ---------------------------------------------------------------------------
-template <int WAVES, int MB>
+template <int WAVES, int MB, int UNITS>
 __global__ void __launch_bounds__(WAVES * 64) skinny_kernel(GemmArgs a) {
-    constexpr int UNITS = MB <= 2 ? 4 : 2;   // (registers: 128 VGPRs at 16 waves)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -704,39 +703,39 @@ __global__ void __launch_bounds__(WAVES * 64) skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int b = 0; b < MB; ++b) acc[b] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
     for (int base = c0 + wave; base < c1; base += WAVES * UNITS) {
+        // The loads are unconditional: a unit past the range re-reads the
+        // range's last unit and both its operands get zero scales, so it
+        // adds exact zeros (never a NaN of the re-read scales),
+        // and rows of A past M are the packed operand's zero padding (they
+        // only feed rows of C that are not stored).  The compiler can then
+        // wait for each unit's loads alone and decode it while the later
+        // units arrive.
         uint4 bw[UNITS], aw[UNITS][MB];
         uint32_t bs[UNITS], as[UNITS][MB];
 #pragma unroll
         for (int u = 0; u < UNITS; ++u) {
-            const int c = base + WAVES * u;
+            const int c = min(base + WAVES * u, c1 - 1);
             const int panel = 2 * c + pl;
-            bw[u] = uint4{0u, 0u, 0u, 0u};
-            bs[u] = 0u;
+            const int64_t bo = (int64_t)panel * a.Np + nrow;
+            bw[u] = *reinterpret_cast<const uint4*>(a.b_codes + bo * 32 + half * 16);
+            bs[u] = *reinterpret_cast<const uint16_t*>(a.b_scales + bo * 4 + half * 2);
 #pragma unroll
             for (int b = 0; b < MB; ++b) {
-                aw[u][b] = uint4{0u, 0u, 0u, 0u};
-                as[u][b] = 0u;
-            }
-            if (c < c1 && panel < a.P) {
-                const int64_t bo = (int64_t)panel * a.Np + nrow;
-                bw[u] = *reinterpret_cast<const uint4*>(a.b_codes + bo * 32 + half * 16);
-                bs[u] = *reinterpret_cast<const uint16_t*>(a.b_scales + bo * 4 + half * 2);
-#pragma unroll
-                for (int b = 0; b < MB; ++b) {
-                    if (16 * b + r16 < a.M) {
-                        const int64_t ao = (int64_t)panel * a.Mp + 16 * b + r16;
-                        aw[u][b] = *reinterpret_cast<const uint4*>(a.a_codes + ao * 32 + half * 16);
-                        as[u][b] = *reinterpret_cast<const uint16_t*>(a.a_scales + ao * 4 + half * 2);
-                    }
-                }
+                const int64_t ao = (int64_t)panel * a.Mp + 16 * b + r16;
+                aw[u][b] = *reinterpret_cast<const uint4*>(a.a_codes + ao * 32 + half * 16);
+                as[u][b] = *reinterpret_cast<const uint16_t*>(a.a_scales + ao * 4 + half * 2);
             }
         }
+        // (keeps every load ahead of the first unit's decode: the scheduler
+        // would otherwise hold back later units' loads to save registers)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < UNITS; ++u) {
-            const h2 sbh = e4m3x2_lo(bs[u]);
+            const bool live = base + WAVES * u < c1;   // (wave-uniform)
+            const h2 sbh = e4m3x2_lo(live ? bs[u] : 0u);
             h2 sah[MB];
 #pragma unroll
-            for (int b = 0; b < MB; ++b) sah[b] = e4m3x2_lo(as[u][b]);
+            for (int b = 0; b < MB; ++b) sah[b] = e4m3x2_lo(live ? as[u][b] : 0u);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const h8 bv = decode8(word_of(bw[u], s), scale_of(sbh, s));
@@ -757,9 +756,12 @@ __global__ void __launch_bounds__(WAVES * 64) skinny_kernel(GemmArgs a) {
     // wave stays until the split-K hand-off is decided (barriers below)
     const int blk = wave < MB ? wave : 0;
     const bool reducer = wave < MB;
-    f4v sum = red[0][blk][lane];
+    f4v part[WAVES];  // all reads issued before the first add
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[w][blk][lane];
+    for (int w = 0; w < WAVES; ++w) part[w] = red[w][blk][lane];
+    f4v sum = part[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += part[w];
 
     if (S > 1) {
         float* mine = a.partials + (((int64_t)g * S + z) * MB + blk) * 256;
@@ -856,26 +858,23 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
         uint4 ca[MI], cb[NI];
         uint32_t sa[MI], sb[NI];
     };
-    auto load = [&](int k, Regs& r) {  // k-th panel of this wave
-        if (k < count) {
-            const int64_t panel = p0 + wave + (int64_t)k * WAVES;
+    // k-th panel of this wave.  Unconditional (count > 0): past the wave's
+    // last panel it reads that panel again, and compute() then gives the
+    // slot zero scales, so the compiler's wait counts stay exact (a branch
+    // around the loads made every ring slot wait for all of them).
+    auto load = [&](int k, Regs& r) {
+        const int64_t panel = p0 + wave + (int64_t)min(k, count - 1) * WAVES;
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int64_t row = panel * a.Mp + a_off[i];
-                r.ca[i] = *reinterpret_cast<const uint4*>(a.a_codes + row * 32 + h * 16);
-                r.sa[i] = *reinterpret_cast<const uint16_t*>(a.a_scales + row * 4 + h * 2);
-            }
+        for (int i = 0; i < MI; ++i) {
+            const int64_t row = panel * a.Mp + a_off[i];
+            r.ca[i] = *reinterpret_cast<const uint4*>(a.a_codes + row * 32 + h * 16);
+            r.sa[i] = *reinterpret_cast<const uint16_t*>(a.a_scales + row * 4 + h * 2);
+        }
 #pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int64_t row = panel * a.Np + b_off[j];
-                r.cb[j] = *reinterpret_cast<const uint4*>(a.b_codes + row * 32 + h * 16);
-                r.sb[j] = *reinterpret_cast<const uint16_t*>(a.b_scales + row * 4 + h * 2);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < MI; ++i) { r.ca[i] = uint4{0u, 0u, 0u, 0u}; r.sa[i] = 0u; }
-#pragma unroll
-            for (int j = 0; j < NI; ++j) { r.cb[j] = uint4{0u, 0u, 0u, 0u}; r.sb[j] = 0u; }
+        for (int j = 0; j < NI; ++j) {
+            const int64_t row = panel * a.Np + b_off[j];
+            r.cb[j] = *reinterpret_cast<const uint4*>(a.b_codes + row * 32 + h * 16);
+            r.sb[j] = *reinterpret_cast<const uint16_t*>(a.b_scales + row * 4 + h * 2);
         }
     };
 
@@ -887,12 +886,12 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    auto compute = [&](const Regs& r) {
+    auto compute = [&](const Regs& r, bool live) {  // live: a panel of the wave (wave-uniform)
         h2 sa[MI], sb[NI];
 #pragma unroll
-        for (int i = 0; i < MI; ++i) sa[i] = e4m3x2_lo(r.sa[i]);
+        for (int i = 0; i < MI; ++i) sa[i] = e4m3x2_lo(live ? r.sa[i] : 0u);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) sb[j] = e4m3x2_lo(r.sb[j]);
+        for (int j = 0; j < NI; ++j) sb[j] = e4m3x2_lo(live ? r.sb[j] : 0u);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             h8 av[MI], bv[NI];
@@ -908,14 +907,34 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
         }
     };
 
-    Regs ring[DEPTH];
+    if (count > 0) {
+        Regs ring[DEPTH];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load(d, ring[d]);
-    for (int k = 0; k < count; k += DEPTH) {
+        for (int d = 0; d < DEPTH; ++d) load(d, ring[d]);
+        // The first panels are taken as they arrive, here; otherwise the
+        // compiler merges these loads with the loop's own (same form, other
+        // index) into one load at the top of each iteration, which waits
+        // for the panel it just asked for instead of one issued a step ahead.
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-            compute(ring[d]);            // panel k + d (zeros past the end)
-            load(k + d + DEPTH, ring[d]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                asm volatile("" : "+v"(ring[d].ca[i].x), "+v"(ring[d].ca[i].y), "+v"(ring[d].ca[i].z),
+                                  "+v"(ring[d].ca[i].w), "+v"(ring[d].sa[i]));
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                asm volatile("" : "+v"(ring[d].cb[j].x), "+v"(ring[d].cb[j].y), "+v"(ring[d].cb[j].z),
+                                  "+v"(ring[d].cb[j].w), "+v"(ring[d].sb[j]));
+        }
+        for (int k = 0; k < count; k += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                compute(ring[d], k + d < count);  // panel k + d (zeros past the end)
+                load(k + d + DEPTH, ring[d]);
+                // (each slot's loads go out right after its MFMAs, not
+                // after the next slot's: the scheduler would sink them)
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
@@ -1267,10 +1286,23 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.Np / 16) * a.split_k));
     const dim3 block(kSkinnyWaves * 64);
-    if (a.M <= 16) hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, 1>), grid, block, 0, stream, a);
-    else if (a.M <= 32) hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, 2>), grid, block, 0, stream, a);
-    else if (a.M <= 48) hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, 3>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, 4>), grid, block, 0, stream, a);
+    const int mb = (a.M + 15) / 16;
+    // Work units in flight per wave: as many as a wave's share of its split
+    // needs, at most 4 (2 with more than two row blocks: 128 VGPRs at 16
+    // waves), so that no unit is loaded and decoded only to be discarded.
+    const int per_split = (a.P / 2 + a.split_k - 1) / a.split_k;
+    const int need = (per_split + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int units = std::max(1, std::min(need, mb <= 2 ? 4 : 2));
+    switch (mb * 8 + units) {
+#define NVFP4_SKINNY_CASE(MB, U) \
+        case MB * 8 + U: hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, MB, U>), grid, block, 0, stream, a); break;
+        NVFP4_SKINNY_CASE(1, 1) NVFP4_SKINNY_CASE(1, 2) NVFP4_SKINNY_CASE(1, 3) NVFP4_SKINNY_CASE(1, 4)
+        NVFP4_SKINNY_CASE(2, 1) NVFP4_SKINNY_CASE(2, 2) NVFP4_SKINNY_CASE(2, 3) NVFP4_SKINNY_CASE(2, 4)
+        NVFP4_SKINNY_CASE(3, 1) NVFP4_SKINNY_CASE(3, 2)
+        NVFP4_SKINNY_CASE(4, 1) NVFP4_SKINNY_CASE(4, 2)
+#undef NVFP4_SKINNY_CASE
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -412,7 +412,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int path, int tile, int split_req
         // Measured on an MI355X over M = 1..16384 for N x K = 256 .. 8192 x
         // 6144 .. 8192 (device time per call):
         //  * the dot-product kernel wins only while the whole output is at
-        //    most 4096 elements of at most four rows; beyond that the skinny
+        //    most 2048 elements of one or two rows; beyond that the skinny
         //    kernel's 16-row MFMA blocks are faster, up to 64 rows while
         //    N <= 2048 (one workgroup per CU and 16 columns: more columns
         //    than that make more than one round);
@@ -423,7 +423,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int path, int tile, int split_req
         //    tiles once those alone give 3/4 of a workgroup per CU.
         const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-        if (M <= 4 && M * N <= 4096) {
+        if (M <= 2 && M * N <= 2048) {
             path = NVFP4_PATH_GEMV;
         } else if (M <= 16 || (M <= 64 && N <= 2048)) {
             path = NVFP4_PATH_SKINNY;

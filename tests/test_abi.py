@@ -166,16 +166,13 @@ def test_plan(no_table):
     def key(M, N, K):
         p = nv.plan(M, N, K)
         return nv.PATH_NAMES[p["path"]], p["tile_m"], p["split_k"]
-    # dot products only for at most 4096 outputs of at most four rows
+    # dot products only for at most 2048 outputs of one or two rows
     assert key(1, 768, 6144)[0] == "gemv"
     assert key(1, 2048, 6144)[0] == "gemv"
     assert key(2, 768, 6144)[0] == "gemv"
-    assert key(2, 2048, 6144)[0] == "gemv"
-    assert key(4, 256, 6144)[0] == "gemv"
-    assert key(4, 768, 6144)[0] == "gemv"
     assert key(1, 6144, 6144)[0] == "skinny"
-    assert key(4, 2048, 6144)[0] == "skinny"
-    assert key(5, 256, 6144)[0] == "skinny"
+    assert key(2, 2048, 6144)[0] == "skinny"
+    assert key(4, 256, 6144)[0] == "skinny"
     assert key(16, 256, 6144)[0] == "skinny"
     # 256 x 256 tiles once they give 3/4 of a workgroup per CU
     assert key(16384, 8192, 8192) == ("tile", 256, 1)
