@@ -13,6 +13,7 @@ constexpr int kPanelCodeBytes = 32;  // bytes of codes per row per panel
 constexpr int kPanelScaleBytes = 4;  // scale bytes per row per panel
 constexpr int kRowPad = 16;
 constexpr int kSkinnyWaves = 16;    // waves per workgroup of the skinny kernel
+constexpr int kCUs = 256;           // compute units of an MI355X (plans and grid sizes)
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // Number of 64-element panels of a packed operand (always even).

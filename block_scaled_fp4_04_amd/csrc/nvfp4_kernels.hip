@@ -1052,10 +1052,12 @@ __device__ __forceinline__ float wave_sum_lane63(float x) {
     return x;
 }
 
-// Waves (rows of B) per workgroup.  Measured against 1 and 2 waves with
-// K = 6144-8192: 4 is the fastest from N = 768 up (1.3-1.7x faster than 1
-// wave at N = 6144-8192, and faster with operands beyond the last-level
-// cache); 1 or 2 waves win only at N = 256 (2.2-2.4 against 2.7 us).
+// Waves (rows of B) per workgroup.  4 consecutive rows share every 128-byte
+// line of a packed panel (32 bytes each), so a workgroup of 4 waves reads
+// whole lines.  Fewer waves per workgroup (more workgroups for small N)
+// measured faster warm at N = 256 (2.4 against 2.7 us) but split lines
+// between workgroups on different XCDs, each fetching them from HBM: with
+// the operands beyond the last-level cache 1 x 768 x 6144 went 3.8 -> 4.7 us.
 constexpr int kGemvWaves = 4;
 
 template <int MR, int HPL>

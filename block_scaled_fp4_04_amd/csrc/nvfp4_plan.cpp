@@ -33,7 +33,6 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int kCUs = 256;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
 // ---- tuned table --------------------------------------------------------------
