@@ -1052,18 +1052,28 @@ __device__ __forceinline__ float wave_sum_lane63(float x) {
     return x;
 }
 
-// Waves (rows of B) per workgroup.  4 consecutive rows share every 128-byte
-// line of a packed panel (32 bytes each), so a workgroup of 4 waves reads
-// whole lines.  Fewer waves per workgroup (more workgroups for small N)
-// measured faster warm at N = 256 (2.4 against 2.7 us) but split lines
-// between workgroups on different XCDs, each fetching them from HBM: with
-// the operands beyond the last-level cache 1 x 768 x 6144 went 3.8 -> 4.7 us.
+// Four waves (rows of B) per workgroup: 4 consecutive rows share every
+// 128-byte line of a packed panel (32 bytes each), so each workgroup reads
+// whole lines.  Workgroups are dealt to the 8 XCDs in turn; the workgroup
+// index is remapped to give each XCD a contiguous range of rows, so that
+// neighbouring workgroups share their XCD's L2 (1 x 768 x 6144: 2.84 ->
+// 2.65 us warm, 3.80 -> 3.60 us with the operands beyond the last-level
+// cache, and the HBM fetches fell from 1.85x to 1.07x of the algorithmic
+// bytes).  Fewer waves per workgroup for small N (more workgroups) was
+// faster on some boxes and up to 12% slower on others with the operands
+// beyond the last-level cache, where a line is then split between
+// workgroups.
 constexpr int kGemvWaves = 4;
 
 template <int MR, int HPL>
 __global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(GemmArgs a) {
     const int lane = threadIdx.x & 63;
-    const int n = blockIdx.x * kGemvWaves + (threadIdx.x >> 6);  // B row (< Np)
+    // XCD x = blockIdx % 8 takes ranks [x q + min(x, r), ...) of the
+    // total = 8 q + r workgroups, one after the other (a bijection).
+    const int total = gridDim.x, q8 = total >> 3, r8 = total & 7;
+    const int x = blockIdx.x & 7;
+    const int bid = x * q8 + min(x, r8) + (int)(blockIdx.x >> 3);
+    const int n = bid * kGemvWaves + (threadIdx.x >> 6);  // B row (< Np: the grid is Np / 4)
     const int hp_total = a.P * 2;               // 32-element half-panels along K
 
     float acc[MR];
