@@ -151,3 +151,40 @@ def test_tail_split_launch(o, M, N, K, tail, split):
     gf = orc.bf16_bits_to_float(g)
     assert np.all(np.isfinite(gf)) and np.count_nonzero(g & 0x7FFF) > 0.99 * g.size
 
+
+
+@pytest.mark.parametrize("M,K", [(5, 6144), (16, 6160), (16, 8192), (32, 6144), (48, 6144), (64, 8192)])
+def test_skinny_units_in_flight(o, M, K):
+    """The skinny kernel at the K lengths that give each wave 3 or 4 units of
+    loads in flight, including units past the end of the range (re-read with
+    zero scales: K = 6160 gives 49 units over 16 waves) and two row blocks,
+    whose 3 units' worth runs as 4 with one discarded."""
+    ops = synth.random_operands(4500 + M + K, M, 72, K, alpha=0.75)
+    say(f"skinny units: {ops.M}x{ops.N}x{ops.K}")
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    out = nv.gemm(a, b, ops.alpha, path=nv.PATH_SKINNY, split_k=1)
+    torch.cuda.synchronize()
+    g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
+    bits, exact, mag = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha)
+    r = compare(g, bits, exact, mag, ops.alpha)
+    say(f"  {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 40, 2048), (2, 56, 4096), (3, 104, 6144), (1, 8, 6160)])
+def test_gemv_half_panels_per_lane(o, M, N, K):
+    """The dot-product kernel with 1, 2 and 3 half-panels per lane (K up to
+    6144), grids that are not a multiple of the 8 XCDs (row remap), and a
+    last half-panel shared by a few lanes only (K = 6160)."""
+    ops = synth.random_operands(4600 + M + N + K, M, N, K, alpha=-0.5)
+    say(f"gemv half-panels: {ops.M}x{ops.N}x{ops.K}")
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    out = nv.gemm(a, b, ops.alpha, path=nv.PATH_GEMV)
+    torch.cuda.synchronize()
+    g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
+    bits, exact, mag = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha)
+    r = compare(g, bits, exact, mag, ops.alpha)
+    say(f"  {r}")
+    assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
