@@ -141,6 +141,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // around them nor inserts its own conservative wait for every LDS read; the
 // kernel waits for them explicitly with wait_vmcnt and orders LDS reuse with
 // barriers.
+// M0 is a reserved register to the compiler (hence its warning for the
+// clobber); it never allocates it, and these kernels contain no instruction
+// that reads it other than these loads, each of which sets it first.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                       uint32_t lds) {
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
@@ -151,6 +156,7 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
                  :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 // Workgroup barrier that is also a compiler barrier for memory operations
 // (it adds no wait for outstanding loads: those are waited for explicitly).
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
