@@ -432,6 +432,74 @@ def decode_sequence_line(nv, torch, steps, warmup):
         "speedup": eager_us / seq_us, "path": "sequence (one HIP graph launch per step)"}
 
 
+def floors_line(nv, torch, steps):
+    """The floors under the decode-sized calls, measured on this GPU: the
+    per-call time of an empty kernel with the headline's launch shape (768/4
+    workgroups of 256 work-items) in a graph replay, timed like the GEMMs,
+    and the latency of one dependent load when the data sit in one XCD's L2,
+    in the last-level cache, or only in HBM (one work-item walking a random
+    single cycle through 1 MiB, 64 MiB or 1 GiB)."""
+    stream = torch.cuda.Stream()
+    blocks, threads = 768 // 4, 256
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            nv.probe_empty(blocks, threads, stream=stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        cap = torch.cuda.current_stream()
+        for _ in range(steps):
+            nv.probe_empty(blocks, threads, stream=cap)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        start.record(stream)
+        g.replay()
+        stop.record(stream)
+    torch.cuda.synchronize()
+    empty_us = start.elapsed_time(stop) * 1000.0 / steps
+    del g
+    lat = {}
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # HBM first, on a buffer no load has touched (4x the last-level cache);
+    # then 64 MiB after one read of it (the last-level cache holds it); then
+    # 1 MiB after one full walk on the same single work-item (its XCD's L2
+    # holds it).  Every walk starts at index 0 and its last index is checked
+    # against the same walk on the host.
+    for name, size, walk in (("hbm_1GiB", 1 << 30, 5000), ("last_level_64MiB", 64 << 20, 5000),
+                             ("l2_1MiB", 1 << 20, 5000)):
+        n = size // 4
+        perm = torch.randperm(n, device="cuda")
+        nxt = torch.empty(n, dtype=torch.int32, device="cuda")
+        nxt[perm] = torch.roll(perm, -1).to(torch.int32)   # one cycle through all n entries
+        del perm
+        host = nxt.cpu().numpy()
+        i = 0
+        for _ in range(walk):
+            i = int(host[i])
+        del host
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            if name.startswith("l2"):
+                nv.probe_chase(nxt, n, out, stream=stream)   # one full pass, back to index 0
+            elif name.startswith("last_level"):
+                nxt.sum()
+            start.record(stream)
+            nv.probe_chase(nxt, walk, out, stream=stream)
+            stop.record(stream)
+        torch.cuda.synchronize()
+        if int(out.item()) != i:
+            raise RuntimeError(f"pointer chase over {name} ended at {int(out.item())}, expected {i}")
+        lat[name] = start.elapsed_time(stop) * 1e6 / walk
+        del nxt
+        torch.cuda.empty_cache()
+    return {"empty_kernel_us_per_call": empty_us,
+            "empty_kernel_launch": f"{blocks} workgroups of {threads} work-items, graph replay of {steps}",
+            "load_latency_ns": lat,
+            "load_latency_how": "one work-item, dependent loads along a random cycle"}
+
+
 def cpu_baseline(cfg, ops, budget_s):
     from oracle import oracle as orc
     o = orc.load()
@@ -547,6 +615,8 @@ def main():
                            "split_k": cr["plan"]["split_k"],
                            "pages_tflops_other_gpu": PAGES_TFLOPS.get(c.index)}
         line["per_shape"] = per
+        torch.cuda.empty_cache()
+        line["floors"] = floors_line(nv, torch, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, ops, args.cpu_seconds)
     print(json.dumps(line), flush=True)

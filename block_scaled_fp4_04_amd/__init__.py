@@ -54,7 +54,7 @@ EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_p
            "nvfp4_plan_table_clear", "nvfp4_build_id", "nvfp4_grouped_gemm", "nvfp4_quantize",
            "nvfp4_sequence_create", "nvfp4_sequence_add_gemm", "nvfp4_sequence_add_grouped_gemm",
            "nvfp4_sequence_add_quantize", "nvfp4_sequence_finalize", "nvfp4_sequence_launch",
-           "nvfp4_sequence_destroy"]
+           "nvfp4_sequence_destroy", "nvfp4_probe_empty", "nvfp4_probe_chase"]
 
 
 class _PlanT(ctypes.Structure):
@@ -103,6 +103,10 @@ def lib() -> ctypes.CDLL:
                                            _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
         L.nvfp4_quantize.restype = ctypes.c_int
         L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
+        L.nvfp4_probe_empty.restype = ctypes.c_int
+        L.nvfp4_probe_empty.argtypes = [_i64, _i64, _vp]
+        L.nvfp4_probe_chase.restype = ctypes.c_int
+        L.nvfp4_probe_chase.argtypes = [_vp, _i64, _i64, _vp, _vp]
         L.nvfp4_grouped_gemm.restype = ctypes.c_int
         L.nvfp4_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float, _vp, _i64,
                                          _i64, _i64, _vp]
@@ -397,6 +401,25 @@ def quantize(x, out: PackedOperand | None = None, stream=None) -> PackedOperand:
     if st:
         raise Nvfp4Error(st, f"nvfp4_quantize(rows={rows}, K={K}, ld={x.stride(0)})")
     return out
+
+
+def probe_empty(blocks: int, threads: int, stream=None) -> None:
+    """Enqueue an empty kernel (nvfp4_probe_empty): a measurement aid for
+    the per-call floor of a launch."""
+    st = lib().nvfp4_probe_empty(blocks, threads, _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_probe_empty(blocks={blocks}, threads={threads})")
+
+
+def probe_chase(next_idx, steps: int, out, stream=None) -> None:
+    """One work-item follows ``next_idx`` (a device int32/uint32 tensor of a
+    power-of-two length holding indices) for ``steps`` dependent loads and
+    writes the last index to ``out`` (nvfp4_probe_chase): a measurement aid
+    for the load latency of the cache level the array fits in."""
+    st = lib().nvfp4_probe_chase(next_idx.data_ptr(), next_idx.numel(), steps, out.data_ptr(),
+                                 _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_probe_chase(n={next_idx.numel()}, steps={steps})")
 
 
 class Sequence:

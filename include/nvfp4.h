@@ -301,6 +301,25 @@ int nvfp4_sequence_finalize(nvfp4_sequence_t seq);
 int nvfp4_sequence_launch(nvfp4_sequence_t seq, void* stream);
 int nvfp4_sequence_destroy(nvfp4_sequence_t seq);
 
+/* ---- measurement aids (not part of the GEMM path) ------------------------
+ * The floors that bound decode-sized calls: what a kernel that does nothing
+ * costs per call, and the latency of a dependent load.
+ *
+ * nvfp4_probe_empty: enqueues an empty kernel of `blocks` workgroups of
+ *   `threads` work-items (1..1024) on `stream`.
+ * nvfp4_probe_chase: one work-item follows next[] from index 0 for `steps`
+ *   dependent loads and writes the last index to *out.  next (device,
+ *   caller-owned) holds n uint32 indices; n must be a power of two (up to
+ *   2^32): each index is masked by n - 1, so no content of next[] can make a
+ *   load leave the array.  A random single cycle through next[] of a chosen
+ *   size measures the load latency of the cache level it fits in.
+ * Both: NVFP4_ERR_INVALID_VALUE for arguments out of range or null pointers
+ * (checked on the host, nothing enqueued), NVFP4_ERR_HIP if the launch
+ * fails; asynchronous on `stream`. */
+int nvfp4_probe_empty(int64_t blocks, int64_t threads, void* stream);
+int nvfp4_probe_chase(const uint32_t* next, int64_t n, int64_t steps, uint32_t* out,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -233,3 +233,20 @@ def test_sequence_state_and_validation():
     assert lib.nvfp4_sequence_add_gemm(None, 0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4,
                                        64) == nv.ERR_INVALID_VALUE
 
+
+
+def test_probe_arguments_are_checked_before_launch():
+    """The measurement aids refuse out-of-range arguments on the host (no
+    launch happens, so this runs without a GPU)."""
+    L = nv.lib()
+    assert L.nvfp4_probe_empty(0, 64, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_empty(1, 0, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_empty(1, 1025, None) == nv.ERR_INVALID_VALUE
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.addressof(buf)
+    assert L.nvfp4_probe_chase(None, 16, 1, p, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_chase(p, 16, 1, None, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_chase(p, 12, 1, p, None) == nv.ERR_INVALID_VALUE   # not a power of two
+    assert L.nvfp4_probe_chase(p, 0, 1, p, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_chase(p, 16, -1, p, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_chase(p, (1 << 32) + 2, 1, p, None) == nv.ERR_INVALID_VALUE
