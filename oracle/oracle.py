@@ -32,10 +32,12 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 _i64 = ctypes.c_int64
 
 
-def build(out_path: str = LIB_PATH, mutant: int = 0) -> str:
+def build(out_path: str = LIB_PATH, mutant: int = 0, extra_flags: tuple[str, ...] = ()) -> str:
     """Compile the oracle with gcc (OpenMP, -O2).  ``mutant`` != 0 plants one
-    deliberate mistake (see the ORACLE_MUTANT cases in the C source)."""
-    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", _SRC, "-o", out_path, "-lm"]
+    deliberate mistake (see the ORACLE_MUTANT cases in the C source);
+    ``extra_flags`` go to gcc as given (for instance sanitizers)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", *extra_flags, _SRC, "-o",
+           out_path, "-lm"]
     if mutant:
         cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
     tmp = out_path + f".tmp{os.getpid()}"
