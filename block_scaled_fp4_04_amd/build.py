@@ -24,6 +24,10 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep the compiler from emitting packed-FP32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernels with plain arguments get the leading ones preloaded into scalar
+    # registers before their waves start (the decode-sized kernels: one
+    # memory round trip less per call)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -687,16 +687,21 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
 // to 64 per lane, so two 16-wave workgroups share a CU and one's memory
 // latency hides under the other's decode work: 16 x 6144 x 6144 7.8 -> 7.0
 // us, 16 x 16384 x 6144 19.1 -> 14.8 us (4 units would spill at that size).
+// (Plain arguments, operands and geometry first, so that those can be
+// preloaded into scalar registers before the waves start.)
 template <int WAVES, int MB, int UNITS>
 __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVES / 4 : 1)
-    skinny_kernel(GemmArgs a) {
+    skinny_kernel(const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
+                  const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+                  int Np, int Mp, int P, int split_k, uint16_t* __restrict__ out,
+                  float* partials, uint32_t* counters, float alpha, int M, int N) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int S = a.split_k;
+    const int S = split_k;
     const int g = blockIdx.x / S;
     const int z = blockIdx.x % S;
-    const int C = a.P / 2;
+    const int C = P / 2;
     const int c0 = (int)((int64_t)z * C / S);
     const int c1 = (int)((int64_t)(z + 1) * C / S);
     const int r16 = lane & 15;
@@ -721,14 +726,14 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
         for (int u = 0; u < UNITS; ++u) {
             const int c = min(base + WAVES * u, c1 - 1);
             const int panel = 2 * c + pl;
-            const int64_t bo = (int64_t)panel * a.Np + nrow;
-            bw[u] = *reinterpret_cast<const uint4*>(a.b_codes + bo * 32 + half * 16);
-            bs[u] = *reinterpret_cast<const uint16_t*>(a.b_scales + bo * 4 + half * 2);
+            const int64_t bo = (int64_t)panel * Np + nrow;
+            bw[u] = *reinterpret_cast<const uint4*>(b_codes + bo * 32 + half * 16);
+            bs[u] = *reinterpret_cast<const uint16_t*>(b_scales + bo * 4 + half * 2);
 #pragma unroll
             for (int b = 0; b < MB; ++b) {
-                const int64_t ao = (int64_t)panel * a.Mp + 16 * b + r16;
-                aw[u][b] = *reinterpret_cast<const uint4*>(a.a_codes + ao * 32 + half * 16);
-                as[u][b] = *reinterpret_cast<const uint16_t*>(a.a_scales + ao * 4 + half * 2);
+                const int64_t ao = (int64_t)panel * Mp + 16 * b + r16;
+                aw[u][b] = *reinterpret_cast<const uint4*>(a_codes + ao * 32 + half * 16);
+                as[u][b] = *reinterpret_cast<const uint16_t*>(a_scales + ao * 4 + half * 2);
             }
         }
         // (keeps every load ahead of the first unit's decode: the scheduler
@@ -769,7 +774,7 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
     for (int w = 1; w < WAVES; ++w) sum += part[w];
 
     if (S > 1) {
-        float* mine = a.partials + (((int64_t)g * S + z) * MB + blk) * 256;
+        float* mine = partials + (((int64_t)g * S + z) * MB + blk) * 256;
         if (reducer) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) publish(mine + v * 64 + lane, sum[v]);
@@ -778,14 +783,14 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
         __shared__ uint32_t s_old;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0) s_old = arrive(a.counters + g);
+        if (tid == 0) s_old = arrive(counters + g);
         __syncthreads();
         if (s_old != (uint32_t)(S - 1)) return;       // (uniform in the workgroup)
-        if (tid == 0) reset_counter(a.counters + g);  // all splits arrived
+        if (tid == 0) reset_counter(counters + g);  // all splits arrived
         if (!reducer) return;
         f4v t = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int zz = 0; zz < S; ++zz) {
-            const float* pz = a.partials + (((int64_t)g * S + zz) * MB + blk) * 256;
+            const float* pz = partials + (((int64_t)g * S + zz) * MB + blk) * 256;
             f4v p;
 #pragma unroll
             for (int v = 0; v < 4; ++v) p[v] = fetch(pz + v * 64 + lane);
@@ -797,11 +802,11 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
 
     // 16x16 MFMA result layout: lane l holds column l % 16, rows 4 * (l / 16) + v.
     const int col = g * 16 + r16;
-    if (col < a.N) {
+    if (col < N) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int row = 16 * blk + 4 * grp + v;
-            if (row < a.M) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * sum[v]);
+            if (row < M) out[(int64_t)row * N + col] = to_bf16(alpha * sum[v]);
         }
     }
 }
@@ -1070,16 +1075,23 @@ __device__ __forceinline__ float wave_sum_lane63(float x) {
 // workgroups.
 constexpr int kGemvWaves = 4;
 
+// Plain arguments rather than the launch structure, in the order the kernel
+// needs them (the operands and their geometry first): the leading ones can
+// then be preloaded into scalar registers before the waves start, instead
+// of being fetched from memory after.
 template <int MR, int HPL>
-__global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(GemmArgs a) {
+__global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int Np, int Mp,
+    int P, int total, uint16_t* __restrict__ out, float alpha, int M, int N) {
     const int lane = threadIdx.x & 63;
     // XCD x = blockIdx % 8 takes ranks [x q + min(x, r), ...) of the
-    // total = 8 q + r workgroups, one after the other (a bijection).
-    const int total = gridDim.x, q8 = total >> 3, r8 = total & 7;
+    // total = 8 q + r workgroups (the grid), one after the other (a bijection).
+    const int q8 = total >> 3, r8 = total & 7;
     const int x = blockIdx.x & 7;
     const int bid = x * q8 + min(x, r8) + (int)(blockIdx.x >> 3);
     const int n = bid * kGemvWaves + (threadIdx.x >> 6);  // B row (< Np: the grid is Np / 4)
-    const int hp_total = a.P * 2;               // 32-element half-panels along K
+    const int hp_total = P * 2;               // 32-element half-panels along K
 
     float acc[MR];
 #pragma unroll
@@ -1097,15 +1109,15 @@ __global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(GemmArgs a) {
             const int hp = min(base + lane + 64 * i, hp_total - 1);
             const int64_t panel = hp >> 1;
             const int half = hp & 1;
-            const int64_t brow = panel * a.Np + n;
-            bw[i] = *reinterpret_cast<const uint4*>(a.b_codes + brow * 32 + half * 16);
-            bsc[i] = *reinterpret_cast<const uint16_t*>(a.b_scales + brow * 4 + half * 2);
+            const int64_t brow = panel * Np + n;
+            bw[i] = *reinterpret_cast<const uint4*>(b_codes + brow * 32 + half * 16);
+            bsc[i] = *reinterpret_cast<const uint16_t*>(b_scales + brow * 4 + half * 2);
             // rows MR-1 < 16 <= Mp: padding rows of A are zeros in memory
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
-                const int64_t arow = panel * a.Mp + m;
-                aw[i][m] = *reinterpret_cast<const uint4*>(a.a_codes + arow * 32 + half * 16);
-                asc[i][m] = *reinterpret_cast<const uint16_t*>(a.a_scales + arow * 4 + half * 2);
+                const int64_t arow = panel * Mp + m;
+                aw[i][m] = *reinterpret_cast<const uint4*>(a_codes + arow * 32 + half * 16);
+                asc[i][m] = *reinterpret_cast<const uint16_t*>(a_scales + arow * 4 + half * 2);
             }
         }
 #pragma unroll
@@ -1145,10 +1157,10 @@ __global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[m] = wave_sum_lane63(acc[m]);
-    if (lane == 63 && n < a.N) {
+    if (lane == 63 && n < N) {
 #pragma unroll
         for (int m = 0; m < MR; ++m)
-            if (m < a.M) a.out[(int64_t)m * a.N + n] = to_bf16(a.alpha * acc[m]);
+            if (m < M) out[(int64_t)m * N + n] = to_bf16(alpha * acc[m]);
     }
 }
 
@@ -1290,7 +1302,9 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
     const int mr = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
     switch (mr * 8 + hpl) {
 #define NVFP4_GEMV_CASE(MR, HPL) \
-        case MR * 8 + HPL: hipLaunchKernelGGL((gemv_kernel<MR, HPL>), grid, block, 0, stream, a); break;
+        case MR * 8 + HPL: hipLaunchKernelGGL((gemv_kernel<MR, HPL>), grid, block, 0, stream, a.b_codes, \
+                                               a.b_scales, a.a_codes, a.a_scales, a.Np, a.Mp, a.P,  \
+                                               (int)grid.x, a.out, a.alpha, a.M, a.N); break;
         NVFP4_GEMV_CASE(1, 1) NVFP4_GEMV_CASE(1, 2) NVFP4_GEMV_CASE(1, 3) NVFP4_GEMV_CASE(1, 4)
         NVFP4_GEMV_CASE(2, 1) NVFP4_GEMV_CASE(2, 2) NVFP4_GEMV_CASE(2, 3) NVFP4_GEMV_CASE(2, 4)
         NVFP4_GEMV_CASE(4, 1) NVFP4_GEMV_CASE(4, 2) NVFP4_GEMV_CASE(4, 3) NVFP4_GEMV_CASE(4, 4)
@@ -1313,7 +1327,10 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
     if (mb == 2 && units == 3) units = 4;  // (3 units of two row blocks spill registers; 4 do not)
     switch (mb * 8 + units) {
 #define NVFP4_SKINNY_CASE(MB, U) \
-        case MB * 8 + U: hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, MB, U>), grid, block, 0, stream, a); break;
+        case MB * 8 + U: hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, MB, U>), grid, block, 0, stream, \
+                                            a.b_codes, a.b_scales, a.a_codes, a.a_scales, a.Np, a.Mp, \
+                                            a.P, a.split_k, a.out, a.partials, a.counters, a.alpha, a.M, \
+                                            a.N); break;
         NVFP4_SKINNY_CASE(1, 1) NVFP4_SKINNY_CASE(1, 2) NVFP4_SKINNY_CASE(1, 3) NVFP4_SKINNY_CASE(1, 4)
         NVFP4_SKINNY_CASE(2, 1) NVFP4_SKINNY_CASE(2, 2) NVFP4_SKINNY_CASE(2, 4)
         NVFP4_SKINNY_CASE(3, 1) NVFP4_SKINNY_CASE(3, 2)

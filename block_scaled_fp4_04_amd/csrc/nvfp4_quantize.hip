@@ -113,24 +113,29 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t A, const E2m1Search& q) {
     return code;
 }
 
-__global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
+// (Plain arguments, so that they are preloaded into scalar registers before
+// the waves start.)
+__global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ x, int64_t ld,
+                                                       int rows, int K, int Rp, int P,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
     // grid: x covers the padded rows of a panel (8 lanes per row, two per
     // 16-element block); the lane walks panels blockIdx.y, + gridDim.y, ...,
     // loading the next one while it quantises the current one
     const int t = (int)blockIdx.x * 256 + (int)threadIdx.x;
     const int r = t >> 3;
     const int blk = (t >> 1) & 3, half = t & 1;
-    const bool live = r < a.Rp;                       // whole 8-lane groups live or not
-    const bool row_has = live && r < a.rows;
+    const bool live = r < Rp;                       // whole 8-lane groups live or not
+    const bool row_has = live && r < rows;
     // The loads are unconditional, clamped into the input (the row to the
     // last one, the lane's 8 elements to end by K): values read for a
     // padding row or past K only feed blocks that are written as zeros.
     // Without a branch around them the compiler waits for each panel's
     // loads alone.  QD panels in flight per lane (the one being quantised
     // included): 3 or 4, and non-temporal loads, measured 2-13% slower.
-    const float* xrow = a.x + (int64_t)min(r, a.rows - 1) * a.ld;
+    const float* xrow = x + (int64_t)min(r, rows - 1) * ld;
     auto load = [&](int p, float (&v)[8]) {
-        const int k = min(min(p, a.P - 1) * 64 + blk * 16 + half * 8, a.K - 8);
+        const int k = min(min(p, P - 1) * 64 + blk * 16 + half * 8, K - 8);
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         const f32x4* src = reinterpret_cast<const f32x4*>(xrow + k);
         const f32x4 q0 = src[0], q1 = src[1];
@@ -142,12 +147,12 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
     int p = (int)blockIdx.y;
 #pragma unroll
     for (int d = 0; d < QD - 1; ++d) load(p + d * (int)gridDim.y, ring[d]);
-    for (; p < a.P; p += (int)gridDim.y) {
+    for (; p < P; p += (int)gridDim.y) {
         load(p + (QD - 1) * (int)gridDim.y, ring[QD - 1]);
         float cur[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) cur[i] = ring[0][i];
-        const bool has = row_has && p * 64 + blk * 16 < a.K;
+        const bool has = row_has && p * 64 + blk * 16 < K;
         // amax (v_max ignores a NaN operand, as the definition's comparison
         // does); the block's two lanes are an aligned pair: exchange within
         // it (DPP quad permutation 1,0,3,2)
@@ -169,9 +174,9 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
         }
         if (!has) w = 0u;
         if (live) {
-            const int64_t slot = (int64_t)p * a.Rp + r;
-            *reinterpret_cast<uint32_t*>(a.codes + slot * 32 + blk * 8 + half * 4) = w;
-            if (half == 0) a.scales[slot * 4 + blk] = has ? (uint8_t)sb : (uint8_t)0;
+            const int64_t slot = (int64_t)p * Rp + r;
+            *reinterpret_cast<uint32_t*>(codes + slot * 32 + blk * 8 + half * 4) = w;
+            if (half == 0) scales[slot * 4 + blk] = has ? (uint8_t)sb : (uint8_t)0;
         }
 #pragma unroll
         for (int d = 0; d + 1 < QD; ++d)
@@ -188,7 +193,8 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
     const int gx = (a.Rp * 8 + 255) / 256;
     const int gy = std::max(1, std::min(a.P, (4096 + gx - 1) / gx));
     const dim3 grid((unsigned)gx, (unsigned)gy);
-    hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, a.x, a.ld, a.rows, a.K, a.Rp, a.P,
+                       a.codes, a.scales);
     return hipGetLastError();
 }
 
