@@ -827,8 +827,14 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
 // flight.  At the end the wave tiles are added in LDS in wave order, then
 // (split_k > 1) across workgroups by the last arrival in split order.
 // ---------------------------------------------------------------------------
+// (Plain arguments, operands and geometry first, so that those can be
+// preloaded into scalar registers before the waves start.)
 template <int BM, int BN, int WAVES, bool SPLIT>
-__global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
+__global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int Mp, int Np,
+    int P, int tiles_n, int split_k, uint16_t* __restrict__ out, float* partials,
+    uint32_t* counters, float alpha, int M, int N) {
     constexpr int MI = BM / 32;
     constexpr int NI = BN / 32;
     // panels of loads in flight per wave (ring of DEPTH slots); 2 measured
@@ -841,16 +847,16 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
     const int wave = tid >> 6;
     const int q = lane & 31, h = lane >> 5;
 
-    const int S = SPLIT ? a.split_k : 1;
+    const int S = SPLIT ? split_k : 1;
     int bid = blockIdx.x;
     const int total = gridDim.x;
     if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
     const int z = bid % S;
     const int t = bid / S;
-    const int tm = t / a.tiles_n, tn = t % a.tiles_n;
+    const int tm = t / tiles_n, tn = t % tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    const int nst = a.P / 2;
+    const int nst = P / 2;
     const int p0 = 2 * (int)((int64_t)z * nst / S);
     const int p1 = 2 * (int)((int64_t)(z + 1) * nst / S);
     // this wave's panels: p0 + wave, p0 + wave + WAVES, ...
@@ -860,9 +866,9 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
     // padded operand; their results are not stored)
     int64_t a_off[MI], b_off[NI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) a_off[i] = min(m0 + i * 32 + q, a.Mp - 1);
+    for (int i = 0; i < MI; ++i) a_off[i] = min(m0 + i * 32 + q, Mp - 1);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) b_off[j] = min(n0 + j * 32 + q, a.Np - 1);
+    for (int j = 0; j < NI; ++j) b_off[j] = min(n0 + j * 32 + q, Np - 1);
 
     struct Regs {
         uint4 ca[MI], cb[NI];
@@ -876,15 +882,15 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
         const int64_t panel = p0 + wave + (int64_t)min(k, count - 1) * WAVES;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const int64_t row = panel * a.Mp + a_off[i];
-            r.ca[i] = *reinterpret_cast<const uint4*>(a.a_codes + row * 32 + h * 16);
-            r.sa[i] = *reinterpret_cast<const uint16_t*>(a.a_scales + row * 4 + h * 2);
+            const int64_t row = panel * Mp + a_off[i];
+            r.ca[i] = *reinterpret_cast<const uint4*>(a_codes + row * 32 + h * 16);
+            r.sa[i] = *reinterpret_cast<const uint16_t*>(a_scales + row * 4 + h * 2);
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int64_t row = panel * a.Np + b_off[j];
-            r.cb[j] = *reinterpret_cast<const uint4*>(a.b_codes + row * 32 + h * 16);
-            r.sb[j] = *reinterpret_cast<const uint16_t*>(a.b_scales + row * 4 + h * 2);
+            const int64_t row = panel * Np + b_off[j];
+            r.cb[j] = *reinterpret_cast<const uint4*>(b_codes + row * 32 + h * 16);
+            r.sb[j] = *reinterpret_cast<const uint16_t*>(b_scales + row * 4 + h * 2);
         }
     };
 
@@ -973,7 +979,7 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
     if (SPLIT) {
         // publish this workgroup's tile (slot order idx * 64 + lane); the
         // last arrival adds the S partial tiles in split order
-        float* mine = a.partials + ((int64_t)t * S + z) * (BM * BN);
+        float* mine = partials + ((int64_t)t * S + z) * (BM * BN);
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int idx = wave + u * WAVES;
@@ -983,13 +989,13 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
-            const uint32_t old = arrive(a.counters + t);
+            const uint32_t old = arrive(counters + t);
             s_last = (old == (uint32_t)(S - 1));
-            if (s_last) reset_counter(a.counters + t);  // all splits arrived
+            if (s_last) reset_counter(counters + t);  // all splits arrived
         }
         __syncthreads();
         if (!s_last) return;
-        const float* all = a.partials + (int64_t)t * S * (BM * BN);
+        const float* all = partials + (int64_t)t * S * (BM * BN);
 #pragma unroll
         for (int u = 0; u < PER; ++u) sum[u] = 0.0f;
         for (int zz = 0; zz < S; ++zz) {  // one batch of independent loads per split
@@ -1011,7 +1017,7 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(GemmArgs a) {
         const int i = ij / NI, j = ij % NI;
         const int row = m0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
         const int col = n0 + j * 32 + q;
-        if (row < a.M && col < a.N) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * sum[u]);
+        if (row < M && col < N) out[(int64_t)row * N + col] = to_bf16(alpha * sum[u]);
     }
 }
 
@@ -1280,16 +1286,21 @@ size_t wsplit_partial_floats(int cfg, const GemmArgs& a) {
 hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.split_k));
     const bool split = a.split_k > 1;
+#define NVFP4_WSPLIT(BM, BN, W, S, T)                                                            \
+    hipLaunchKernelGGL((wsplit_kernel<BM, BN, W, S>), grid, dim3(T), 0, stream, a.a_codes,       \
+                       a.a_scales, a.b_codes, a.b_scales, a.Mp, a.Np, a.P, a.tiles_n, a.split_k, \
+                       a.out, a.partials, a.counters, a.alpha, a.M, a.N)
     switch (cfg) {
         case WSPLIT_64x64:
-            if (split) hipLaunchKernelGGL((wsplit_kernel<64, 64, 8, true>), grid, dim3(512), 0, stream, a);
-            else hipLaunchKernelGGL((wsplit_kernel<64, 64, 8, false>), grid, dim3(512), 0, stream, a);
+            if (split) NVFP4_WSPLIT(64, 64, 8, true, 512);
+            else NVFP4_WSPLIT(64, 64, 8, false, 512);
             break;
         default:  // WSPLIT_128x64
-            if (split) hipLaunchKernelGGL((wsplit_kernel<128, 64, 4, true>), grid, dim3(256), 0, stream, a);
-            else hipLaunchKernelGGL((wsplit_kernel<128, 64, 4, false>), grid, dim3(256), 0, stream, a);
+            if (split) NVFP4_WSPLIT(128, 64, 4, true, 256);
+            else NVFP4_WSPLIT(128, 64, 4, false, 256);
             break;
     }
+#undef NVFP4_WSPLIT
     return hipGetLastError();
 }
 
