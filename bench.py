@@ -614,6 +614,13 @@ def main():
                            "path": path_name(nv, cr["plan"]["path"]),
                            "split_k": cr["plan"]["split_k"],
                            "pages_tflops_other_gpu": PAGES_TFLOPS.get(c.index)}
+            if c.M <= 16:   # the other decode-sized workload: also with operands beyond the cache
+                cc = time_workload(nv, torch, c, args.steps, args.warmup, cold=True, ops=cr["ops"])
+                per[c.name]["cold"] = {
+                    "ms": cc["graph_ms"],
+                    "tflops": synth.flops(c.M, c.N, c.K) / (cc["graph_ms"] * 1e-3) / 1e12,
+                    "roofline": roofline_for(c, cc["graph_ms"] * 1e-3),
+                    "note": "operand copies rotated beyond the last-level cache"}
         line["per_shape"] = per
         torch.cuda.empty_cache()
         line["floors"] = floors_line(nv, torch, args.steps)
