@@ -14,8 +14,8 @@
  *
  * i.e. C = alpha * (A . B^T) on block-scaled FP4 operands.  Sources:
  *   - "The SM120 FP4 Kernel Disaster", section "Input Knowledge Required",
- *     item 3: FP4 packs two 4-bit values into one byte and carries
- *     per-block scaling factors.
+ *     item 3: each byte holds a pair of 4-bit codes, and blocks of codes
+ *     share a scale.
  *   - "Peeling the Kernel Onion", section "The Benchmark Design": the data is
  *     packed as uint8 (two codes per byte), the scales are FP8 with one scale
  *     per 16 elements, and the output is 2 bytes per element.
@@ -236,42 +236,41 @@ static void one_element(const uint8_t* a_codes, const uint8_t* a_scales, const u
  *   exact    [M][N] alpha*S in fp64 (optional, may be NULL)
  *   mag      [M][N] T = sum_k |a'_k b'_k| (optional, may be NULL)
  * Returns 0, or -1 when M, N or K is negative or K is not a multiple of 16
- * (K must be divisible by the block size and the packing factor: "The SM120
- * FP4 Kernel Disaster", section "The Bash Command"). */
+ * (the pages require K to be a whole number of scale blocks, and so of code
+ * pairs: "The SM120 FP4 Kernel Disaster", section "The Bash Command").
+ * Work is spread over the host threads by output element, so a product with
+ * a single row uses every thread as well; each element is still the same
+ * plain sum over k in increasing order. */
 int oracle_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                 const uint8_t* b_scales, float alpha, int64_t M, int64_t N, int64_t K,
                 uint16_t* out, double* exact, double* mag) {
     if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return -1;
     if (M == 0 || N == 0) return 0;
-    /* Step 1: decode every B row once to fp64 (exact). */
-    double* bdec = (double*)malloc((size_t)(N * (K > 0 ? K : 1)) * sizeof(double));
-    if (!bdec) return -2;
+    const size_t kk = (size_t)(K > 0 ? K : 1);
+    /* Step 1: decode every row of A and of B once to fp64 (exact). */
+    double* adec = (double*)malloc((size_t)M * kk * sizeof(double));
+    double* bdec = (double*)malloc((size_t)N * kk * sizeof(double));
+    if (!adec || !bdec) {
+        free(adec);
+        free(bdec);
+        return -2;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) adec[m * K + k] = operand_at(a_codes, a_scales, K, m, k);
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) bdec[n * K + k] = b_at(b_codes, b_scales, N, K, n, k);
-    int fail = 0;
-    /* Step 2: per output row, decode the A row, then contract with every B row. */
-#pragma omp parallel
-    {
-        double* adec = (double*)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
-        if (!adec) {
-#pragma omp atomic write
-            fail = 1;
-        } else {
-#pragma omp for schedule(dynamic, 1)
-            for (int64_t m = 0; m < M; ++m) {
-                for (int64_t k = 0; k < K; ++k) adec[k] = operand_at(a_codes, a_scales, K, m, k);
-                for (int64_t n = 0; n < N; ++n) {
-                    int64_t i = m * N + n;
-                    one_element(a_codes, a_scales, b_codes, b_scales, bdec + n * K, alpha, N, K,
-                                m, n, adec, out + i, exact ? exact + i : NULL,
-                                mag ? mag + i : NULL);
-                }
-            }
-            free(adec);
-        }
+    /* Step 2: every output element is the contraction of its two rows. */
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < M * N; ++i) {
+        const int64_t m = i / N, n = i % N;
+        one_element(a_codes, a_scales, b_codes, b_scales, bdec + n * K, alpha, N, K, m, n,
+                    adec + m * K, out + i, exact ? exact + i : NULL, mag ? mag + i : NULL);
     }
+    free(adec);
     free(bdec);
-    return fail ? -2 : 0;
+    return 0;
 }
 
 /* Selected output elements only, each computed on its own from the packed
