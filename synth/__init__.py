@@ -179,11 +179,19 @@ def quantized_operands(seed: int, M: int, N: int, K: int, alpha: float = 1.0,
     return Operands(ac, as_, bc, bs, alpha, M, N, K)
 
 
+def operand_bytes(rows: int, K: int) -> int:
+    """Unpadded size of one NVFP4 operand: a byte holds two 4-bit codes, and
+    every 16-element block of a row carries one 1-byte scale."""
+    codes = rows * K // 2
+    scales = rows * (K // 16)
+    return codes + scales
+
+
 def algorithmic_bytes(M: int, N: int, K: int) -> int:
-    """Bytes the GEMM must move: packed A and B codes, their FP8 scales and
-    the 2-byte output ("Peeling the Kernel Onion", section "The Benchmark
-    Design")."""
-    return (M * K // 2) + (K * N // 2) + (M * K // 16) + (K * N // 16) + (M * N * 2)
+    """Bytes the GEMM must move at least once: both operands read and the
+    bfloat16 output written (the traffic model of "Peeling the Kernel Onion",
+    section "The Benchmark Design")."""
+    return operand_bytes(M, K) + operand_bytes(N, K) + 2 * M * N
 
 
 def flops(M: int, N: int, K: int) -> int:
@@ -294,6 +302,6 @@ def make_grouped_inputs(cfg: GroupedConfig) -> GroupedOperands:
 
 
 def grouped_algorithmic_bytes(M: int, N: int, K: int, G: int) -> int:
-    """Packed A (M rows), G packed weight operands (N rows each), the FP8
-    scales of both, and the 2-byte output."""
-    return (M * K // 2) + G * (K * N // 2) + (M * K // 16) + G * (K * N // 16) + (M * N * 2)
+    """A (M rows) and the G weight operands (N rows each) read once, the
+    bfloat16 output written once."""
+    return operand_bytes(M, K) + G * operand_bytes(N, K) + 2 * M * N
