@@ -37,6 +37,9 @@ ERR_HIP = 4
 ERR_ALLOC = 5
 ERR_CAPTURE = 6
 ERR_STATE = 7
+ERR_DEVICE_FLAGS = 8
+
+FLAG_HANDOFF = 1
 
 PATH_AUTO = 0
 PATH_TILE = 1
@@ -54,7 +57,9 @@ EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_p
            "nvfp4_plan_table_clear", "nvfp4_build_id", "nvfp4_grouped_gemm", "nvfp4_quantize",
            "nvfp4_sequence_create", "nvfp4_sequence_add_gemm", "nvfp4_sequence_add_grouped_gemm",
            "nvfp4_sequence_add_quantize", "nvfp4_sequence_finalize", "nvfp4_sequence_launch",
-           "nvfp4_sequence_destroy", "nvfp4_probe_empty", "nvfp4_probe_chase"]
+           "nvfp4_sequence_destroy", "nvfp4_probe_empty", "nvfp4_probe_chase",
+           "nvfp4_probe_mfma", "nvfp4_probe_read", "nvfp4_device_flags",
+           "nvfp4_debug_set_handoff_polls"]
 
 
 class _PlanT(ctypes.Structure):
@@ -107,6 +112,14 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_probe_empty.argtypes = [_i64, _i64, _vp]
         L.nvfp4_probe_chase.restype = ctypes.c_int
         L.nvfp4_probe_chase.argtypes = [_vp, _i64, _i64, _vp, _vp]
+        L.nvfp4_probe_mfma.restype = ctypes.c_int
+        L.nvfp4_probe_mfma.argtypes = [_i64, _i64, _vp, _vp]
+        L.nvfp4_probe_read.restype = ctypes.c_int
+        L.nvfp4_probe_read.argtypes = [_vp, _i64, _i64, _vp, _vp]
+        L.nvfp4_device_flags.restype = ctypes.c_int
+        L.nvfp4_device_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+        L.nvfp4_debug_set_handoff_polls.restype = ctypes.c_int
+        L.nvfp4_debug_set_handoff_polls.argtypes = [ctypes.c_uint32]
         L.nvfp4_grouped_gemm.restype = ctypes.c_int
         L.nvfp4_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float, _vp, _i64,
                                          _i64, _i64, _vp]
@@ -309,6 +322,22 @@ def gemm(a: PackedOperand, b: PackedOperand, alpha: float = 1.0, out=None,
     return out
 
 
+def device_flags() -> int:
+    """Synchronise the current device and return (and clear) the error
+    flags its kernels raised (FLAG_* bits; 0 = none)."""
+    f = ctypes.c_uint32()
+    st = lib().nvfp4_device_flags(ctypes.byref(f))
+    if st not in (OK, ERR_DEVICE_FLAGS):
+        raise Nvfp4Error(st, "nvfp4_device_flags")
+    return int(f.value)
+
+
+def set_handoff_polls(polls: int | None) -> None:
+    """Test hook: poll budget of a two-way split-K hand-off for calls
+    planned from now on (None restores the default)."""
+    lib().nvfp4_debug_set_handoff_polls(0xFFFFFFFF if polls is None else int(polls))
+
+
 def gemm_raw(a_codes: int, a_scales: int, b_codes: int, b_scales: int, alpha: float, out: int,
              M: int, N: int, K: int, stream: int | None = None) -> int:
     """Direct call of nvfp4_gemm with raw device addresses; returns the status."""
@@ -420,6 +449,26 @@ def probe_chase(next_idx, steps: int, out, stream=None) -> None:
                                  _stream_handle(stream))
     if st:
         raise Nvfp4Error(st, f"nvfp4_probe_chase(n={next_idx.numel()}, steps={steps})")
+
+
+def probe_mfma(blocks: int, iters: int, out, stream=None) -> None:
+    """Enqueue the MFMA-rate kernel (nvfp4_probe_mfma): blocks x 4 waves x
+    iters x 8 fp16 MFMAs of 32 x 32 x 16; ``out`` is a float32 device tensor
+    of at least blocks x 256 elements."""
+    if out.numel() < blocks * 256:
+        raise ValueError("out must hold blocks x 256 floats")
+    st = lib().nvfp4_probe_mfma(blocks, iters, out.data_ptr(), _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_probe_mfma(blocks={blocks}, iters={iters})")
+
+
+def probe_read(src, blocks: int, out, stream=None) -> None:
+    """Enqueue the streaming-read kernel (nvfp4_probe_read) over all bytes
+    of the device tensor ``src``."""
+    st = lib().nvfp4_probe_read(src.data_ptr(), src.numel() * src.element_size(), blocks,
+                                out.data_ptr(), _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_probe_read(blocks={blocks})")
 
 
 class Sequence:

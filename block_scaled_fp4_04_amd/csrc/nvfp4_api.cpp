@@ -12,11 +12,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "nvfp4.h"
 #include "nvfp4_host.h"
@@ -32,6 +34,10 @@ bool valid_rows_k(int64_t rows, int64_t K) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Poll budget of the two-way split-K hand-off given to the kernels
+// (nvfp4_debug_set_handoff_polls changes it for tests).
+std::atomic<uint32_t> g_handoff_polls{kHandoffPolls};
 
 // ---- device checks -------------------------------------------------------
 
@@ -63,6 +69,11 @@ struct Workspace {
     size_t partial_floats = 0;
     uint32_t* counters = nullptr;
     size_t counter_count = 0;
+    // Buffers replaced by larger ones.  A graph captured on the stream may
+    // still hold their addresses, so they stay allocated until
+    // nvfp4_shutdown (freeing them would leave such a graph writing into
+    // freed memory).
+    std::vector<void*> retired;
 };
 
 std::map<std::pair<int, void*>, Workspace> g_ws;
@@ -74,9 +85,10 @@ bool capturing(void* stream) {
 }
 
 // Makes sure the workspace of (device, stream) can hold the request.  Growing
-// it frees the old buffers (hipFree waits for work that may still use them)
-// and zero-fills the new counters; this happens only when a larger shape is
-// seen for the first time on that stream, and never while the stream is
+// it allocates larger buffers and zero-fills the new counters (synchronously,
+// so they are zero before any kernel uses them); the old buffers are retired,
+// not freed (see Workspace::retired).  This happens only when a larger shape
+// is seen for the first time on that stream, and never while the stream is
 // being captured into a graph (NVFP4_ERR_CAPTURE: allocation and the
 // synchronous fill are not allowed there).
 int get_workspace(int device, void* stream, size_t floats, size_t counters, Workspace** out) {
@@ -85,18 +97,21 @@ int get_workspace(int device, void* stream, size_t floats, size_t counters, Work
     if ((floats > ws.partial_floats || counters > ws.counter_count) && capturing(stream))
         return NVFP4_ERR_CAPTURE;
     if (floats > ws.partial_floats) {
-        if (ws.partials) (void)hipFree(ws.partials);
-        ws.partials = nullptr;
-        ws.partial_floats = 0;
-        if (hipMalloc(&ws.partials, floats * sizeof(float)) != hipSuccess) return NVFP4_ERR_ALLOC;
+        float* p = nullptr;
+        if (hipMalloc(&p, floats * sizeof(float)) != hipSuccess) return NVFP4_ERR_ALLOC;
+        if (ws.partials) ws.retired.push_back(ws.partials);
+        ws.partials = p;
         ws.partial_floats = floats;
     }
     if (counters > ws.counter_count) {
-        if (ws.counters) (void)hipFree(ws.counters);
-        ws.counters = nullptr;
-        ws.counter_count = 0;
-        if (hipMalloc(&ws.counters, counters * sizeof(uint32_t)) != hipSuccess) return NVFP4_ERR_ALLOC;
-        if (hipMemset(ws.counters, 0, counters * sizeof(uint32_t)) != hipSuccess) return NVFP4_ERR_HIP;
+        uint32_t* c = nullptr;
+        if (hipMalloc(&c, counters * sizeof(uint32_t)) != hipSuccess) return NVFP4_ERR_ALLOC;
+        if (hipMemset(c, 0, counters * sizeof(uint32_t)) != hipSuccess) {
+            (void)hipFree(c);
+            return NVFP4_ERR_HIP;
+        }
+        if (ws.counters) ws.retired.push_back(ws.counters);
+        ws.counters = c;
         ws.counter_count = counters;
     }
     *out = &ws;
@@ -178,6 +193,7 @@ int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packe
     a.tile_count = plan.tiles_m * plan.tiles_n;
     a.tail_tiles = plan.tail_tiles;
     a.tail_split = plan.tail_split;
+    a.handoff_polls = g_handoff_polls.load(std::memory_order_relaxed);
     job->floats = plan.path == NVFP4_PATH_GEMV     ? 0
                   : plan.path == NVFP4_PATH_SKINNY ? skinny_partial_floats(a)
                   : plan.path == NVFP4_PATH_WSPLIT ? wsplit_partial_floats(plan.cfg, a)
@@ -241,6 +257,7 @@ int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_pa
             g.tile_count = (int)(tiles_m * tiles_n);
             g.offsets = row_offsets;
             g.groups = (int)groups;
+            g.handoff_polls = g_handoff_polls.load(std::memory_order_relaxed);
             return NVFP4_OK;
         }
     }
@@ -315,11 +332,12 @@ const char* nvfp4_status_string(int status) {
         case NVFP4_ERR_ALLOC: return "workspace allocation failed";
         case NVFP4_ERR_CAPTURE: return "workspace needed while the stream is being captured";
         case NVFP4_ERR_STATE: return "call not allowed in the object's current state";
+        case NVFP4_ERR_DEVICE_FLAGS: return "a kernel raised a device error flag (see nvfp4_device_flags)";
         default: return "unknown status";
     }
 }
 
-int nvfp4_version(void) { return 10200; }
+int nvfp4_version(void) { return 10300; }
 
 int nvfp4_packed_size(int64_t rows, int64_t K, size_t* code_bytes, size_t* scale_bytes) {
     if (!code_bytes || !scale_bytes || !valid_rows_k(rows, K)) return NVFP4_ERR_INVALID_VALUE;
@@ -396,9 +414,24 @@ void nvfp4_shutdown(void) {
         (void)hipSetDevice(kv.first.first);
         if (kv.second.partials) (void)hipFree(kv.second.partials);
         if (kv.second.counters) (void)hipFree(kv.second.counters);
+        for (void* p : kv.second.retired) (void)hipFree(p);
     }
     (void)hipSetDevice(current);
     g_ws.clear();
+}
+
+int nvfp4_device_flags(uint32_t* flags) {
+    if (!flags) return NVFP4_ERR_INVALID_VALUE;
+    int device = 0;
+    const int st = current_device(&device);
+    if (st != NVFP4_OK) return st;
+    if (take_device_flags(flags) != hipSuccess) return NVFP4_ERR_HIP;
+    return *flags ? NVFP4_ERR_DEVICE_FLAGS : NVFP4_OK;
+}
+
+int nvfp4_debug_set_handoff_polls(uint32_t polls) {
+    g_handoff_polls.store(polls == 0xFFFFFFFFu ? kHandoffPolls : polls, std::memory_order_relaxed);
+    return NVFP4_OK;
 }
 
 int nvfp4_gemm(const void* a_packed, const void* a_scales, const void* b_packed,

@@ -39,7 +39,22 @@ struct GemmArgs {
                                  // run in a second launch split tail_split ways along K
     const int32_t* offsets;   // grouped tile launch: [groups + 1] row offsets (device), else null
     int groups;               // grouped tile launch: number of groups (B holds one N x K operand each)
+    uint32_t handoff_polls;   // tile kernel, two K slices: polls before the second workgroup
+                              // gives up waiting for the first one's partial tile
 };
+
+// Polls of a two-way split-K hand-off before it gives up (each poll sleeps
+// about 128 cycles, so the default is a fraction of a second; the partner
+// workgroup is already running when the wait starts, so it never runs out in
+// practice).
+constexpr uint32_t kHandoffPolls = 1u << 22;
+
+// Sticky error flags the kernels raise on the device (include/nvfp4.h,
+// nvfp4_device_flags); bit values match NVFP4_FLAG_*.
+constexpr uint32_t kFlagHandoff = 1u;
+
+// Reads the flags of the current device (after synchronising it) and clears them.
+hipError_t take_device_flags(uint32_t* flags);
 
 // Tile configurations of the large-M kernel.
 enum TileConfig { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x64 = 2 };

@@ -24,6 +24,13 @@
 namespace nvfp4 {
 namespace {
 
+// Sticky error flags of this device's kernels (kFlag* bits), read and
+// cleared by the host through take_device_flags.
+__device__ uint32_t g_device_flags;
+
+__device__ __forceinline__ void raise_flag(uint32_t bit) {
+    (void)__hip_atomic_fetch_or(&g_device_flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ---------------------------------------------------------------------------
 // Large-M tile kernel.
@@ -570,7 +577,12 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
             // The tile's counter takes one increment per arrival and one
             // from the first workgroup once its tile is out, so the second
             // (ticket 1 or 2) waits until it reads 3.  The first workgroup
-            // never waits, so the wait ends; it is bounded all the same.
+            // is already running and never waits, so the wait ends; it is
+            // bounded all the same (a.handoff_polls).  A second workgroup
+            // that runs out of polls takes the tile's three increments back
+            // (the counter is zero again once the first one has finished, so
+            // later calls stay in step), leaves the tile unwritten and raises
+            // the device's hand-off flag for the host to read.
             __syncthreads();
             if (tid == 0) s_last = (int)arrive(a.counters + t0);
             __syncthreads();
@@ -588,14 +600,26 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
                 if (tid == 0) (void)arrive(a.counters + t0);  // the partial tile is out
                 return;
             }
+            __shared__ int s_ready;
             if (tid == 0) {
-                for (int it = 0; it < (1 << 22); ++it) {
-                    if (__hip_atomic_load(a.counters + t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= 3u) break;
+                int ready = 0;
+                for (uint32_t it = 0; it < a.handoff_polls; ++it) {
+                    if (__hip_atomic_load(a.counters + t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= 3u) {
+                        ready = 1;
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(2);
                 }
-                reset_counter(a.counters + t0);
+                if (ready) {
+                    reset_counter(a.counters + t0);
+                } else {
+                    (void)__hip_atomic_fetch_sub(a.counters + t0, 3u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    raise_flag(kFlagHandoff);
+                }
+                s_ready = ready;
             }
             __syncthreads();
+            if (!s_ready) return;
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const float* po = a.partials + slot + (i * NI) * 16 * 256 + tid;
@@ -1171,6 +1195,17 @@ __global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(
 }
 
 }  // namespace
+
+hipError_t take_device_flags(uint32_t* flags) {
+    *flags = 0;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_device_flags), sizeof(uint32_t));
+    if (e == hipSuccess && *flags) {
+        const uint32_t zero = 0;
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_device_flags), &zero, sizeof(uint32_t));
+    }
+    return e;
+}
 
 size_t tile_partial_floats(int cfg, const GemmArgs& a) {
     const TileShape s = tile_shape(cfg);

@@ -5,7 +5,7 @@
  *   - A is M x K and B is N x K, both held as FP4 E2M1 codes packed two per
  *     byte, with one FP8 E4M3 scale per 16-element block along K ("Peeling
  *     the Kernel Onion", section "The Benchmark Design": packed uint8 data,
- *     FP8 scale factors, one per 16 elements; "The SM120 FP4 Kernel
+ *     an FP8 scale for every 16 elements; "The SM120 FP4 Kernel
  *     Disaster", section "Input Knowledge Required", item 3);
  *   - alpha is an FP32 scalar and C is a caller-provided M x N bfloat16
  *     output ("Peeling the Kernel Onion", section "The Chain of Reasoning":
@@ -54,8 +54,16 @@ typedef enum nvfp4_status {
     NVFP4_ERR_ALLOC = 5,         /* workspace allocation failed */
     NVFP4_ERR_CAPTURE = 6,       /* a split-K workspace would have to be created or
                                     grown while the stream is being captured */
-    NVFP4_ERR_STATE = 7          /* call not allowed in the object's current state */
+    NVFP4_ERR_STATE = 7,         /* call not allowed in the object's current state */
+    NVFP4_ERR_DEVICE_FLAGS = 8   /* nvfp4_device_flags: a kernel raised an error flag */
 } nvfp4_status;
+
+/* Device error flags (nvfp4_device_flags). */
+enum {
+    /* a two-way split-K hand-off ran out of polls waiting for its partner's
+     * partial tile: that output tile was left unwritten */
+    NVFP4_FLAG_HANDOFF = 1
+};
 
 /* Kernel paths for nvfp4_gemm_with_plan and nvfp4_plan. */
 enum {
@@ -95,9 +103,28 @@ int nvfp4_unpack(const uint8_t* packed_codes, const uint8_t* packed_scales, int6
  * for a non-gfx950 device, NVFP4_ERR_HIP if the device cannot be queried. */
 int nvfp4_init(int device);
 
-/* Frees every workspace the library allocated.  The caller must make sure no
- * nvfp4 kernel is still running; later calls re-create what they need. */
+/* Frees every workspace the library allocated, including buffers retired
+ * when a workspace grew.  The caller must make sure no nvfp4 kernel is still
+ * running and that no graph captured from nvfp4 calls will be replayed
+ * again; later calls re-create what they need. */
 void nvfp4_shutdown(void);
+
+/* Sticky error flags raised by the library's kernels on the current device
+ * (NVFP4_FLAG_* bits).  Synchronises the device, stores the flags in *flags,
+ * clears them, and returns NVFP4_ERR_DEVICE_FLAGS if any was set (the
+ * results of the calls since the last check may then be incomplete), else
+ * NVFP4_OK.  The only flag is NVFP4_FLAG_HANDOFF; a kernel that raises it
+ * still finishes normally and leaves the split-K counters ready for the next
+ * call.  "The SM120 FP4 Kernel Disaster", section "Finding 2": a GEMM that
+ * silently returns a wrong result is the failure to guard against. */
+int nvfp4_device_flags(uint32_t* flags);
+
+/* Test hook: the number of polls (each about 128 clock cycles) a two-way
+ * split-K hand-off waits for its partner before it gives up; applies to the
+ * calls planned afterwards (a recorded sequence keeps the value of its
+ * add).  0 makes every such wait give up at once; 0xFFFFFFFF restores the
+ * default (2^22).  Always NVFP4_OK. */
+int nvfp4_debug_set_handoff_polls(uint32_t polls);
 
 /* C = alpha * (A . B^T), bfloat16 output, round-to-nearest-even.
  *   a_packed, a_scales : DEVICE pointers, A packed by nvfp4_pack (rows = M)
@@ -113,11 +140,18 @@ void nvfp4_shutdown(void);
  * synchronisation.  The tile path needs each packed code buffer to stay
  * below 2 GiB (else NVFP4_ERR_UNSUPPORTED).  Split-K paths use a
  * library-owned workspace per
- * (device, stream) pair, allocated on the first call that needs it (the
- * only allocation the library makes); calls on one stream are ordered, calls
- * on different streams use different workspaces.  Under stream capture the
- * workspace must already be large enough (make one call of the same shape
- * on that stream first), else NVFP4_ERR_CAPTURE.  Launch failures return
+ * (device, stream) pair, allocated (and its counters zeroed with a
+ * synchronous fill) on the first call that needs it and again, larger, on the
+ * first call of a shape that needs more; these are the only allocations the
+ * library makes.  Calls on one stream are ordered, calls on different
+ * streams use different workspaces.  Buffers replaced by larger ones stay
+ * allocated until nvfp4_shutdown, so a graph captured earlier keeps working.
+ * Under stream capture the workspace must already be large enough (make one
+ * call of the same shape on that stream first), else NVFP4_ERR_CAPTURE.  A
+ * captured call keeps the workspace of the stream it was captured on,
+ * wherever the graph is replayed: do not let a replay overlap other calls
+ * on that stream or other replays of graphs captured on it (order them, for
+ * instance by replaying on the capture stream).  Launch failures return
  * NVFP4_ERR_HIP. */
 int nvfp4_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
                const void* b_scales, float alpha, void* out, int64_t M, int64_t N, int64_t K,
@@ -319,6 +353,23 @@ int nvfp4_sequence_destroy(nvfp4_sequence_t seq);
 int nvfp4_probe_empty(int64_t blocks, int64_t threads, void* stream);
 int nvfp4_probe_chase(const uint32_t* next, int64_t n, int64_t steps, uint32_t* out,
                       void* stream);
+
+/* The two measured peaks beside the datasheet ones (the pages stress that a
+ * quoted peak is an estimate: "Peeling the Kernel Onion", section
+ * "Assumptions Embedded in the Benchmark"; "The SM120 FP4 Kernel Disaster",
+ * section "Finding 4").
+ * nvfp4_probe_mfma: `blocks` workgroups of 4 waves; every wave issues
+ *   iters x 8 fp16 MFMAs of 32 x 32 x 16 (2 x 32 x 32 x 16 FLOP each) and
+ *   writes one float per work-item to out (device, caller-owned, at least
+ *   blocks x 256 floats).  blocks in 1 .. 2^20, iters >= 1.
+ * nvfp4_probe_read: `blocks` workgroups of 256 work-items read the first
+ *   `bytes` of src (device, 16-byte aligned; bytes a positive multiple of
+ *   16) once, with 16-byte loads, and write nothing to out (device, one
+ *   uint32, caller-owned) unless the bytes fold to a fixed improbable value.
+ * Same error rules as the probes above. */
+int nvfp4_probe_mfma(int64_t blocks, int64_t iters, float* out, void* stream);
+int nvfp4_probe_read(const void* src, int64_t bytes, int64_t blocks, uint32_t* out,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -250,3 +250,21 @@ def test_probe_arguments_are_checked_before_launch():
     assert L.nvfp4_probe_chase(p, 0, 1, p, None) == nv.ERR_INVALID_VALUE
     assert L.nvfp4_probe_chase(p, 16, -1, p, None) == nv.ERR_INVALID_VALUE
     assert L.nvfp4_probe_chase(p, (1 << 32) + 2, 1, p, None) == nv.ERR_INVALID_VALUE
+    out = ctypes.create_string_buffer(64 * 1024)
+    q = ctypes.addressof(out)
+    assert L.nvfp4_probe_mfma(0, 1, q, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_mfma(1, 0, q, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_mfma(1, 1, None, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_read(p, 64, 1, None, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_read(None, 64, 1, p, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_read(p, 40, 1, p, None) == nv.ERR_INVALID_VALUE    # not whole 16-byte chunks
+    assert L.nvfp4_probe_read(p, 64, 0, p, None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_probe_read(p + 4, 64, 1, p, None) == nv.ERR_INVALID_VALUE  # misaligned
+
+
+def test_device_flags_and_poll_hook_on_the_host():
+    L = nv.lib()
+    assert L.nvfp4_device_flags(None) == nv.ERR_INVALID_VALUE
+    assert L.nvfp4_debug_set_handoff_polls(0) == nv.OK
+    assert L.nvfp4_debug_set_handoff_polls(0xFFFFFFFF) == nv.OK
+    assert "flag" in nv.status_string(nv.ERR_DEVICE_FLAGS)
