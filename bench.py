@@ -49,6 +49,8 @@ def parse():
                     help="time only the fp32 -> NVFP4 quantisation shapes")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step: eager calls against one recorded sequence")
+    ap.add_argument("--floors-only", action="store_true",
+                    help="measure only the floors (empty kernel, load latencies, measured peaks)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--cold", action="store_true",
@@ -247,8 +249,12 @@ def time_workload(nv, torch, cfg, steps, warmup, cold=False, ops=None):
     wall = time.perf_counter() - t0
     graph_ms = start.elapsed_time(stop) / steps
     plan = nv.plan(cfg.M, cfg.N, cfg.K)
+    # the timed replay's own output (warm: every call wrote the one output
+    # buffer), copied out after the timing for the parity check
+    out_bits = None if cold else sets[0][2].view(torch.int16).cpu().numpy().astype(np.uint16)
     del g, sets
-    return {"graph_ms": graph_ms, "eager_ms": eager_ms, "wall_s": wall, "plan": plan, "ops": ops}
+    return {"graph_ms": graph_ms, "eager_ms": eager_ms, "wall_s": wall, "plan": plan, "ops": ops,
+            "out_bits": out_bits}
 
 
 def grouped_roofline(g, seconds_per_call):
@@ -500,6 +506,111 @@ def floors_line(nv, torch, steps):
             "load_latency_how": "one work-item, dependent loads along a random cycle"}
 
 
+def measured_peaks(nv, torch, steps):
+    """The two peaks measured on this GPU with the library's measurement aids:
+    the fp16 MFMA rate (nvfp4_probe_mfma: 1024 workgroups x 4 waves, 8
+    independent 32 x 32 x 16 MFMAs per round) and the rate of a streaming
+    read of 1 GiB from HBM (nvfp4_probe_read, 16-byte loads; best of two grid
+    sizes), each timed over a graph replay of several launches."""
+    stream = torch.cuda.Stream()
+
+    def replay_ms(fn, reps):
+        with torch.cuda.stream(stream):
+            fn()
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                fn()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            start.record(stream)
+            g.replay()
+            stop.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return start.elapsed_time(stop) / reps
+
+    blocks, iters = 1024, 2000
+    mout = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    ms = replay_ms(lambda: nv.probe_mfma(blocks, iters, mout, stream=torch.cuda.current_stream()), 5)
+    mfma = blocks * 4 * iters * 8 * 2 * 32 * 32 * 16 / (ms * 1e-3) / 1e12
+    del mout
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    src.random_(0, 256)
+    rout = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for b in (2048, 8192):
+        rms = replay_ms(lambda: nv.probe_read(src, b, rout, stream=torch.cuda.current_stream()), 5)
+        best = max(best, src.numel() / (rms * 1e-3) / 1e9)
+    del src
+    torch.cuda.empty_cache()
+    return {"mfma_f16_tflops": mfma, "hbm_read_gbps": best,
+            "how": "nvfp4_probe_mfma (1024 x 4 waves x 2000 rounds of 8 fp16 32x32x16 MFMAs) and "
+                   "nvfp4_probe_read (1 GiB, best of 2048 / 8192 workgroups), graph replays of 5"}
+
+
+def add_measured_fracs(node, peaks):
+    """Every roofline object in the line also gets its fraction of the
+    measured peak of its bound."""
+    if isinstance(node, dict):
+        if "bound" in node and "achieved" in node:
+            p = peaks["hbm_read_gbps"] if node["bound"] == "hbm" else peaks["mfma_f16_tflops"]
+            node["peak_measured"] = p
+            node["frac_of_measured"] = node["achieved"] / p
+        for v in node.values():
+            add_measured_fracs(v, peaks)
+
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def oracle_leg(o, cfg, ops, gpu_bits):
+    """Parity of the timed run's output against the oracle, and the oracle's
+    own time for it (all host threads).  Full matrix up to 10^10 MACs; above
+    that, whole rows, columns, tiles and random elements (oracle/parity.py's
+    large_sample), with the full-matrix oracle time extrapolated by MACs."""
+    from oracle import parity
+    M, N, K = cfg.M, cfg.N, cfg.K
+    if M * N * K <= 10 ** 10:
+        t0 = time.perf_counter()
+        bits, exact, mag = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, cfg.alpha)
+        el = time.perf_counter() - t0
+        r = parity.compare(gpu_bits, bits, exact, mag, cfg.alpha)
+        return ({k: r[k] for k in ("n", "over", "max_err_over_tol", "bit_exact_frac")} |
+                {"elements": "all"},
+                {"oracle_s": el, "tflops": synth.flops(M, N, K) / el / 1e12, "threads": o.threads,
+                 "sample": "the full GEMM once"})
+    sample = parity.large_sample(M, N)
+    r = parity.check_sample(o, ops, gpu_bits, sample)
+    macs = r["n"] * K
+    el = r["oracle_s"]
+    what = (f"rows {sample['rows']}, columns {sample['cols']}, {len(sample['tiles'])} whole 256x256 "
+            f"tiles at {sample['tiles']}, {len(sample['points'][0])} random elements")
+    return ({k: r[k] for k in ("n", "over", "max_err_over_tol", "bit_exact_frac")} |
+            {"elements": what},
+            {"oracle_s": el, "tflops": 2 * macs / el / 1e12, "threads": o.threads,
+             "full_matrix_s_extrapolated": el * (M * N * K) / macs,
+             "sample": f"{r['n']} output elements ({what}); the full-matrix time is extrapolated "
+                       "by the number of multiply-adds"})
+
+
 def cpu_baseline(cfg, ops, budget_s):
     from oracle import oracle as orc
     o = orc.load()
@@ -513,10 +624,11 @@ def cpu_baseline(cfg, ops, budget_s):
         o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, cfg.alpha, want_exact=False)
     el = time.perf_counter() - t0
     tflops = synth.flops(cfg.M, cfg.N, cfg.K) * reps / el / 1e12
-    # the oracle parallelises over output rows, so it uses at most M threads
-    return {"value": tflops, "unit": "TFLOPS", "cores": min(o.threads, cfg.M), "kind": "oracle",
+    # the oracle spreads its output elements over all its OpenMP threads
+    return {"value": tflops, "unit": "TFLOPS", "cores": min(o.threads, cfg.M * cfg.N),
+            "kind": "oracle",
             "sample": f"the full {cfg.M}x{cfg.N}x{cfg.K} GEMM repeated {reps} times "
-                      f"({el:.1f} s, fp64 C oracle, OpenMP over rows)"}
+                      f"({el:.1f} s, fp64 C oracle, OpenMP over output elements)"}
 
 
 def main():
@@ -557,10 +669,17 @@ def main():
         name, g = grouped_line(nv, torch, args.steps, args.warmup)
         print(json.dumps({"workload": name, **g}), flush=True)
         return
+    if args.floors_only:
+        f = floors_line(nv, torch, args.steps)
+        f["measured_peaks"] = measured_peaks(nv, torch, args.steps)
+        print(json.dumps({"floors": f}), flush=True)
+        return
+    peaks = None if args.only_headline else measured_peaks(nv, torch, args.steps)
 
     cfg = synth.config(args.workload)
     r = time_workload(nv, torch, cfg, args.steps, args.warmup)
     ms, plan, ops = r["graph_ms"], r["plan"], r["ops"]
+    outputs = {cfg.name: (cfg, ops, r["out_bits"])}   # checked against the oracle at the end
     tflops = synth.flops(cfg.M, cfg.N, cfg.K) / (ms * 1e-3) / 1e12
     line = {
         "metric": "NVFP4 GEMM TFLOPS (2MNK/s) per shape + % of HBM/MFMA roofline, 1 MI355X",
@@ -608,6 +727,7 @@ def main():
             cr = time_workload(nv, torch, c, args.steps, args.warmup)
             cms = cr["graph_ms"]
             ctf = synth.flops(c.M, c.N, c.K) / (cms * 1e-3) / 1e12
+            outputs[c.name] = (c, cr["ops"], cr["out_bits"])
             per[c.name] = {"M": c.M, "N": c.N, "K": c.K, "ms": cms, "tflops": ctf,
                            "eager_ms": cr["eager_ms"],
                            "roofline": dict(roofline_for(c, cms * 1e-3), traffic=stored_traffic(c)),
@@ -624,8 +744,25 @@ def main():
         line["per_shape"] = per
         torch.cuda.empty_cache()
         line["floors"] = floors_line(nv, torch, args.steps)
+        line["floors"]["measured_peaks"] = peaks
+        add_measured_fracs(line, peaks)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, ops, args.cpu_seconds)
+        # after every GPU timing: the oracle on all host threads, for the
+        # headline's baseline figure and, per workload, for the parity of the
+        # timed run's own output and the oracle's time
+        from oracle import oracle as orc
+        o = orc.load()
+        cb = cpu_baseline(cfg, ops, args.cpu_seconds)
+        cb["host"] = host_info() | {"oracle_threads": o.threads}
+        cb["per_config"] = {}
+        for name, (c, c_ops, bits) in outputs.items():
+            par, stats = oracle_leg(o, c, c_ops, bits)
+            cb["per_config"][name] = stats
+            if c.index == cfg.index:
+                line["parity"] = par
+            else:
+                line["per_shape"][name]["parity"] = par
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 

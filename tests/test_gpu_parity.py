@@ -15,7 +15,7 @@ import pytest
 
 import synth
 from oracle import oracle as orc
-from parity import compare
+from parity import check_sample, compare, large_sample
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -140,26 +140,28 @@ def test_parity_workload(o, i):
     assert not r["all_zero"]
 
 
-def test_parity_saturation_sampled(o):
-    """16384 x 8192 x 8192 in the launch configuration the benchmark times;
-    checked at sampled elements (full rows, full columns and random ones)."""
+def test_parity_saturation(o):
+    """16384 x 8192 x 8192 in the launch configuration the benchmark times
+    (persistent 256 x 256 tiles, no split), checked element by element
+    against the oracle on: four whole rows and four whole columns (the
+    first, both sides of the first tile edge, the last); whole 256 x 256
+    tiles at the start of the grid, at the start of each XCD's contiguous
+    range of tiles and at the end of the grid; and 4096 random elements.
+    Every other element is checked to be finite."""
+    import os
     cfg = synth.config(5)
+    p = nv.plan(cfg.M, cfg.N, cfg.K)
+    assert (p["path"], p["tile_m"], p["split_k"], p["tail_tiles"]) == (nv.PATH_TILE, 256, 1, 0), p
     ops = synth.make_inputs(cfg)
     g = run_gpu(ops, label="workload 5 saturation")
-    rng = np.random.Generator(np.random.PCG64(5))
-    rows = [0, 255, 256, cfg.M - 1]
-    cols = [0, 255, 256, cfg.N - 1]
-    ms = np.concatenate([np.repeat(rows, 512), np.tile(rng.integers(0, cfg.M, 512), 1)])
-    ns = np.concatenate([np.tile(rng.integers(0, cfg.N, 512), len(rows)),
-                         rng.integers(0, cfg.N, 512)])
-    ms = np.concatenate([ms, rng.integers(0, cfg.M, 512)])
-    ns = np.concatenate([ns, np.repeat(cols, 128)])
-    pb, pe, pm = o.gemm_points(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha,
-                               ms, ns)
-    r = compare(g[ms, ns], pb, pe, pm, ops.alpha)
-    say(f"workload 5 sampled: {r}")
+    sample = large_sample(cfg.M, cfg.N)
+    assert len(sample["tiles"]) == 9, sample["tiles"]   # 2048 tiles: 8 XCD ranges + the last
+    r = check_sample(o, ops, g, sample)
+    say(f"workload 5: rows {sample['rows']} cols {sample['cols']} tiles {sample['tiles']} "
+        f"+ {len(sample['points'][0])} random: {r} (oracle on {o.threads} threads, "
+        f"nproc {os.cpu_count()})")
+    assert r["n"] == 4 * cfg.N + 4 * cfg.M + 9 * 256 * 256 + 4096
     assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
-    # property at every element: finite, and not all zero
     gf = orc.bf16_bits_to_float(g)
     assert np.all(np.isfinite(gf)) and np.count_nonzero(g & 0x7FFF) > 0.99 * g.size
 
