@@ -38,8 +38,11 @@ ERR_ALLOC = 5
 ERR_CAPTURE = 6
 ERR_STATE = 7
 ERR_DEVICE_FLAGS = 8
+ERR_SCRATCH = 9
 
 FLAG_HANDOFF = 1
+NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_MAX_COUNTERS = 16384
 
 PATH_AUTO = 0
 PATH_TILE = 1
@@ -59,7 +62,7 @@ EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_p
            "nvfp4_sequence_add_quantize", "nvfp4_sequence_finalize", "nvfp4_sequence_launch",
            "nvfp4_sequence_destroy", "nvfp4_probe_empty", "nvfp4_probe_chase",
            "nvfp4_probe_mfma", "nvfp4_probe_read", "nvfp4_device_flags",
-           "nvfp4_debug_set_handoff_polls"]
+           "nvfp4_debug_set_handoff_polls", "nvfp4_gemm_noalloc", "nvfp4_noalloc_scratch_bytes"]
 
 
 class _PlanT(ctypes.Structure):
@@ -120,6 +123,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_device_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
         L.nvfp4_debug_set_handoff_polls.restype = ctypes.c_int
         L.nvfp4_debug_set_handoff_polls.argtypes = [ctypes.c_uint32]
+        L.nvfp4_gemm_noalloc.restype = ctypes.c_int
+        L.nvfp4_gemm_noalloc.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
+                                         _i64, _vp]
+        L.nvfp4_noalloc_scratch_bytes.restype = ctypes.c_int
+        L.nvfp4_noalloc_scratch_bytes.argtypes = [_i64, _i64, _i64,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
         L.nvfp4_grouped_gemm.restype = ctypes.c_int
         L.nvfp4_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float, _vp, _i64,
                                          _i64, _i64, _vp]
@@ -320,6 +329,40 @@ def gemm(a: PackedOperand, b: PackedOperand, alpha: float = 1.0, out=None,
     if st:
         raise Nvfp4Error(st, f"nvfp4_gemm(M={M}, N={N}, K={K})")
     return out
+
+
+def gemm_noalloc(a: PackedOperand, b: PackedOperand, alpha: float = 1.0, out=None, stream=None):
+    """C = alpha * (A . B^T) through nvfp4_gemm_noalloc: the plan and result
+    of gemm(), with the split-K workspace in the library's static device
+    array instead of an allocation (``out`` given: nothing is allocated by
+    this call).  Raises Nvfp4Error (status ERR_SCRATCH) for a shape whose
+    plan needs more scratch than the array holds."""
+    import torch
+    if a.K != b.K:
+        raise ValueError(f"K dimension mismatch: A has K={a.K}, B has K={b.K}")
+    M, N, K = a.rows, b.rows, a.K
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
+    a.check("a")
+    b.check("b")
+    st = lib().nvfp4_gemm_noalloc(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
+                                  b.scales.data_ptr(), float(alpha), out.data_ptr(), M, N, K,
+                                  _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_gemm_noalloc(M={M}, N={N}, K={K})")
+    return out
+
+
+def noalloc_scratch_bytes(M: int, N: int, K: int) -> tuple[int, bool]:
+    """(scratch bytes the shape's plan needs, whether nvfp4_gemm_noalloc
+    accepts it)."""
+    b = ctypes.c_size_t()
+    st = lib().nvfp4_noalloc_scratch_bytes(M, N, K, ctypes.byref(b))
+    if st not in (OK, ERR_SCRATCH):
+        raise Nvfp4Error(st, f"nvfp4_noalloc_scratch_bytes(M={M}, N={N}, K={K})")
+    return b.value, st == OK
 
 
 def device_flags() -> int:

@@ -14,7 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4.so")
 SOURCES = [os.path.join(CSRC, "nvfp4_api.cpp"), os.path.join(CSRC, "nvfp4_plan.cpp"),
            os.path.join(CSRC, "nvfp4_sequence.cpp"), os.path.join(CSRC, "nvfp4_kernels.hip"), os.path.join(CSRC, "nvfp4_grouped.hip"),
-           os.path.join(CSRC, "nvfp4_quantize.hip"), os.path.join(CSRC, "nvfp4_probe.hip")]
+           os.path.join(CSRC, "nvfp4_quantize.hip"), os.path.join(CSRC, "nvfp4_probe.hip"),
+           os.path.join(CSRC, "nvfp4_noalloc.hip")]
 # what the kernels and their launches are built from
 KERNEL_FILES = [os.path.join(CSRC, f) for f in ("nvfp4_kernels.hip", "nvfp4_grouped.hip",
                                                 "nvfp4_quantize.hip", "nvfp4_internal.h",

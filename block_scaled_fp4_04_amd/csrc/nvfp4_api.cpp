@@ -332,6 +332,7 @@ const char* nvfp4_status_string(int status) {
         case NVFP4_ERR_ALLOC: return "workspace allocation failed";
         case NVFP4_ERR_CAPTURE: return "workspace needed while the stream is being captured";
         case NVFP4_ERR_STATE: return "call not allowed in the object's current state";
+        case NVFP4_ERR_SCRATCH: return "the plan needs more split-K scratch than the static maximum";
         case NVFP4_ERR_DEVICE_FLAGS: return "a kernel raised a device error flag (see nvfp4_device_flags)";
         default: return "unknown status";
     }
@@ -403,7 +404,8 @@ int nvfp4_init(int device) {
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess) return NVFP4_ERR_HIP;
     if (device < 0 || device >= count) return NVFP4_ERR_INVALID_VALUE;
-    return check_device(device);
+    const int st = check_device(device);
+    return st != NVFP4_OK ? st : noalloc_setup(device);
 }
 
 void nvfp4_shutdown(void) {

@@ -119,6 +119,15 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);
 // tiles_m = ceil(M / 256) + groups row blocks.
 hipError_t launch_grouped_tile(const GemmArgs& a, hipStream_t stream);
 
+// Static split-K scratch of the allocation-free entry point
+// (nvfp4_gemm_noalloc): arrival counters first, then FP32 partial tiles.
+constexpr size_t kScratchCounters = 16384;
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr size_t kScratchPartialFloats = (kScratchBytes - kScratchCounters * 4) / 4;
+// Looks up the device address of the scratch array on `device` (made
+// current for the call) once; returns its status.
+int noalloc_setup(int device);
+
 // NVFP4 quantisation of fp32 rows into the packed operand layout.
 struct QuantArgs {
     const float* x;   // rows x K values, row stride ld elements

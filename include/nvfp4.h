@@ -55,7 +55,9 @@ typedef enum nvfp4_status {
     NVFP4_ERR_CAPTURE = 6,       /* a split-K workspace would have to be created or
                                     grown while the stream is being captured */
     NVFP4_ERR_STATE = 7,         /* call not allowed in the object's current state */
-    NVFP4_ERR_DEVICE_FLAGS = 8   /* nvfp4_device_flags: a kernel raised an error flag */
+    NVFP4_ERR_DEVICE_FLAGS = 8,  /* nvfp4_device_flags: a kernel raised an error flag */
+    NVFP4_ERR_SCRATCH = 9        /* nvfp4_gemm_noalloc: the shape's plan needs more
+                                    split-K scratch than the static maximum */
 } nvfp4_status;
 
 /* Device error flags (nvfp4_device_flags). */
@@ -334,6 +336,36 @@ int nvfp4_sequence_add_quantize(nvfp4_sequence_t seq, const float* x, int64_t ro
 int nvfp4_sequence_finalize(nvfp4_sequence_t seq);
 int nvfp4_sequence_launch(nvfp4_sequence_t seq, void* stream);
 int nvfp4_sequence_destroy(nvfp4_sequence_t seq);
+
+/* ---- allocation-free GEMM ------------------------------------------------
+ * For callers that cannot allocate device memory: code being captured into
+ * a graph, tight serving loops, harnesses that forbid allocation.
+ * nvfp4_gemm_noalloc is nvfp4_gemm (same arguments, plan, kernels and
+ * results, bit for bit) except that its split-K workspace is a static device
+ * array of NVFP4_NOALLOC_SCRATCH_BYTES per GPU (arrival counters first,
+ * NVFP4_NOALLOC_MAX_COUNTERS of them, then FP32 partial tiles), which each
+ * GPU the library runs on holds until the process ends.  It calls no
+ * allocation routine of HIP or any other library.  Its device address is
+ * looked up once per device, by nvfp4_init(device) or by the first call on
+ * the device; make that first call outside a graph capture if the runtime
+ * might refuse the lookup there.
+ * Every call on one GPU shares that GPU's array: calls that can overlap on
+ * one GPU (other streams, concurrent graph replays) race and give wrong
+ * results; order them.  A shape whose plan needs more scratch than the
+ * maximum is rejected with NVFP4_ERR_SCRATCH before anything is enqueued
+ * (nvfp4_noalloc_scratch_bytes tells in advance). */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define NVFP4_NOALLOC_MAX_COUNTERS 16384
+int nvfp4_gemm_noalloc(const void* a_packed, const void* a_scales, const void* b_packed,
+                       const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
+                       int64_t K, void* stream);
+
+/* Scratch nvfp4_gemm_noalloc needs for a shape: *bytes = 4 x the plan's
+ * counters + 4 x its FP32 partials (0 when the plan does not split K).
+ * Returns NVFP4_OK when that fits the static array, NVFP4_ERR_SCRATCH when
+ * nvfp4_gemm_noalloc would reject the shape, and nvfp4_gemm's size errors.
+ * Host-only, no device call. */
+int nvfp4_noalloc_scratch_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
 /* ---- measurement aids (not part of the GEMM path) ------------------------
  * The floors that bound decode-sized calls: what a kernel that does nothing

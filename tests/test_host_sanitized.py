@@ -41,11 +41,15 @@ size_t skinny_counters(const GemmArgs&) { return 0; }
 size_t wsplit_partial_floats(int, const GemmArgs&) { return 0; }
 int resident_tiles(int, int) { return 0; }
 hipError_t take_device_flags(uint32_t* flags) { *flags = 0; return hipErrorInvalidValue; }
+int noalloc_setup(int) { return 4; }
 }
 extern "C" int nvfp4_probe_empty(int64_t, int64_t, void*) { return 1; }
 extern "C" int nvfp4_probe_chase(const uint32_t*, int64_t, int64_t, uint32_t*, void*) { return 1; }
 extern "C" int nvfp4_probe_mfma(int64_t, int64_t, float*, void*) { return 1; }
 extern "C" int nvfp4_probe_read(const void*, int64_t, int64_t, uint32_t*, void*) { return 1; }
+extern "C" int nvfp4_gemm_noalloc(const void*, const void*, const void*, const void*, float, void*,
+                                  int64_t, int64_t, int64_t, void*) { return 1; }
+extern "C" int nvfp4_noalloc_scratch_bytes(int64_t, int64_t, int64_t, size_t*) { return 1; }
 """
 
 CHILD = r"""
