@@ -67,6 +67,8 @@ int check_device(int device) {
 struct Workspace {
     float* partials = nullptr;
     size_t partial_floats = 0;
+    uint64_t* flagged = nullptr;
+    size_t flagged_words = 0;
     uint32_t* counters = nullptr;
     size_t counter_count = 0;
     // Buffers replaced by larger ones.  A graph captured on the stream may
@@ -84,37 +86,48 @@ bool capturing(void* stream) {
            cs != hipStreamCaptureStatusNone;
 }
 
-// Makes sure the workspace of (device, stream) can hold the request.  Growing
-// it allocates larger buffers and zero-fills the new counters (synchronously,
-// so they are zero before any kernel uses them); the old buffers are retired,
-// not freed (see Workspace::retired).  This happens only when a larger shape
-// is seen for the first time on that stream, and never while the stream is
-// being captured into a graph (NVFP4_ERR_CAPTURE: allocation and the
-// synchronous fill are not allowed there).
-int get_workspace(int device, void* stream, size_t floats, size_t counters, Workspace** out) {
+// Replaces *buf (holding *have elements) by an allocation of `need`
+// elements if it is smaller, zero-filled on `stream` (so the fill is ordered
+// before the kernels the caller enqueues next on that stream); the old
+// buffer is retired.
+template <typename T>
+int grow(T** buf, size_t* have, size_t need, std::vector<void*>& retired, void* stream) {
+    if (need <= *have) return NVFP4_OK;
+    T* p = nullptr;
+    if (hipMalloc(&p, need * sizeof(T)) != hipSuccess) return NVFP4_ERR_ALLOC;
+    if (hipMemsetAsync(p, 0, need * sizeof(T), static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipFree(p);
+        return NVFP4_ERR_HIP;
+    }
+    if (*buf) retired.push_back(*buf);
+    *buf = p;
+    *have = need;
+    return NVFP4_OK;
+}
+
+// Makes sure the workspace of (device, stream) can hold the job's needs.
+// Growing it allocates larger buffers and zero-fills them on the stream
+// itself, ahead of the job's kernels (counters and flagged words must be
+// clear before any kernel uses them; a fill on another stream could land
+// after a kernel had published a word); the old buffers are retired, not
+// freed (see Workspace::retired).  This happens only when a larger shape is
+// seen for the first time on that stream, and never while the stream is
+// being captured into a graph (NVFP4_ERR_CAPTURE: allocation and fills are
+// not allowed there).
+int get_workspace(int device, void* stream, const Job& job, WorkspacePtrs* out) {
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace& ws = g_ws[{device, stream}];
-    if ((floats > ws.partial_floats || counters > ws.counter_count) && capturing(stream))
+    if ((job.floats > ws.partial_floats || job.flagged > ws.flagged_words ||
+         job.counters > ws.counter_count) &&
+        capturing(stream))
         return NVFP4_ERR_CAPTURE;
-    if (floats > ws.partial_floats) {
-        float* p = nullptr;
-        if (hipMalloc(&p, floats * sizeof(float)) != hipSuccess) return NVFP4_ERR_ALLOC;
-        if (ws.partials) ws.retired.push_back(ws.partials);
-        ws.partials = p;
-        ws.partial_floats = floats;
-    }
-    if (counters > ws.counter_count) {
-        uint32_t* c = nullptr;
-        if (hipMalloc(&c, counters * sizeof(uint32_t)) != hipSuccess) return NVFP4_ERR_ALLOC;
-        if (hipMemset(c, 0, counters * sizeof(uint32_t)) != hipSuccess) {
-            (void)hipFree(c);
-            return NVFP4_ERR_HIP;
-        }
-        if (ws.counters) ws.retired.push_back(ws.counters);
-        ws.counters = c;
-        ws.counter_count = counters;
-    }
-    *out = &ws;
+    int st = grow(&ws.partials, &ws.partial_floats, job.floats, ws.retired, stream);
+    if (st == NVFP4_OK) st = grow(&ws.flagged, &ws.flagged_words, job.flagged, ws.retired, stream);
+    if (st == NVFP4_OK) st = grow(&ws.counters, &ws.counter_count, job.counters, ws.retired, stream);
+    if (st != NVFP4_OK) return st;
+    out->partials = ws.partials;
+    out->flagged = ws.flagged;
+    out->counters = ws.counters;
     return NVFP4_OK;
 }
 
@@ -123,16 +136,12 @@ int run_job(const Job& job, void* stream) {
     int device = 0;
     const int dst = current_device(&device);
     if (dst != NVFP4_OK || job.empty) return dst;
-    float* partials = nullptr;
-    uint32_t* counters = nullptr;
-    if (job.floats || job.counters) {
-        Workspace* ws = nullptr;
-        const int wst = get_workspace(device, stream, job.floats, job.counters, &ws);
+    WorkspacePtrs ws;
+    if (job.floats || job.flagged || job.counters) {
+        const int wst = get_workspace(device, stream, job, &ws);
         if (wst != NVFP4_OK) return wst;
-        partials = ws->partials;
-        counters = ws->counters;
     }
-    const hipError_t e = launch_job(job, device, partials, counters, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_job(job, device, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
@@ -166,8 +175,8 @@ int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packe
     Plan& plan = job->plan;
     const int pst = make_plan(M, N, K, path, tile, split_k, &plan);
     if (pst != NVFP4_OK) return pst;
-    if (plan.path == NVFP4_PATH_TILE) {
-        // the tile kernel addresses each packed operand with 32-bit offsets
+    if (plan.path == NVFP4_PATH_TILE || plan.path == NVFP4_PATH_WSPLIT) {
+        // the tile and wsplit kernels address each packed operand with 32-bit offsets
         const int64_t P = num_panels(K);
         const int64_t limit = (int64_t)1 << 31;
         if (P * round_up(M, kRowPad) * kPanelCodeBytes >= limit ||
@@ -194,10 +203,10 @@ int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packe
     a.tail_tiles = plan.tail_tiles;
     a.tail_split = plan.tail_split;
     a.handoff_polls = g_handoff_polls.load(std::memory_order_relaxed);
-    job->floats = plan.path == NVFP4_PATH_GEMV     ? 0
-                  : plan.path == NVFP4_PATH_SKINNY ? skinny_partial_floats(a)
+    job->floats = plan.path == NVFP4_PATH_TILE     ? tile_partial_floats(plan.cfg, a)
                   : plan.path == NVFP4_PATH_WSPLIT ? wsplit_partial_floats(plan.cfg, a)
-                                                   : tile_partial_floats(plan.cfg, a);
+                                                   : 0;
+    job->flagged = plan.path == NVFP4_PATH_SKINNY ? skinny_flagged_words(a) : 0;
     job->counters = plan.path == NVFP4_PATH_GEMV     ? 0
                     : plan.path == NVFP4_PATH_SKINNY ? skinny_counters(a)
                                                      : tile_counters(plan.cfg, a);
@@ -302,15 +311,15 @@ int prepare_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* 
     return NVFP4_OK;
 }
 
-hipError_t launch_job(const Job& job, int device, float* partials, uint32_t* counters,
-                      hipStream_t s) {
+hipError_t launch_job(const Job& job, int device, const WorkspacePtrs& ws, hipStream_t s) {
     if (job.empty) return hipSuccess;
     if (job.kind == JOB_GROUPED) return launch_grouped(job.grouped, s);
     if (job.kind == JOB_GROUPED_TILE) return launch_grouped_tile(job.gemm, s);
     if (job.kind == JOB_QUANTIZE) return launch_quantize(job.quant, s);
     GemmArgs a = job.gemm;
-    a.partials = partials;
-    a.counters = counters;
+    a.partials = ws.partials;
+    a.flagged = ws.flagged;
+    a.counters = ws.counters;
     const Plan& plan = job.plan;
     return plan.path == NVFP4_PATH_GEMV     ? launch_gemv(a, s)
            : plan.path == NVFP4_PATH_SKINNY ? launch_skinny(a, s)
@@ -415,6 +424,7 @@ void nvfp4_shutdown(void) {
     for (auto& kv : g_ws) {
         (void)hipSetDevice(kv.first.first);
         if (kv.second.partials) (void)hipFree(kv.second.partials);
+        if (kv.second.flagged) (void)hipFree(kv.second.flagged);
         if (kv.second.counters) (void)hipFree(kv.second.counters);
         for (void* p : kv.second.retired) (void)hipFree(p);
     }

@@ -100,6 +100,54 @@ __device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
 __device__ __forceinline__ void reset_counter(uint32_t* counter) {
     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Takes a ticket without waiting for this wave's earlier stores (for
+// partials published with flags, which the reader checks itself).
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* counter) {
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Flagged partial sums: each FP32 value travels in one 64-bit word with a
+// ready flag in its upper half, written by a single 64-bit store, so a
+// reader that sees the flag also sees the value -- the writer need not wait
+// for its stores before it takes its ticket.  The reader clears every word
+// it consumed (flag 0) before the kernel ends, so the next call starts from
+// cleared words.
+constexpr uint64_t kReady = 1ull << 32;
+__device__ __forceinline__ void publish_flagged(uint64_t* p, float v) {
+    __hip_atomic_store(p, (uint64_t)__builtin_bit_cast(uint32_t, v) | kReady, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t fetch_flagged(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void clear_flagged(uint64_t* p) {
+    __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float flagged_value(uint64_t w) {
+    return __builtin_bit_cast(float, (uint32_t)w);
+}
+
+// Reads N flagged words at p[k * stride] (lane-relative) once they are all
+// ready: polls at most `polls` times (each about 128 cycles apart); returns
+// false, with whatever was read, if some word was still not ready then.
+template <int N>
+__device__ __forceinline__ bool gather_flagged(const uint64_t* p, int stride, uint32_t polls,
+                                               float (&v)[N]) {
+    uint64_t w[N];
+    for (uint32_t it = 0;; ++it) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) w[k] = fetch_flagged(p + k * stride);
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < N; ++k) ok = ok && (w[k] >> 32) != 0;
+        if (__all(ok) || it + 1 >= polls) {
+#pragma unroll
+            for (int k = 0; k < N; ++k) v[k] = flagged_value(w[k]);
+            return __all(ok);
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
 
 // Wait until at most N vector-memory instructions of this wave are in flight
 // (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
@@ -132,6 +180,14 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16-byte buffer load into registers at voff + soff inside the buffer
+// (bytes past its end read as zeros).
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return uint4{t[0], t[1], t[2], t[3]};
 }
 
 // Direct HBM -> LDS copies (buffer_load ... lds): every lane fetches 16 (or

@@ -17,7 +17,8 @@ struct Job {
     int kind = JOB_GEMM;
     Plan plan{};                 // JOB_GEMM (JOB_GROUPED_TILE: plan.cfg)
     GemmArgs gemm{};             // JOB_GEMM, JOB_GROUPED_TILE (workspace pointers set at launch)
-    size_t floats = 0;           // split-K partial floats the job needs
+    size_t floats = 0;           // split-K partial floats the job needs (tile, wsplit)
+    size_t flagged = 0;          // flagged 64-bit partial words the job needs (skinny)
     size_t counters = 0;         // split-K arrival counters the job needs
     GroupedArgs grouped{};       // JOB_GROUPED
     QuantArgs quant{};           // JOB_QUANTIZE
@@ -38,9 +39,17 @@ int prepare_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* 
 // The current device, checked to be a gfx950 GPU (status).
 int current_device(int* device);
 
+// The split-K workspace of a launch.  Counters and flagged words are zero
+// between calls (every kernel that uses them leaves them so); the FP32
+// partials need no initial value.
+struct WorkspacePtrs {
+    float* partials = nullptr;
+    uint64_t* flagged = nullptr;
+    uint32_t* counters = nullptr;
+};
+
 // Enqueues a prepared job on `stream`, with the split-K workspace given
-// (null when the job needs none).
-hipError_t launch_job(const Job& job, int device, float* partials, uint32_t* counters,
-                      hipStream_t stream);
+// (null pointers when the job needs none).
+hipError_t launch_job(const Job& job, int device, const WorkspacePtrs& ws, hipStream_t stream);
 
 }  // namespace nvfp4

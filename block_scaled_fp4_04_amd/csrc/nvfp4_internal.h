@@ -25,7 +25,8 @@ struct GemmArgs {
     const uint8_t* b_codes;   // [P][Np][32]
     const uint8_t* b_scales;  // [P][Np][4]
     uint16_t* out;            // [M][N] bfloat16 bits
-    float* partials;          // split-K partial sums (workspace), or null
+    float* partials;          // split-K partial sums (tile, wsplit kernels; workspace), or null
+    uint64_t* flagged;        // split-K partial sums with ready flags (skinny kernel), or null
     uint32_t* counters;       // split-K arrival counters (workspace), or null
     float alpha;
     int M, N;                 // logical output size
@@ -69,10 +70,11 @@ inline TileShape tile_shape(int cfg) {
 }
 
 
-// Workspace needs (bytes of partials, number of counters) of a launch.
+// Workspace needs of a launch: FP32 partials, flagged 64-bit partial words,
+// arrival counters.
 size_t tile_partial_floats(int cfg, const GemmArgs& a);
 size_t tile_counters(int cfg, const GemmArgs& a);
-size_t skinny_partial_floats(const GemmArgs& a);
+size_t skinny_flagged_words(const GemmArgs& a);
 size_t skinny_counters(const GemmArgs& a);
 
 // Mid-size kernel configurations (waves split K inside a workgroup).
@@ -120,10 +122,13 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);
 hipError_t launch_grouped_tile(const GemmArgs& a, hipStream_t stream);
 
 // Static split-K scratch of the allocation-free entry point
-// (nvfp4_gemm_noalloc): arrival counters first, then FP32 partial tiles.
+// (nvfp4_gemm_noalloc): arrival counters, then flagged partial words, then
+// FP32 partial tiles.
 constexpr size_t kScratchCounters = 16384;
 constexpr size_t kScratchBytes = (size_t)32 << 20;
-constexpr size_t kScratchPartialFloats = (kScratchBytes - kScratchCounters * 4) / 4;
+constexpr size_t kScratchFlaggedWords = (size_t)1 << 20;
+constexpr size_t kScratchPartialFloats =
+    (kScratchBytes - kScratchCounters * 4 - kScratchFlaggedWords * 8) / 4;
 // Looks up the device address of the scratch array on `device` (made
 // current for the call) once; returns its status.
 int noalloc_setup(int device);

@@ -718,7 +718,8 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
     skinny_kernel(const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
                   const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
                   int Np, int Mp, int P, int split_k, uint16_t* __restrict__ out,
-                  float* partials, uint32_t* counters, float alpha, int M, int N) {
+                  uint64_t* flagged, uint32_t* counters, float alpha, int M, int N,
+                  uint32_t polls) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -798,28 +799,42 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
     for (int w = 1; w < WAVES; ++w) sum += part[w];
 
     if (S > 1) {
-        float* mine = partials + (((int64_t)g * S + z) * MB + blk) * 256;
+        // Split K across workgroups (S <= WAVES): every workgroup publishes
+        // its blocks as flagged words and takes a ticket without waiting for
+        // the stores.  In the last arrival, wave w fetches split w's blocks
+        // (all in flight at once, waiting only for their flags: the stores
+        // belong to workgroups that already took their tickets) into the
+        // LDS partial buffer -- the reducer waves put their own sums in slot
+        // z -- and then clears that split's words; the reducer waves add the
+        // S slots in split order.  A wave whose fetch runs past `polls`
+        // adds what it has and raises the device's hand-off flag.
+        uint64_t* slots = flagged + (int64_t)g * S * MB * 256;
         if (reducer) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) publish(mine + v * 64 + lane, sum[v]);
+            for (int v = 0; v < 4; ++v)
+                publish_flagged(slots + ((int64_t)z * MB + blk) * 256 + v * 64 + lane, sum[v]);
         }
-        // one arrival per workgroup, after every block's partials are out
         __shared__ uint32_t s_old;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) s_old = arrive(counters + g);
-        __syncthreads();
+        if (tid == 0) s_old = take_ticket(counters + g);
+        __syncthreads();  // (also: every wave is done reading red)
         if (s_old != (uint32_t)(S - 1)) return;       // (uniform in the workgroup)
         if (tid == 0) reset_counter(counters + g);  // all splits arrived
-        if (!reducer) return;
-        f4v t = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int zz = 0; zz < S; ++zz) {
-            const float* pz = partials + (((int64_t)g * S + zz) * MB + blk) * 256;
-            f4v p;
+        if (wave < S) {
+            uint64_t* mine = slots + (int64_t)wave * MB * 256 + lane;
+            if (wave != z) {
+                float p[4 * MB];
+                if (!gather_flagged<4 * MB>(mine, 64, polls, p) && lane == 0) raise_flag(kFlagHandoff);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) p[v] = fetch(pz + v * 64 + lane);
-            t += p;
+                for (int b = 0; b < MB; ++b) red[wave][b][lane] = f4v{p[4 * b], p[4 * b + 1], p[4 * b + 2], p[4 * b + 3]};
+            }
+#pragma unroll
+            for (int k = 0; k < 4 * MB; ++k) clear_flagged(mine + k * 64);
         }
+        if (reducer) red[z][blk][lane] = sum;
+        __syncthreads();
+        if (!reducer) return;
+        f4v t = red[0][blk][lane];
+        for (int zz = 1; zz < S; ++zz) t += red[zz][blk][lane];
         sum = t;
     }
     if (!reducer) return;
@@ -846,9 +861,9 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
 // range, so each element is decoded exactly once per tile and the waves
 // share nothing until the end: no LDS staging and no barriers in the main
 // loop.  Lane l of a 32-row block reads row l % 32, half l / 32 of a panel
-// (16 bytes of codes, 2 bytes of scales) straight from HBM -- a wave's
-// reads of one block are 1 KB contiguous -- with DEPTH panels of loads in
-// flight.  At the end the wave tiles are added in LDS in wave order, then
+// (16 bytes of codes, 2 bytes of scales) straight from HBM into registers
+// -- a wave's reads of one block are 1 KB contiguous -- with DEPTH panels of
+// loads in flight; the panel's offset is the loads' scalar offset.  At the end the wave tiles are added in LDS in wave order, then
 // (split_k > 1) across workgroups by the last arrival in split order.
 // ---------------------------------------------------------------------------
 // (Plain arguments, operands and geometry first, so that those can be
@@ -868,7 +883,7 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: scalar load offsets)
     const int q = lane & 31, h = lane >> 5;
 
     const int S = SPLIT ? split_k : 1;
@@ -886,13 +901,28 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(
     // this wave's panels: p0 + wave, p0 + wave + WAVES, ...
     const int count = (p1 - p0 > wave) ? (p1 - p0 - wave + WAVES - 1) / WAVES : 0;
 
-    // lane byte offsets of its rows inside one panel (rows clamped to the
-    // padded operand; their results are not stored)
-    int64_t a_off[MI], b_off[NI];
+    // Lane byte offsets inside one panel: the lane's row (clamped to the
+    // padded operand; results of clamped rows are not stored), half h of its
+    // 32 code bytes and of its 4 scale bytes.  The panel's own offset is
+    // wave-uniform and goes into the loads' scalar offset, so addresses cost
+    // no vector instructions.
+    uint32_t a_code[MI], a_sc[MI], b_code[NI], b_sc[NI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) a_off[i] = min(m0 + i * 32 + q, Mp - 1);
+    for (int i = 0; i < MI; ++i) {
+        const uint32_t r = (uint32_t)min(m0 + i * 32 + q, Mp - 1);
+        a_code[i] = r * 32u + (uint32_t)h * 16u;
+        a_sc[i] = r * 4u + (uint32_t)h * 2u;
+    }
 #pragma unroll
-    for (int j = 0; j < NI; ++j) b_off[j] = min(n0 + j * 32 + q, Np - 1);
+    for (int j = 0; j < NI; ++j) {
+        const uint32_t r = (uint32_t)min(n0 + j * 32 + q, Np - 1);
+        b_code[j] = r * 32u + (uint32_t)h * 16u;
+        b_sc[j] = r * 4u + (uint32_t)h * 2u;
+    }
+    const __amdgpu_buffer_rsrc_t rac = make_rsrc(a_codes, (uint32_t)P * Mp * 32u);
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (uint32_t)P * Mp * 4u);
+    const __amdgpu_buffer_rsrc_t rbc = make_rsrc(b_codes, (uint32_t)P * Np * 32u);
+    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(b_scales, (uint32_t)P * Np * 4u);
 
     struct Regs {
         uint4 ca[MI], cb[NI];
@@ -903,18 +933,17 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(
     // slot zero scales, so the compiler's wait counts stay exact (a branch
     // around the loads made every ring slot wait for all of them).
     auto load = [&](int k, Regs& r) {
-        const int64_t panel = p0 + wave + (int64_t)min(k, count - 1) * WAVES;
+        const uint32_t pnl = (uint32_t)(p0 + wave + min(k, count - 1) * WAVES);
+        const uint32_t sa_off = pnl * (uint32_t)Mp, sb_off = pnl * (uint32_t)Np;  // rows before
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const int64_t row = panel * Mp + a_off[i];
-            r.ca[i] = *reinterpret_cast<const uint4*>(a_codes + row * 32 + h * 16);
-            r.sa[i] = *reinterpret_cast<const uint16_t*>(a_scales + row * 4 + h * 2);
+            r.ca[i] = load16(rac, a_code[i], sa_off * 32u);
+            r.sa[i] = __builtin_amdgcn_raw_buffer_load_b16(ras, a_sc[i], sa_off * 4u, 0);
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int64_t row = panel * Np + b_off[j];
-            r.cb[j] = *reinterpret_cast<const uint4*>(b_codes + row * 32 + h * 16);
-            r.sb[j] = *reinterpret_cast<const uint16_t*>(b_scales + row * 4 + h * 2);
+            r.cb[j] = load16(rbc, b_code[j], sb_off * 32u);
+            r.sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rbs, b_sc[j], sb_off * 4u, 0);
         }
     };
 
@@ -987,16 +1016,15 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(
             for (int v = 0; v < 16; ++v) red[wave][(i * NI + j) * 16 + v][lane] = acc[i][j][v];
     __syncthreads();
     constexpr int IDX = MI * NI * 16;  // accumulator slots per lane
-    constexpr int PER = (IDX + WAVES - 1) / WAVES;
+    static_assert(IDX % WAVES == 0, "every wave adds the same number of slots");
+    constexpr int PER = IDX / WAVES;   // slots wave w adds: w, w + WAVES, ...
     float sum[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int idx = wave + u * WAVES;
         float x = 0.0f;
-        if (idx < IDX) {
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) x += red[w][idx][lane];
-        }
+        for (int w = 0; w < WAVES; ++w) x += red[w][idx][lane];
         sum[u] = x;
     }
 
@@ -1005,10 +1033,7 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(
         // last arrival adds the S partial tiles in split order
         float* mine = partials + ((int64_t)t * S + z) * (BM * BN);
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int idx = wave + u * WAVES;
-            if (idx < IDX) publish(mine + idx * 64 + lane, sum[u]);
-        }
+        for (int u = 0; u < PER; ++u) publish(mine + (wave + u * WAVES) * 64 + lane, sum[u]);
         __shared__ int s_last;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -1023,11 +1048,12 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(
 #pragma unroll
         for (int u = 0; u < PER; ++u) sum[u] = 0.0f;
         for (int zz = 0; zz < S; ++zz) {  // one batch of independent loads per split
+            float part[PER];
 #pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int idx = wave + u * WAVES;
-                if (idx < IDX) sum[u] += fetch(all + (int64_t)zz * (BM * BN) + idx * 64 + lane);
-            }
+            for (int u = 0; u < PER; ++u)
+                part[u] = fetch(all + (int64_t)zz * (BM * BN) + (wave + u * WAVES) * 64 + lane);
+#pragma unroll
+            for (int u = 0; u < PER; ++u) sum[u] += part[u];
         }
     }
 
@@ -1036,7 +1062,6 @@ __global__ void __launch_bounds__(WAVES * 64) wsplit_kernel(
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int idx = wave + u * WAVES;
-        if (idx >= IDX) continue;
         const int v = idx & 15, ij = idx >> 4;
         const int i = ij / NI, j = ij % NI;
         const int row = m0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -1219,7 +1244,7 @@ size_t tile_counters(int cfg, const GemmArgs& a) {
     if (a.tail_tiles > 0) return (size_t)a.tail_tiles;
     return 0;
 }
-size_t skinny_partial_floats(const GemmArgs& a) {
+size_t skinny_flagged_words(const GemmArgs& a) {
     const int mb = (a.M + 15) / 16;
     return a.split_k <= 1 ? 0 : (size_t)(a.Np / 16) * a.split_k * mb * 256;
 }
@@ -1375,8 +1400,8 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
 #define NVFP4_SKINNY_CASE(MB, U) \
         case MB * 8 + U: hipLaunchKernelGGL((skinny_kernel<kSkinnyWaves, MB, U>), grid, block, 0, stream, \
                                             a.b_codes, a.b_scales, a.a_codes, a.a_scales, a.Np, a.Mp, \
-                                            a.P, a.split_k, a.out, a.partials, a.counters, a.alpha, a.M, \
-                                            a.N); break;
+                                            a.P, a.split_k, a.out, a.flagged, a.counters, a.alpha, a.M, \
+                                            a.N, a.handoff_polls); break;
         NVFP4_SKINNY_CASE(1, 1) NVFP4_SKINNY_CASE(1, 2) NVFP4_SKINNY_CASE(1, 3) NVFP4_SKINNY_CASE(1, 4)
         NVFP4_SKINNY_CASE(2, 1) NVFP4_SKINNY_CASE(2, 2) NVFP4_SKINNY_CASE(2, 4)
         NVFP4_SKINNY_CASE(3, 1) NVFP4_SKINNY_CASE(3, 2)

@@ -3,18 +3,20 @@
 // device memory: code under graph capture, tight serving loops, harnesses
 // that forbid it.
 //
-// The split-K workspace (arrival counters, then FP32 partial tiles) is a
-// file-scope device array of fixed size instead of a library allocation.
+// The split-K workspace (arrival counters, then flagged partial words, then
+// FP32 partial tiles) is a file-scope device array of fixed size instead of
+// a library allocation.
 // Each device holds its own copy of the array, at its own address, for the
 // life of the process.  In host code the array's name stands for a host-side
 // shadow, not for device memory, so the host never passes it to a kernel:
 // the device address is looked up once per device with hipGetSymbolAddress
 // (with that device current) and that address is what the kernels receive.
 //
-// The counters are zero when the code object is loaded, and every kernel
-// that uses a counter leaves it at zero again when it finishes (the last
-// arrival resets it; a two-way hand-off that gives up takes its increments
-// back), so every call finds them at zero without a fill.
+// The array is zero when the code object is loaded, and every kernel that
+// uses a counter or a flagged word leaves it at zero again when it finishes
+// (the last arrival resets its counter and clears the words it read; a
+// two-way hand-off that gives up takes its increments back), so every call
+// finds them at zero without a fill.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -53,6 +55,12 @@ int scratch_of(int device, uint8_t** ptr) {
     return NVFP4_OK;
 }
 
+// Whether the array holds what a job's plan needs.
+bool fits(const Job& job) {
+    return job.counters <= kScratchCounters && job.flagged <= kScratchFlaggedWords &&
+           job.floats <= kScratchPartialFloats;
+}
+
 }  // namespace
 
 namespace nvfp4 {
@@ -74,9 +82,9 @@ int nvfp4_noalloc_scratch_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) 
     const int st = prepare_gemm(p, p, p, p, 1.0f, const_cast<void*>(p), M, N, K, NVFP4_PATH_AUTO,
                                 0, 0, &job);
     if (st != NVFP4_OK) return st;
-    *bytes = job.counters * sizeof(uint32_t) + job.floats * sizeof(float);
-    return job.counters > kScratchCounters || job.floats > kScratchPartialFloats ? NVFP4_ERR_SCRATCH
-                                                                                 : NVFP4_OK;
+    *bytes = job.counters * sizeof(uint32_t) + job.flagged * sizeof(uint64_t) +
+             job.floats * sizeof(float);
+    return fits(job) ? NVFP4_OK : NVFP4_ERR_SCRATCH;
 }
 
 int nvfp4_gemm_noalloc(const void* a_packed, const void* a_scales, const void* b_packed,
@@ -86,22 +94,21 @@ int nvfp4_gemm_noalloc(const void* a_packed, const void* a_scales, const void* b
     int st = prepare_gemm(a_packed, a_scales, b_packed, b_scales, alpha, out, M, N, K,
                           NVFP4_PATH_AUTO, 0, 0, &job);
     if (st != NVFP4_OK) return st;
-    if (job.counters > kScratchCounters || job.floats > kScratchPartialFloats)
-        return NVFP4_ERR_SCRATCH;
+    if (!fits(job)) return NVFP4_ERR_SCRATCH;
     int device = 0;
     st = current_device(&device);
     if (st != NVFP4_OK) return st;
-    float* partials = nullptr;
-    uint32_t* counters = nullptr;
-    if (job.floats || job.counters) {
+    WorkspacePtrs ws;
+    if (job.floats || job.flagged || job.counters) {
         uint8_t* base = nullptr;
         st = scratch_of(device, &base);
         if (st != NVFP4_OK) return st;
-        counters = reinterpret_cast<uint32_t*>(base);
-        partials = reinterpret_cast<float*>(base + kScratchCounters * sizeof(uint32_t));
+        ws.counters = reinterpret_cast<uint32_t*>(base);
+        ws.flagged = reinterpret_cast<uint64_t*>(base + kScratchCounters * sizeof(uint32_t));
+        ws.partials = reinterpret_cast<float*>(base + kScratchCounters * sizeof(uint32_t) +
+                                               kScratchFlaggedWords * sizeof(uint64_t));
     }
-    const hipError_t e =
-        launch_job(job, device, partials, counters, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_job(job, device, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

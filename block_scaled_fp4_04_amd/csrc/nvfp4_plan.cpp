@@ -310,20 +310,31 @@ bool parse_entry(const JValue& e, int64_t* M, int64_t* N, int64_t* K, Choice* c)
 
 void plan_skinny(int64_t M, int64_t N, int steps, int split_req, Plan* p) {
     // One workgroup of kSkinnyWaves waves per 16 output columns covers the
-    // whole K range: the split-K hand-off costs more than it saves once
-    // there are 8 or more column groups (measured at 1x768x6144 and
-    // 16x256x6144).  Fewer groups split K (each wave keeps at least one
-    // 128-element work unit); with three or four blocks of 16 rows of A,
-    // two K slices (measured at 64 x 256..2048 x 6144).
+    // whole K range when A has one block of 16 rows: the split-K hand-off
+    // costs more than it saves once there are 8 or more column groups
+    // (measured at 1x768x6144 and 16x256x6144); fewer groups split K (each
+    // wave keeping at least one 128-element work unit).  With two to four
+    // row blocks every workgroup decodes 2-4 fragments of A per unit, and
+    // for up to 64 column groups K is split 3 ways (two blocks) or 4 ways
+    // (three or four): 32 x 256..768 x 6144 6.3 -> 5.3-5.6 us, 64 x
+    // 256..768 x 6144 7.6-7.8 -> 6.1-6.6 us; with more groups, two K slices
+    // from three blocks on (64 x 2048 x 6144).
     const int64_t groups = round_up(N, kRowPad) / 16;
     int s = split_req;
     if (s <= 0) {
-        s = (int)((8 + groups - 1) / groups);
-        if (M > 32 && s < 2) s = 2;
-        const int cap = steps / kSkinnyWaves;
-        if (s > cap) s = cap;
+        if (M > 16 && groups <= 64) {
+            s = M <= 32 ? 3 : 4;
+            const int cap = steps / 4;  // at least four K steps per workgroup
+            if (s > cap) s = cap;
+        } else {
+            s = (int)((8 + groups - 1) / groups);
+            if (M > 32 && s < 2) s = 2;
+            const int cap = steps / kSkinnyWaves;
+            if (s > cap) s = cap;
+        }
     }
     if (s > steps) s = steps;
+    if (s > kSkinnyWaves) s = kSkinnyWaves;  // the last arrival fetches one split per wave
     p->split_k = s < 1 ? 1 : s;
     p->tiles_m = 1;
     p->tiles_n = (int)groups;

@@ -7,9 +7,9 @@
 // Impact": graphs to cut launch overhead for small GEMMs).  A sequence keeps
 // the validated, planned calls; finalize captures them, in order, on a
 // private stream into a graph that owns nothing but kernel nodes (the
-// workspace's counters are zeroed once with a synchronous fill before the
-// capture and reset themselves in the kernels, so no memset node is ever
-// recorded), and launch replays that graph.
+// workspace is zeroed once with a synchronous fill before the capture; the
+// kernels leave counters and ready flags clear again, so no memset node is
+// ever recorded), and launch replays that graph.
 #include <hip/hip_runtime.h>
 
 #include <new>
@@ -24,8 +24,7 @@ struct nvfp4_sequence {
     std::vector<Job> jobs;
     bool finalized = false;
     int device = -1;
-    float* partials = nullptr;
-    uint32_t* counters = nullptr;
+    WorkspacePtrs ws;   // the sequence's own split-K workspace
     hipGraphExec_t exec = nullptr;
 };
 
@@ -39,11 +38,11 @@ int add_job(nvfp4_sequence* seq, int status, const Job& job) {
 
 void release(nvfp4_sequence* seq) {
     if (seq->exec) (void)hipGraphExecDestroy(seq->exec);
-    if (seq->partials) (void)hipFree(seq->partials);
-    if (seq->counters) (void)hipFree(seq->counters);
+    if (seq->ws.partials) (void)hipFree(seq->ws.partials);
+    if (seq->ws.flagged) (void)hipFree(seq->ws.flagged);
+    if (seq->ws.counters) (void)hipFree(seq->ws.counters);
     seq->exec = nullptr;
-    seq->partials = nullptr;
-    seq->counters = nullptr;
+    seq->ws = WorkspacePtrs{};
 }
 
 // Captures the jobs on a private stream and instantiates the graph.
@@ -56,9 +55,7 @@ int capture(nvfp4_sequence* seq) {
         st = NVFP4_ERR_HIP;
     } else {
         for (const Job& job : seq->jobs) {
-            const bool ws = job.floats || job.counters;
-            if (launch_job(job, seq->device, ws ? seq->partials : nullptr,
-                           ws ? seq->counters : nullptr, cs) != hipSuccess) {
+            if (launch_job(job, seq->device, seq->ws, cs) != hipSuccess) {
                 st = NVFP4_ERR_HIP;
                 break;
             }
@@ -127,28 +124,31 @@ int nvfp4_sequence_finalize(nvfp4_sequence_t seq) {
     if (st != NVFP4_OK) return st;
     seq->device = device;
     // one workspace serves every call: they run one after another
-    size_t floats = 0, counters = 0;
+    size_t floats = 0, flagged = 0, counters = 0;
     for (const Job& job : seq->jobs) {
         floats = job.floats > floats ? job.floats : floats;
+        flagged = job.flagged > flagged ? job.flagged : flagged;
         counters = job.counters > counters ? job.counters : counters;
         // resolve every device query the launch makes before the capture
         if (job.kind == JOB_GEMM && job.plan.path == NVFP4_PATH_TILE &&
             resident_tiles(job.plan.cfg, device) <= 0)
             return NVFP4_ERR_HIP;
     }
-    if (floats && hipMalloc(&seq->partials, floats * sizeof(float)) != hipSuccess) {
+    // zero-filled once, synchronously: counters and flagged words start clear
+    auto alloc = [&](auto** p, size_t n) -> int {
+        if (!n) return (int)NVFP4_OK;
+        const size_t bytes = n * sizeof(**p);
+        if (hipMalloc(p, bytes) != hipSuccess) return (int)NVFP4_ERR_ALLOC;
+        return hipMemset(*p, 0, bytes) == hipSuccess ? (int)NVFP4_OK : (int)NVFP4_ERR_HIP;
+    };
+    st = alloc(&seq->ws.partials, floats);
+    if (st == NVFP4_OK) st = alloc(&seq->ws.flagged, flagged);
+    if (st == NVFP4_OK) st = alloc(&seq->ws.counters, counters);
+    // the fills are complete before any launch of the sequence, on any stream
+    if (st == NVFP4_OK && hipDeviceSynchronize() != hipSuccess) st = NVFP4_ERR_HIP;
+    if (st != NVFP4_OK) {
         release(seq);
-        return NVFP4_ERR_ALLOC;
-    }
-    if (counters) {
-        if (hipMalloc(&seq->counters, counters * sizeof(uint32_t)) != hipSuccess) {
-            release(seq);
-            return NVFP4_ERR_ALLOC;
-        }
-        if (hipMemset(seq->counters, 0, counters * sizeof(uint32_t)) != hipSuccess) {
-            release(seq);
-            return NVFP4_ERR_HIP;
-        }
+        return st;
     }
     st = capture(seq);
     if (st != NVFP4_OK) {

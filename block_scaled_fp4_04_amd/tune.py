@@ -33,7 +33,7 @@ WEIGHT_SHAPES = [(256, 6144), (768, 6144), (2048, 6144), (6144, 6144), (8192, 81
 M_SWEEP = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
 EXTRA_SHAPES = [(1, 2048, 6144)]
 KEEP_MARGIN = 0.02
-SKINNY_WAVES = 16  # waves per workgroup of the skinny kernel; each keeps >= 1 K step
+SKINNY_MAX_SPLIT = 16  # the skinny kernel's last arrival fetches one split per wave (16 waves)
 
 
 def shapes(quick: bool) -> list[tuple[int, int, int]]:
@@ -52,8 +52,9 @@ def candidates(M: int, N: int, K: int) -> list[tuple[int, int, int]]:
         out.append((nv.PATH_GEMV, 0, 1))
     if M <= 64:
         groups = cdiv(N, 16)
-        for s in (1, 2, 4, 8, 16):
-            if s <= max(1, steps // SKINNY_WAVES) and groups * s <= 4096:
+        for s in (1, 2, 3, 4, 8, 16):
+            # at least four 128-element K steps per workgroup
+            if s <= min(SKINNY_MAX_SPLIT, max(1, steps // 4)) and groups * s <= 4096:
                 out.append((nv.PATH_SKINNY, 0, s))
     if M > 4:
         for tile in (64, 128):

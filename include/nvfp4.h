@@ -139,13 +139,13 @@ int nvfp4_debug_set_handoff_polls(uint32_t polls);
  * All device buffers are caller-owned and must be 16-byte aligned (else
  * NVFP4_ERR_MISALIGNED).  The call is asynchronous: it returns after the
  * kernels are enqueued; device-side faults surface at the caller's next
- * synchronisation.  The tile path needs each packed code buffer to stay
- * below 2 GiB (else NVFP4_ERR_UNSUPPORTED).  Split-K paths use a
+ * synchronisation.  The tile and wsplit paths need each packed code buffer
+ * to stay below 2 GiB (else NVFP4_ERR_UNSUPPORTED).  Split-K paths use a
  * library-owned workspace per
- * (device, stream) pair, allocated (and its counters zeroed with a
- * synchronous fill) on the first call that needs it and again, larger, on the
- * first call of a shape that needs more; these are the only allocations the
- * library makes.  Calls on one stream are ordered, calls on different
+ * (device, stream) pair, allocated (and zero-filled on that stream, ahead of
+ * the call's kernels) on the first call that needs it and again, larger, on
+ * the first call of a shape that needs more; these are the only allocations
+ * the library makes.  Calls on one stream are ordered, calls on different
  * streams use different workspaces.  Buffers replaced by larger ones stay
  * allocated until nvfp4_shutdown, so a graph captured earlier keeps working.
  * Under stream capture the workspace must already be large enough (make one

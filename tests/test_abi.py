@@ -185,9 +185,14 @@ def test_plan(no_table):
     assert key(1024, 2048, 6144) == ("wsplit", 128, 1)        # 256 tiles of 128 x 64
     assert key(512, 2048, 6144) == ("wsplit", 64, 1)
     assert key(512, 768, 6144) == ("wsplit", 64, 2)
-    # skinny up to 64 rows while N <= 2048, two K slices from 33 rows on
-    assert key(32, 256, 6144)[0] == "skinny" and nv.plan(32, 256, 6144)["split_k"] == 1
-    assert key(64, 2048, 6144)[0] == "skinny" and nv.plan(64, 2048, 6144)["split_k"] == 2
+    # skinny up to 64 rows while N <= 2048: with 2-4 row blocks and up to 64
+    # column groups K splits 3 ways (two blocks) or 4 ways, else two K slices
+    # from 33 rows on
+    assert key(32, 256, 6144) == ("skinny", 16, 3)
+    assert key(64, 768, 6144) == ("skinny", 16, 4)
+    assert key(32, 2048, 6144) == ("skinny", 16, 1)
+    assert key(64, 2048, 6144) == ("skinny", 16, 2)
+    assert key(16, 256, 6144) == ("skinny", 16, 1)
     assert key(64, 6144, 6144)[0] == "wsplit"
     assert key(65, 256, 6144) == ("wsplit", 64, 3)            # at most 3 slices
     for M, N, K in [(512, 768, 6144), (512, 2048, 6144), (300, 5000, 64), (128, 64, 4096)]:

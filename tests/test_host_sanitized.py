@@ -36,7 +36,7 @@ hipError_t launch_grouped_tile(const GemmArgs&, hipStream_t) { return hipErrorIn
 hipError_t launch_quantize(const QuantArgs&, hipStream_t) { return hipErrorInvalidValue; }
 size_t tile_partial_floats(int, const GemmArgs&) { return 0; }
 size_t tile_counters(int, const GemmArgs&) { return 0; }
-size_t skinny_partial_floats(const GemmArgs&) { return 0; }
+size_t skinny_flagged_words(const GemmArgs&) { return 0; }
 size_t skinny_counters(const GemmArgs&) { return 0; }
 size_t wsplit_partial_floats(int, const GemmArgs&) { return 0; }
 int resident_tiles(int, int) { return 0; }
