@@ -38,11 +38,12 @@ def o():
     return orc.load()
 
 
-def run_gpu(ops: synth.Operands, path=nv.PATH_AUTO, split_k=0, stream=None, label=""):
-    say(f"{label} M={ops.M} N={ops.N} K={ops.K} alpha={ops.alpha} path={path} split_k={split_k}")
+def run_gpu(ops: synth.Operands, path=nv.PATH_AUTO, split_k=0, stream=None, label="", tile=0):
+    say(f"{label} M={ops.M} N={ops.N} K={ops.K} alpha={ops.alpha} path={path} split_k={split_k} "
+        f"tile={tile}")
     a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
     b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
-    out = nv.gemm(a, b, ops.alpha, path=path, split_k=split_k, stream=stream)
+    out = nv.gemm(a, b, ops.alpha, path=path, split_k=split_k, stream=stream, tile=tile)
     torch.cuda.synchronize()
     return out.view(torch.int16).cpu().numpy().astype(np.uint16)
 
@@ -197,6 +198,19 @@ def test_tile_several_tiles_per_workgroup(o, M, N, K):
     check_full(o, ops, g, f"tile {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (17, 16, 16), (65, 31, 128), (257, 130, 336),
+                                   (300, 513, 1040), (520, 264, 4096), (512, 1030, 256)])
+def test_tile256_unsplit(o, M, N, K):
+    """The unsplit 256 x 256 kernel on its own: outputs smaller than one
+    tile, ragged edges in both dimensions (the 128-row quarters that each
+    wave decodes reach past the padded rows), N % 8 != 0 and N % 4 != 0
+    (the direct stores) beside N % 8 == 0 (the staged ones), and K from one
+    panel pair up to 64 panels."""
+    ops = synth.random_operands(31 * M + 7 * N + K, M, N, K, alpha=-1.5)
+    g = run_gpu(ops, path=nv.PATH_TILE, tile=256, split_k=1, label="tile 256 unsplit")
+    check_full(o, ops, g, f"tile 256 {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("split_k", [1, 2, 3, 5, 16])
 def test_split_k_variants(o, split_k):
     ops = synth.quantized_operands(91, 200, 160, 2048, alpha=1.25)
@@ -226,8 +240,8 @@ def test_wide_scale_range(o):
                          g0.choice(fin, (M, K // 16)).astype(np.uint8),
                          g0.integers(0, 256, (N, K // 2), dtype=np.uint8),
                          g0.choice(fin, (N, K // 16)).astype(np.uint8), 1.0, M, N, K)
-    for path in (nv.PATH_TILE, nv.PATH_WSPLIT):
-        g = run_gpu(ops, path=path, label="wide scales")
+    for path, tile in ((nv.PATH_TILE, 0), (nv.PATH_TILE, 256), (nv.PATH_WSPLIT, 0)):
+        g = run_gpu(ops, path=path, tile=tile, label="wide scales")
         check_full(o, ops, g, "wide scales", min_exact=0.99)
 
 
