@@ -107,6 +107,20 @@ def test_gemm_rejects_bad_arguments_before_launch():
         assert _wp(4, 32, 64, path, tile) == nv.ERR_INVALID_VALUE, (path, tile)
 
 
+def test_gemm_refuses_operands_past_32bit_offsets():
+    """The tile and wsplit kernels address a packed operand with 32-bit byte
+    offsets, so a tile or wsplit plan whose packed codes would reach 2 GiB
+    (32768 rows x 131072 K: 2048 panels x 32768 rows x 32 bytes) is refused
+    before launch, for A and for B, forced or chosen by the library.  (Only
+    refusals are asserted here: an accepted call would launch on a GPU host;
+    the GPU parity tests run operands one row-block under the limit.)"""
+    K = 131072
+    for path, tile in ((nv.PATH_TILE, 256), (nv.PATH_TILE, 128), (nv.PATH_WSPLIT, 64),
+                       (nv.PATH_WSPLIT, 128), (nv.PATH_AUTO, 0)):
+        assert _wp(32768, 256, K, path, tile) == nv.ERR_UNSUPPORTED, (path, tile)
+        assert _wp(256, 32768, K, path, tile) == nv.ERR_UNSUPPORTED, (path, tile)
+
+
 def _wp(M, N, K, path, tile=0, split_k=0):
     return nv.lib().nvfp4_gemm_with_plan(0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, M, N, K,
                                          path, tile, split_k, None)

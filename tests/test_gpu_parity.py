@@ -15,7 +15,7 @@ import pytest
 
 import synth
 from oracle import oracle as orc
-from parity import check_sample, compare, large_sample
+from parity import check_sample, compare, large_sample, merge
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -209,6 +209,48 @@ def test_tile256_unsplit(o, M, N, K):
     ops = synth.random_operands(31 * M + 7 * N + K, M, N, K, alpha=-1.5)
     g = run_gpu(ops, path=nv.PATH_TILE, tile=256, split_k=1, label="tile 256 unsplit")
     check_full(o, ops, g, f"tile 256 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("big", ["a", "b"])
+def test_operand_just_under_32bit_offsets(o, big):
+    """One operand one row block under the tile and wsplit kernels' 32-bit
+    byte-offset limit (packed codes 2048 panels x 32752 rows x 32 bytes =
+    2 GiB - 1 MiB), the other 512 rows, K = 131072: the library's plan and
+    every forced tile and wsplit plan against the oracle on the last 2048
+    elements of the last row and of the last column (each reads the highest
+    panels; together they take the highest rows of both operands) and 2048
+    random elements, one oracle pass for all."""
+    K = 131072
+    M, N = (32752, 512) if big == "a" else (512, 32752)
+    say(f"generating {M}x{N}x{K} operands")
+    ops = synth.random_operands(4242 + M, M, N, K, alpha=0.5)
+    a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+    b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+    m0, n0 = max(0, M - 2048), max(0, N - 2048)
+    ms = np.random.Generator(np.random.PCG64(9)).integers(0, M, 2048)
+    ns = np.random.Generator(np.random.PCG64(10)).integers(0, N, 2048)
+    outs = {}
+    for path, tile in ((nv.PATH_AUTO, 0), (nv.PATH_TILE, 256), (nv.PATH_TILE, 128),
+                       (nv.PATH_WSPLIT, 64), (nv.PATH_WSPLIT, 128)):
+        say(f"{big}: path {path} tile {tile}")
+        g = nv.gemm(a, b, ops.alpha, path=path, tile=tile)
+        torch.cuda.synchronize()
+        outs[(path, tile)] = g.view(torch.int16).cpu().numpy().astype(np.uint16)
+        del g
+    del a, b
+    # the oracle's values of the sampled elements, computed once
+    row = o.gemm(np.ascontiguousarray(ops.a_codes[M - 1:]), np.ascontiguousarray(ops.a_scales[M - 1:]),
+                 np.ascontiguousarray(ops.b_codes[n0:]), np.ascontiguousarray(ops.b_scales[n0:]),
+                 ops.alpha)
+    col = o.gemm(np.ascontiguousarray(ops.a_codes[m0:]), np.ascontiguousarray(ops.a_scales[m0:]),
+                 np.ascontiguousarray(ops.b_codes[N - 1:]), np.ascontiguousarray(ops.b_scales[N - 1:]),
+                 ops.alpha)
+    pts = o.gemm_points(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha, ms, ns)
+    for key, g in outs.items():
+        r = merge([compare(g[M - 1:, n0:], *row, ops.alpha), compare(g[m0:, N - 1:], *col, ops.alpha),
+                   compare(g[ms, ns], *pts, ops.alpha)])
+        say(f"{big} {key}: {r}")
+        assert r["over"] == 0 and r["bit_exact_frac"] >= 0.99 and not r["all_zero"], (key, r)
 
 
 @pytest.mark.parametrize("split_k", [1, 2, 3, 5, 16])
