@@ -253,6 +253,33 @@ def test_operand_just_under_32bit_offsets(o, big):
         assert r["over"] == 0 and r["bit_exact_frac"] >= 0.99 and not r["all_zero"], (key, r)
 
 
+@pytest.mark.parametrize("alpha", [0.0, -0.0, -1.75, 1e36, -1e36, 1e-40, 3e-39,
+                                   float("inf"), float("-inf"), float("nan")])
+def test_alpha_special_values(o, alpha):
+    """The epilogue's degenerate cases on every path: alpha of either zero,
+    products past the bfloat16 range (1e36 x sums of a few hundred or more),
+    results among the bfloat16 subnormals (alpha 1e-40 and 3e-39, both FP32
+    subnormals themselves: a flushed denormal would show as zeros), infinite
+    alpha (sums of zero give NaN) and NaN.  NaN positions must match the oracle's and
+    every other element its bits (zeros of either sign count as equal),
+    infinities included: with an infinite alpha the relative tolerance says
+    nothing."""
+    for M, paths in ((40, (nv.PATH_AUTO, nv.PATH_TILE, nv.PATH_WSPLIT, nv.PATH_SKINNY)),
+                     (3, (nv.PATH_AUTO, nv.PATH_GEMV))):
+        ops = synth.random_operands(77 + M, M, 72, 256, alpha=alpha)
+        bits, _, _ = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, alpha)
+        nan_o = ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
+        for path in paths:
+            g = run_gpu(ops, path=path, label=f"alpha {alpha}")
+            nan_g = ((g & 0x7F80) == 0x7F80) & ((g & 0x7F) != 0)
+            ok = ~nan_o
+            same = (g[ok] == bits[ok]) | (((g[ok] & 0x7FFF) == 0) & ((bits[ok] & 0x7FFF) == 0))
+            say(f"alpha {alpha} M {M} path {path}: NaN {int(nan_o.sum())}/{int(nan_g.sum())}, "
+                f"bit-equal {float(same.mean()) if same.size else 1.0}")
+            assert np.array_equal(nan_o, nan_g), (alpha, path)
+            assert same.all(), (alpha, path, g[ok][~same][:8], bits[ok][~same][:8])
+
+
 @pytest.mark.parametrize("split_k", [1, 2, 3, 5, 16])
 def test_split_k_variants(o, split_k):
     ops = synth.quantized_operands(91, 200, 160, 2048, alpha=1.25)
