@@ -330,17 +330,21 @@ def grouped_line(nv, torch, steps, warmup):
 QUANT_SHAPES = [(16, 6144), (16384, 8192)]   # decode activations of one expert; saturation-shape A
 
 
-def quantize_bytes(rows: int, K: int) -> int:
-    """fp32 input read once plus the packed output written (padding included)."""
+def quantize_bytes(rows: int, K: int, in_bytes: int = 4) -> int:
+    """Input read once (4 bytes per fp32 value, 2 per bfloat16) plus the
+    packed output written (padding included)."""
     rp = -(-rows // 16) * 16
     kp = -(-K // 128) * 128
-    return rows * K * 4 + rp * kp // 2 + rp * kp // 16
+    return rows * K * in_bytes + rp * kp // 2 + rp * kp // 16
 
 
-def quantize_line(nv, torch, rows, K, steps, warmup):
-    """Per-call time of nvfp4_quantize on a resident fp32 tensor, graph-replayed."""
+def quantize_line(nv, torch, rows, K, steps, warmup, bf16=False):
+    """Per-call time of nvfp4_quantize (nvfp4_quantize_bf16) on a resident
+    fp32 (bfloat16) tensor, graph-replayed."""
     g = np.random.Generator(np.random.PCG64(rows + K))
     x = torch.from_numpy(g.standard_normal((rows, K), dtype=np.float32)).to("cuda")
+    if bf16:
+        x = x.to(torch.bfloat16)
     out = nv.quantize(x)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -361,11 +365,12 @@ def quantize_line(nv, torch, rows, K, steps, warmup):
         stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
-    b = quantize_bytes(rows, K)
+    b = quantize_bytes(rows, K, 2 if bf16 else 4)
     ach = b / (ms * 1e-3) / 1e9
     del gr
-    return f"quantize_{rows}x{K}", {
-        "rows": rows, "K": K, "ms": ms, "gelem_per_s": rows * K / (ms * 1e-3) / 1e9,
+    return f"quantize_{'bf16_' if bf16 else ''}{rows}x{K}", {
+        "rows": rows, "K": K, "input": "bfloat16" if bf16 else "float32", "ms": ms,
+        "gelem_per_s": rows * K / (ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
                      "frac": ach / HBM_GBPS, "traffic": None, "algorithmic_bytes_per_launch": b},
         "path": "quantize"}
@@ -657,9 +662,10 @@ def main():
         return
 
     if args.quantize_only:
-        for rows, K in QUANT_SHAPES:
-            name, q = quantize_line(nv, torch, rows, K, args.steps, args.warmup)
-            print(json.dumps({"workload": name, **q}), flush=True)
+        for bf16 in (False, True):
+            for rows, K in QUANT_SHAPES:
+                name, q = quantize_line(nv, torch, rows, K, args.steps, args.warmup, bf16)
+                print(json.dumps({"workload": name, **q}), flush=True)
         return
     if args.decode_only:
         name, d = decode_sequence_line(nv, torch, args.steps, args.warmup)
@@ -716,10 +722,11 @@ def main():
         torch.cuda.empty_cache()
         name, d = decode_sequence_line(nv, torch, args.steps, args.warmup)
         per[name] = d
-        for rows, K in QUANT_SHAPES:
-            torch.cuda.empty_cache()
-            name, q = quantize_line(nv, torch, rows, K, args.steps, args.warmup)
-            per[name] = q
+        for bf16 in (False, True):
+            for rows, K in QUANT_SHAPES:
+                torch.cuda.empty_cache()
+                name, q = quantize_line(nv, torch, rows, K, args.steps, args.warmup, bf16)
+                per[name] = q
         for c in synth.CONFIGS:
             if c.index == cfg.index:
                 continue

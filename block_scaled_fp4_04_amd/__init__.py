@@ -60,6 +60,7 @@ EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_p
            "nvfp4_plan_table_clear", "nvfp4_build_id", "nvfp4_grouped_gemm", "nvfp4_quantize",
            "nvfp4_sequence_create", "nvfp4_sequence_add_gemm", "nvfp4_sequence_add_grouped_gemm",
            "nvfp4_sequence_add_quantize", "nvfp4_sequence_finalize", "nvfp4_sequence_launch",
+           "nvfp4_quantize_bf16", "nvfp4_sequence_add_quantize_bf16",
            "nvfp4_sequence_destroy", "nvfp4_probe_empty", "nvfp4_probe_chase",
            "nvfp4_probe_mfma", "nvfp4_probe_read", "nvfp4_device_flags",
            "nvfp4_debug_set_handoff_polls", "nvfp4_gemm_noalloc", "nvfp4_noalloc_scratch_bytes"]
@@ -109,8 +110,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemm_with_plan.restype = ctypes.c_int
         L.nvfp4_gemm_with_plan.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64,
                                            _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
-        L.nvfp4_quantize.restype = ctypes.c_int
-        L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
+        for f in ("nvfp4_quantize", "nvfp4_quantize_bf16"):
+            getattr(L, f).restype = ctypes.c_int
+            getattr(L, f).argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
         L.nvfp4_probe_empty.restype = ctypes.c_int
         L.nvfp4_probe_empty.argtypes = [_i64, _i64, _vp]
         L.nvfp4_probe_chase.restype = ctypes.c_int
@@ -147,8 +149,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_sequence_add_grouped_gemm.restype = ctypes.c_int
         L.nvfp4_sequence_add_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                                       ctypes.c_float, _vp, _i64, _i64, _i64]
-        L.nvfp4_sequence_add_quantize.restype = ctypes.c_int
-        L.nvfp4_sequence_add_quantize.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp]
+        for f in ("nvfp4_sequence_add_quantize", "nvfp4_sequence_add_quantize_bf16"):
+            getattr(L, f).restype = ctypes.c_int
+            getattr(L, f).argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp]
         for f in ("nvfp4_sequence_finalize", "nvfp4_sequence_destroy"):
             getattr(L, f).restype = ctypes.c_int
             getattr(L, f).argtypes = [_vp]
@@ -453,13 +456,22 @@ def grouped_gemm(a: PackedOperand, b: PackedGroups, row_offsets, alpha: float = 
     return out
 
 
-def quantize(x, out: PackedOperand | None = None, stream=None) -> PackedOperand:
-    """Quantise a 2-D fp32 device tensor (rows x K, unit stride along K, row
-    stride a multiple of 4 elements) to NVFP4 in the packed layout
-    (nvfp4_quantize); returns the PackedOperand (or fills ``out``)."""
+def _quantize_fn(x, prefix: str) -> str:
+    """The C function for x's dtype: float32 -> <prefix>, bfloat16 ->
+    <prefix>_bf16 (rows of 16-byte multiples either way)."""
     import torch
-    if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a 2-D float32 tensor with unit stride along K")
+    if x.dtype not in (torch.float32, torch.bfloat16) or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 or bfloat16 tensor with unit stride along K")
+    return prefix if x.dtype == torch.float32 else prefix + "_bf16"
+
+
+def quantize(x, out: PackedOperand | None = None, stream=None) -> PackedOperand:
+    """Quantise a 2-D fp32 or bfloat16 device tensor (rows x K, unit stride
+    along K, row stride a multiple of 4 fp32 or 8 bfloat16 elements) to NVFP4
+    in the packed layout (nvfp4_quantize / nvfp4_quantize_bf16); returns the
+    PackedOperand (or fills ``out``)."""
+    import torch
+    fn = _quantize_fn(x, "nvfp4_quantize")
     rows, K = x.shape
     if out is None:
         cb, sb = packed_size(rows, K)
@@ -468,10 +480,10 @@ def quantize(x, out: PackedOperand | None = None, stream=None) -> PackedOperand:
     elif out.rows != rows or out.K != K:
         raise ValueError("out has the wrong shape")
     out.check("out")
-    st = lib().nvfp4_quantize(x.data_ptr(), rows, K, x.stride(0), out.codes.data_ptr(),
-                              out.scales.data_ptr(), _stream_handle(stream))
+    st = getattr(lib(), fn)(x.data_ptr(), rows, K, x.stride(0), out.codes.data_ptr(),
+                            out.scales.data_ptr(), _stream_handle(stream))
     if st:
-        raise Nvfp4Error(st, f"nvfp4_quantize(rows={rows}, K={K}, ld={x.stride(0)})")
+        raise Nvfp4Error(st, f"{fn}(rows={rows}, K={K}, ld={x.stride(0)})")
     return out
 
 
@@ -568,17 +580,16 @@ class Sequence:
             M, N, a.K), f"nvfp4_sequence_add_grouped_gemm(G={b.groups}, M={M}, N={N})")
 
     def add_quantize(self, x, out: PackedOperand) -> None:
-        import torch
-        if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
-            raise ValueError("x must be a 2-D float32 tensor with unit stride along K")
+        """Records quantize(x, out): fp32 or bfloat16 x."""
+        fn = _quantize_fn(x, "nvfp4_sequence_add_quantize")
         rows, K = x.shape
         if out.rows != rows or out.K != K:
             raise ValueError("out has the wrong shape")
         out.check("out")
         self._keep += [x, out]
-        self._check(lib().nvfp4_sequence_add_quantize(
+        self._check(getattr(lib(), fn)(
             self._h, x.data_ptr(), rows, K, x.stride(0), out.codes.data_ptr(),
-            out.scales.data_ptr()), f"nvfp4_sequence_add_quantize(rows={rows}, K={K})")
+            out.scales.data_ptr()), f"{fn}(rows={rows}, K={K})")
 
     def finalize(self) -> None:
         st = lib().nvfp4_sequence_finalize(self._h)

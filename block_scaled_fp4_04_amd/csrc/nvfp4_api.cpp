@@ -288,9 +288,11 @@ int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_pa
     return NVFP4_OK;
 }
 
-int prepare_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
-                     void* packed_scales, Job* job) {
-    if (!x || !packed_codes || !packed_scales || !valid_rows_k(rows, K) || ld < K || ld % 4 != 0)
+int prepare_quantize(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
+                     void* packed_codes, void* packed_scales, Job* job) {
+    // rows start on 16-byte boundaries: 4 fp32 or 8 bfloat16 values
+    if (!x || !packed_codes || !packed_scales || !valid_rows_k(rows, K) || ld < K ||
+        ld % (bf16 ? 8 : 4) != 0)
         return NVFP4_ERR_INVALID_VALUE;
     if (!aligned16(x) || !aligned16(packed_codes) || !aligned16(packed_scales))
         return NVFP4_ERR_MISALIGNED;
@@ -301,6 +303,7 @@ int prepare_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* 
     job->kind = JOB_QUANTIZE;
     QuantArgs& a = job->quant;
     a.x = x;
+    a.bf16 = bf16;
     a.codes = static_cast<uint8_t*>(packed_codes);
     a.scales = static_cast<uint8_t*>(packed_scales);
     a.ld = ld;
@@ -465,7 +468,14 @@ int nvfp4_gemm_with_plan(const void* a_packed, const void* a_scales, const void*
 int nvfp4_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
                    void* packed_scales, void* stream) {
     Job job;
-    const int st = prepare_quantize(x, rows, K, ld, packed_codes, packed_scales, &job);
+    const int st = prepare_quantize(x, false, rows, K, ld, packed_codes, packed_scales, &job);
+    return st != NVFP4_OK ? st : run_job(job, stream);
+}
+
+int nvfp4_quantize_bf16(const void* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
+                        void* packed_scales, void* stream) {
+    Job job;
+    const int st = prepare_quantize(x, true, rows, K, ld, packed_codes, packed_scales, &job);
     return st != NVFP4_OK ? st : run_job(job, stream);
 }
 

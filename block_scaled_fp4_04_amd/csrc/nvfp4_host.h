@@ -33,8 +33,8 @@ int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packe
 int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_packed,
                     const void* b_scales, const int32_t* row_offsets, int64_t groups, float alpha,
                     void* out, int64_t M, int64_t N, int64_t K, Job* job);
-int prepare_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
-                     void* packed_scales, Job* job);
+int prepare_quantize(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
+                     void* packed_codes, void* packed_scales, Job* job);
 
 // The current device, checked to be a gfx950 GPU (status).
 int current_device(int* device);

@@ -135,7 +135,8 @@ int noalloc_setup(int device);
 
 // NVFP4 quantisation of fp32 rows into the packed operand layout.
 struct QuantArgs {
-    const float* x;   // rows x K values, row stride ld elements
+    const void* x;    // rows x K values (fp32, or bfloat16 if bf16), row stride ld elements
+    bool bf16;
     uint8_t* codes;   // packed codes  [P][Rp][32]
     uint8_t* scales;  // packed scales [P][Rp][4]
     int64_t ld;

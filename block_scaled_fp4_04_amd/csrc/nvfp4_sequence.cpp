@@ -111,7 +111,16 @@ int nvfp4_sequence_add_quantize(nvfp4_sequence_t seq, const float* x, int64_t ro
     if (!seq) return NVFP4_ERR_INVALID_VALUE;
     if (seq->finalized) return NVFP4_ERR_STATE;
     Job job;
-    const int st = prepare_quantize(x, rows, K, ld, packed_codes, packed_scales, &job);
+    const int st = prepare_quantize(x, false, rows, K, ld, packed_codes, packed_scales, &job);
+    return add_job(seq, st, job);
+}
+
+int nvfp4_sequence_add_quantize_bf16(nvfp4_sequence_t seq, const void* x, int64_t rows, int64_t K,
+                                     int64_t ld, void* packed_codes, void* packed_scales) {
+    if (!seq) return NVFP4_ERR_INVALID_VALUE;
+    if (seq->finalized) return NVFP4_ERR_STATE;
+    Job job;
+    const int st = prepare_quantize(x, true, rows, K, ld, packed_codes, packed_scales, &job);
     return add_job(seq, st, job);
 }
 

@@ -197,6 +197,17 @@ int nvfp4_gemm_with_plan(const void* a_packed, const void* a_scales, const void*
 int nvfp4_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
                    void* packed_scales, void* stream);
 
+/* The same quantisation of bfloat16 rows.  The GEMM's output, and so the
+ * activations the next layer quantises, is bfloat16 ("Peeling the Kernel
+ * Onion", section "The Benchmark Design", the BF16 output term of the byte
+ * count); every bfloat16 value is exactly an fp32 value, and the result is
+ * that of nvfp4_quantize on the rows widened to fp32, byte for byte.
+ *   x : DEVICE bfloat16, rows x K values, row stride ld elements (ld >= K,
+ *       ld % 8 == 0); the buffer holds at least (rows - 1) * ld + K values
+ * Everything else as nvfp4_quantize. */
+int nvfp4_quantize_bf16(const void* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
+                        void* packed_scales, void* stream);
+
 /* Grouped GEMM for mixture-of-experts layers: `groups` weight operands B_g
  * (each N x K) share one launch; group g owns rows
  * row_offsets[g] .. row_offsets[g+1]-1 of A and of C:
@@ -299,7 +310,8 @@ const char* nvfp4_build_id(void);
  *   nvfp4_sequence_create   : an empty sequence (host object, caller-owned)
  *   nvfp4_sequence_add_*    : append one call; arguments and checks as for
  *                             nvfp4_gemm / nvfp4_grouped_gemm / nvfp4_quantize
- *                             (minus the stream); the plan is fixed here.
+ *                             / nvfp4_quantize_bf16 (minus the stream); the
+ *                             plan is fixed here.
  *                             Buffers are used by address at every launch:
  *                             they must stay allocated for the sequence's
  *                             lifetime, and their contents are read when the
@@ -333,6 +345,9 @@ int nvfp4_sequence_add_grouped_gemm(nvfp4_sequence_t seq, const void* a_packed,
                                     int64_t K);
 int nvfp4_sequence_add_quantize(nvfp4_sequence_t seq, const float* x, int64_t rows, int64_t K,
                                 int64_t ld, void* packed_codes, void* packed_scales);
+int nvfp4_sequence_add_quantize_bf16(nvfp4_sequence_t seq, const void* x, int64_t rows,
+                                     int64_t K, int64_t ld, void* packed_codes,
+                                     void* packed_scales);
 int nvfp4_sequence_finalize(nvfp4_sequence_t seq);
 int nvfp4_sequence_launch(nvfp4_sequence_t seq, void* stream);
 int nvfp4_sequence_destroy(nvfp4_sequence_t seq);

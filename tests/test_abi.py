@@ -168,6 +168,18 @@ def test_quantize_rejects_bad_arguments_before_launch():
     assert q(0x3000, 4, 64, 64, 0x1008, 0x2000, None) == nv.ERR_MISALIGNED
 
 
+def test_quantize_bf16_rejects_bad_arguments_before_launch():
+    """The bfloat16 entry point: the same rules, rows of 8-element multiples."""
+    q = nv.lib().nvfp4_quantize_bf16
+    assert q(None, 4, 64, 64, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE
+    assert q(0x3000, 0, 64, 64, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE
+    assert q(0x3000, 4, 24, 24, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE   # K % 16
+    assert q(0x3000, 4, 64, 32, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE   # ld < K
+    assert q(0x3000, 4, 64, 68, 0x1000, 0x2000, None) == nv.ERR_INVALID_VALUE   # ld % 8
+    assert q(0x3008, 4, 64, 64, 0x1000, 0x2000, None) == nv.ERR_MISALIGNED
+    assert q(0x3000, 4, 64, 64, 0x1000, 0x2004, None) == nv.ERR_MISALIGNED
+
+
 def test_python_gemm_rejects_k_mismatch():
     a = nv.PackedOperand(None, None, 4, 128)
     b = nv.PackedOperand(None, None, 4, 256)
@@ -237,11 +249,14 @@ def test_sequence_state_and_validation():
             == nv.ERR_MISALIGNED
         q = lib.nvfp4_sequence_add_quantize
         assert q(h, 0x3000, 4, 64, 32, 0x1000, 0x2000) == nv.ERR_INVALID_VALUE
+        qb = lib.nvfp4_sequence_add_quantize_bf16
+        assert qb(h, 0x3000, 4, 64, 68, 0x1000, 0x2000) == nv.ERR_INVALID_VALUE   # ld % 8
         # nothing recorded: nothing to finalize; not finalized: no launch
         assert lib.nvfp4_sequence_finalize(h) == nv.ERR_INVALID_VALUE
         assert lib.nvfp4_sequence_launch(h, None) == nv.ERR_STATE
         assert add(h, 0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64) == nv.OK
         assert q(h, 0x3000, 4, 64, 64, 0x1000, 0x2000) == nv.OK
+        assert qb(h, 0x3000, 4, 64, 72, 0x1000, 0x2000) == nv.OK
         assert g(h, 0x1000, 0x2000, 0x3000, 0x4000, 0x6000, 2, 1.0, 0x5000, 0, 4, 64) == nv.OK
     finally:
         assert lib.nvfp4_sequence_destroy(h) == nv.OK

@@ -162,3 +162,103 @@ def test_quantize_saturation_shape_activations(o):
     g = np.random.Generator(np.random.PCG64(1005))
     x = g.standard_normal((16384, 8192), dtype=np.float32)
     check_quantize(o, x, "16384 x 8192 activations")
+
+
+# ---------------------------------------------------------------- bfloat16 input
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    """The fp32 values that bfloat16 bit patterns equal (exact)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_tensor(bits: np.ndarray, ld: int | None = None):
+    """A device bfloat16 tensor holding `bits` (rows x K), row stride ld."""
+    rows, K = bits.shape
+    if ld is None:
+        host = np.ascontiguousarray(bits)
+    else:
+        host = np.full((rows, ld), 0x7FC0, np.uint16)   # NaN in the gap: it must not be read
+        host[:, :K] = bits
+    t = torch.from_numpy(host.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return t if ld is None else t[:, :K]
+
+
+def check_quantize_bf16(o, bits: np.ndarray, label: str, ld: int | None = None):
+    """nvfp4_quantize_bf16 of bfloat16 rows against the oracle's quantiser
+    of the same values widened to fp32, every packed byte."""
+    rows, K = bits.shape
+    say(f"{label} (bf16): rows={rows} K={K} ld={ld or K}")
+    q = nv.quantize(bf16_tensor(bits, ld))
+    torch.cuda.synchronize()
+    gc, gs = q.codes.cpu().numpy(), q.scales.cpu().numpy()
+    oc, os_ = o.quantize(widen(bits))
+    pc, ps = nv.pack(oc, os_)
+    bad_c, bad_s = int(np.count_nonzero(gc != pc)), int(np.count_nonzero(gs != ps))
+    say(f"{label} (bf16): {bad_c} code bytes and {bad_s} scale bytes differ")
+    assert bad_c == 0 and bad_s == 0
+    return q, oc, os_
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bits, round to nearest even (torch's conversion)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("rows,K,sigma", [(130, 6160, 1.0), (16, 6144, 1.0), (1, 16, 1e3),
+                                          (33, 2048, 1e-3)])
+def test_quantize_bf16_distributions(o, rows, K, sigma):
+    g = np.random.Generator(np.random.PCG64(rows * 100 + K + 1))
+    check_quantize_bf16(o, to_bf16_bits(g.standard_normal((rows, K)) * sigma), f"N(0,{sigma})")
+
+
+def test_quantize_bf16_every_finite_pattern(o):
+    """Every finite bfloat16 bit pattern once, shuffled into blocks (scales
+    from the smallest subnormal block maxima to saturation at 448)."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = allb[(allb & 0x7F80) != 0x7F80]
+    g = np.random.Generator(np.random.PCG64(3))
+    x = g.permutation(fin)
+    x = np.concatenate([x, np.zeros((-x.size) % 64, np.uint16)]).reshape(-1, 64)
+    check_quantize_bf16(o, x, "every finite pattern")
+
+
+def test_quantize_bf16_boundary_neighbours(o):
+    """Every positive scale byte s and E2M1 rounding boundary T: x = T*s
+    (exact in bfloat16) and its 4 bfloat16 neighbours on each side, both
+    signs, in blocks whose amax fixes the scale at s."""
+    rows = []
+    for sb in range(0x01, 0x7F):
+        s = np.float32(qp.e4m3_val(sb))
+        amax = to_bf16_bits(np.array([6.0 * s], np.float32))[0]
+        for T in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+            p = to_bf16_bits(np.array([T * s], np.float32))[0]
+            assert widen(np.array([p]))[0] == np.float32(T) * s   # exact
+            vals = [int(p)] + [int(p) + d for i in range(1, 5) for d in (i, -i)]
+            vals = [int(amax)] + vals + [v | 0x8000 for v in vals[:6]]
+            rows.append(np.array(vals[:16], np.uint16))
+    x = np.stack(rows)
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 4, 16), np.uint16)]).reshape(-1, 64)
+    _, _, os_ = check_quantize_bf16(o, x, "boundary neighbours")
+    assert np.array_equal(os_.reshape(-1)[:126 * 7], np.repeat(np.arange(1, 0x7F), 7))
+
+
+def test_quantize_bf16_strided_rows_and_sequence(o):
+    """Rows with a stride past K, eagerly and recorded in a sequence: both
+    equal the oracle, byte for byte."""
+    g = np.random.Generator(np.random.PCG64(19))
+    bits = to_bf16_bits(g.standard_normal((40, 496)))
+    q, _, _ = check_quantize_bf16(o, bits, "strided rows", ld=504)
+    out = nv.PackedOperand(torch.zeros_like(q.codes), torch.zeros_like(q.scales), 40, 496)
+    seq = nv.Sequence()
+    xd = bf16_tensor(bits, 504)
+    seq.add_quantize(xd, out)
+    seq.finalize()
+    for rep in range(2):
+        out.codes.zero_()
+        out.scales.zero_()
+        torch.cuda.synchronize()
+        seq.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(out.codes, q.codes) and torch.equal(out.scales, q.scales), rep
+    say("strided rows (bf16): sequence replays equal the eager result")
