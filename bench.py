@@ -415,6 +415,14 @@ def decode_sequence_line(nv, torch, steps, warmup):
         seq.add_quantize(x16, a16)
         seq.add_gemm(a16, w_up, o16, 1.0)
     seq.finalize()
+    # the same step with the one-row projection quantising its own
+    # activations (nvfp4_gemm_quantized): 3 calls per layer
+    seq_f = nv.Sequence()
+    for w_attn, w_up, o1, o16 in layers:
+        seq_f.add_gemm_quantized(x1, w_attn, 0.5, o1)
+        seq_f.add_quantize(x16, a16)
+        seq_f.add_gemm(a16, w_up, o16, 1.0)
+    seq_f.finalize()
 
     def timed(fn):
         with torch.cuda.stream(stream):
@@ -433,14 +441,65 @@ def decode_sequence_line(nv, torch, steps, warmup):
 
     eager_us = timed(eager_step)
     seq_us = timed(lambda: seq.launch(stream))
-    calls = seq.calls
+    fused_us = timed(lambda: seq_f.launch(stream))
+    calls, calls_f = seq.calls, seq_f.calls
     seq.close()
+    seq_f.close()
     return "decode_step_sequence", {
         "layers": DECODE_LAYERS, "calls_per_step": calls,
         "calls": "per layer: quantize 1x6144, GEMM 1x768x6144, quantize 16x6144, GEMM 16x256x6144",
         "us_per_step_eager": eager_us, "us_per_step_sequence": seq_us,
         "us_per_call_eager": eager_us / calls, "us_per_call_sequence": seq_us / calls,
-        "speedup": eager_us / seq_us, "path": "sequence (one HIP graph launch per step)"}
+        "speedup": eager_us / seq_us,
+        "fused_calls_per_step": calls_f,
+        "fused_calls": "per layer: GEMM 1x768x6144 quantising its fp32 row (nvfp4_gemm_quantized), "
+                       "quantize 16x6144, GEMM 16x256x6144",
+        "us_per_step_sequence_fused": fused_us,
+        "path": "sequence (one HIP graph launch per step)"}
+
+
+def fused_projection_line(nv, torch, steps, warmup):
+    """The decode attention projection from unquantised activations (one
+    row of 6144, N = 768, alpha 0.5), per call in a graph replay: quantise
+    then GEMM (two launches) against nvfp4_gemm_quantized (one), for fp32
+    and bfloat16 rows; the outputs of the two forms are compared bit for bit."""
+    K, N = 6144, 768
+    g = torch.Generator(device="cuda").manual_seed(2027)
+    b = nv.quantize(torch.randn((N, K), generator=g, device="cuda") * 0.02)
+    res = {"shape": "1 x 768 x 6144", "alpha": 0.5}
+    for name, dt in (("float32", torch.float32), ("bfloat16", torch.bfloat16)):
+        x = torch.randn((1, K), generator=g, device="cuda").to(dt)
+        a = nv.quantize(x)
+        o2 = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+        o1 = torch.empty_like(o2)
+        stream = torch.cuda.Stream()
+
+        def per_call(fn):
+            with torch.cuda.stream(stream):
+                for _ in range(max(1, warmup)):
+                    fn(stream)
+            stream.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                cap = torch.cuda.current_stream()
+                for _ in range(steps):
+                    fn(cap)
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                gr.replay()
+                start.record(stream)
+                gr.replay()
+                stop.record(stream)
+            torch.cuda.synchronize()
+            del gr
+            return start.elapsed_time(stop) * 1000.0 / steps
+
+        two = per_call(lambda s: (nv.quantize(x, out=a, stream=s), nv.gemm(a, b, 0.5, out=o2, stream=s)))
+        one = per_call(lambda s: nv.gemm_quantized(x, b, 0.5, out=o1, stream=s))
+        res[name] = {"us_quantize_then_gemm": two, "us_gemm_quantized": one,
+                     "identical": bool(torch.equal(o1.view(torch.int16), o2.view(torch.int16)))}
+    return "decode_attn_proj_from_activations", res
 
 
 def floors_line(nv, torch, steps):
@@ -670,6 +729,8 @@ def main():
     if args.decode_only:
         name, d = decode_sequence_line(nv, torch, args.steps, args.warmup)
         print(json.dumps({"workload": name, **d}), flush=True)
+        name, d = fused_projection_line(nv, torch, args.steps, args.warmup)
+        print(json.dumps({"workload": name, **d}), flush=True)
         return
     if args.grouped_only:
         name, g = grouped_line(nv, torch, args.steps, args.warmup)
@@ -721,6 +782,8 @@ def main():
         per[name] = g
         torch.cuda.empty_cache()
         name, d = decode_sequence_line(nv, torch, args.steps, args.warmup)
+        per[name] = d
+        name, d = fused_projection_line(nv, torch, args.steps, args.warmup)
         per[name] = d
         for bf16 in (False, True):
             for rows, K in QUANT_SHAPES:

@@ -49,6 +49,8 @@ PATH_TILE = 1
 PATH_SKINNY = 2
 PATH_WSPLIT = 3
 PATH_GEMV = 4
+INPUT_F32 = 0     # element types of nvfp4_gemm_quantized's activation rows
+INPUT_BF16 = 1
 PATH_NAMES = {PATH_TILE: "tile", PATH_SKINNY: "skinny", PATH_WSPLIT: "wsplit", PATH_GEMV: "gemv"}
 
 PLAN_HEURISTIC = 0
@@ -60,7 +62,8 @@ EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_p
            "nvfp4_plan_table_clear", "nvfp4_build_id", "nvfp4_grouped_gemm", "nvfp4_quantize",
            "nvfp4_sequence_create", "nvfp4_sequence_add_gemm", "nvfp4_sequence_add_grouped_gemm",
            "nvfp4_sequence_add_quantize", "nvfp4_sequence_finalize", "nvfp4_sequence_launch",
-           "nvfp4_quantize_bf16", "nvfp4_sequence_add_quantize_bf16",
+           "nvfp4_quantize_bf16", "nvfp4_sequence_add_quantize_bf16", "nvfp4_gemm_quantized",
+           "nvfp4_sequence_add_gemm_quantized",
            "nvfp4_sequence_destroy", "nvfp4_probe_empty", "nvfp4_probe_chase",
            "nvfp4_probe_mfma", "nvfp4_probe_read", "nvfp4_device_flags",
            "nvfp4_debug_set_handoff_polls", "nvfp4_gemm_noalloc", "nvfp4_noalloc_scratch_bytes"]
@@ -134,6 +137,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_grouped_gemm.restype = ctypes.c_int
         L.nvfp4_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float, _vp, _i64,
                                          _i64, _i64, _vp]
+        L.nvfp4_gemm_quantized.restype = ctypes.c_int
+        L.nvfp4_gemm_quantized.argtypes = [_vp, ctypes.c_int, _i64, _vp, _vp, ctypes.c_float, _vp,
+                                           _i64, _i64, _i64, _vp]
+        L.nvfp4_sequence_add_gemm_quantized.restype = ctypes.c_int
+        L.nvfp4_sequence_add_gemm_quantized.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp, _vp,
+                                                        ctypes.c_float, _vp, _i64, _i64, _i64]
         L.nvfp4_plan.restype = ctypes.c_int
         L.nvfp4_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_PlanT)]
         L.nvfp4_plan_table_load.restype = ctypes.c_int
@@ -487,6 +496,37 @@ def quantize(x, out: PackedOperand | None = None, stream=None) -> PackedOperand:
     return out
 
 
+def _activation_rows(x, b: PackedOperand, out):
+    """Checks of gemm_quantized's arguments: x (M x K fp32 or bfloat16, unit
+    stride along K) against B; returns (x_type, M, N, out)."""
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16) or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 or bfloat16 tensor with unit stride along K")
+    M, K = x.shape
+    if K != b.K:
+        raise ValueError(f"K dimension mismatch: x has K={K}, B has K={b.K}")
+    N = b.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
+    b.check("b")
+    return (INPUT_F32 if x.dtype == torch.float32 else INPUT_BF16), M, N, out
+
+
+def gemm_quantized(x, b: PackedOperand, alpha: float = 1.0, out=None, stream=None):
+    """C = gemm(quantize(x), b, alpha) in one launch (nvfp4_gemm_quantized):
+    x holds 1-4 rows of fp32 or bfloat16 activations; the result equals the
+    two-call form bit for bit."""
+    x_type, M, N, out = _activation_rows(x, b, out)
+    st = lib().nvfp4_gemm_quantized(x.data_ptr(), x_type, x.stride(0), b.codes.data_ptr(),
+                                    b.scales.data_ptr(), float(alpha), out.data_ptr(), M, N, b.K,
+                                    _stream_handle(stream))
+    if st:
+        raise Nvfp4Error(st, f"nvfp4_gemm_quantized(M={M}, N={N}, K={b.K})")
+    return out
+
+
 def probe_empty(blocks: int, threads: int, stream=None) -> None:
     """Enqueue an empty kernel (nvfp4_probe_empty): a measurement aid for
     the per-call floor of a launch."""
@@ -560,6 +600,14 @@ class Sequence:
             self._h, a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
             b.scales.data_ptr(), float(alpha), out.data_ptr(), M, N, a.K),
             f"nvfp4_sequence_add_gemm(M={M}, N={N}, K={a.K})")
+
+    def add_gemm_quantized(self, x, b: PackedOperand, alpha: float, out) -> None:
+        """Records gemm_quantized(x, b, alpha, out)."""
+        x_type, M, N, out = _activation_rows(x, b, out)
+        self._keep += [x, b, out]
+        self._check(lib().nvfp4_sequence_add_gemm_quantized(
+            self._h, x.data_ptr(), x_type, x.stride(0), b.codes.data_ptr(), b.scales.data_ptr(),
+            float(alpha), out.data_ptr(), M, N, b.K), f"nvfp4_sequence_add_gemm_quantized(M={M}, N={N})")
 
     def add_grouped_gemm(self, a: PackedOperand, b: "PackedGroups", row_offsets, out,
                          alpha: float = 1.0) -> None:

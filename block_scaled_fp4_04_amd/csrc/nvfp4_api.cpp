@@ -314,8 +314,39 @@ int prepare_quantize(const void* x, bool bf16, int64_t rows, int64_t K, int64_t 
     return NVFP4_OK;
 }
 
+int prepare_gemm_quantized(const void* x, int x_type, int64_t ldx, const void* b_packed,
+                           const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
+                           int64_t K, Job* job) {
+    if (!x || !b_packed || !b_scales || !out) return NVFP4_ERR_INVALID_VALUE;
+    if (x_type != NVFP4_INPUT_F32 && x_type != NVFP4_INPUT_BF16) return NVFP4_ERR_INVALID_VALUE;
+    const bool bf16 = x_type == NVFP4_INPUT_BF16;
+    if (M < 1 || N < 1 || N > kMaxDim || !valid_rows_k(1, K) || ldx < K || ldx % (bf16 ? 8 : 4) != 0)
+        return NVFP4_ERR_INVALID_VALUE;
+    if (!aligned16(x) || !aligned16(b_packed) || !aligned16(b_scales) || !aligned16(out))
+        return NVFP4_ERR_MISALIGNED;
+    const int64_t P = num_panels(K);
+    if (M > 4 || gemv_rows((int)M) * P * 64 > kGemvQuantElems) return NVFP4_ERR_UNSUPPORTED;
+    *job = Job{};
+    job->kind = JOB_GEMV_QUANT;
+    GemvQuantArgs& g = job->gemvq;
+    g.x = x;
+    g.bf16 = bf16;
+    g.ldx = ldx;
+    g.b_codes = static_cast<const uint8_t*>(b_packed);
+    g.b_scales = static_cast<const uint8_t*>(b_scales);
+    g.out = static_cast<uint16_t*>(out);
+    g.alpha = alpha;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.Np = (int)round_up(N, kRowPad);
+    g.P = (int)P;
+    return NVFP4_OK;
+}
+
 hipError_t launch_job(const Job& job, int device, const WorkspacePtrs& ws, hipStream_t s) {
     if (job.empty) return hipSuccess;
+    if (job.kind == JOB_GEMV_QUANT) return launch_gemv_quant(job.gemvq, s);
     if (job.kind == JOB_GROUPED) return launch_grouped(job.grouped, s);
     if (job.kind == JOB_GROUPED_TILE) return launch_grouped_tile(job.gemm, s);
     if (job.kind == JOB_QUANTIZE) return launch_quantize(job.quant, s);
@@ -476,6 +507,15 @@ int nvfp4_quantize_bf16(const void* x, int64_t rows, int64_t K, int64_t ld, void
                         void* packed_scales, void* stream) {
     Job job;
     const int st = prepare_quantize(x, true, rows, K, ld, packed_codes, packed_scales, &job);
+    return st != NVFP4_OK ? st : run_job(job, stream);
+}
+
+int nvfp4_gemm_quantized(const void* x, int x_type, int64_t ldx, const void* b_packed,
+                         const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
+                         int64_t K, void* stream) {
+    Job job;
+    const int st = prepare_gemm_quantized(x, x_type, ldx, b_packed, b_scales, alpha, out, M, N, K,
+                                          &job);
     return st != NVFP4_OK ? st : run_job(job, stream);
 }
 

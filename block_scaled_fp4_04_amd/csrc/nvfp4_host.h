@@ -11,7 +11,13 @@
 
 namespace nvfp4 {
 
-enum JobKind { JOB_GEMM = 0, JOB_GROUPED = 1, JOB_QUANTIZE = 2, JOB_GROUPED_TILE = 3 };
+enum JobKind {
+    JOB_GEMM = 0,
+    JOB_GROUPED = 1,
+    JOB_QUANTIZE = 2,
+    JOB_GROUPED_TILE = 3,
+    JOB_GEMV_QUANT = 4
+};
 
 struct Job {
     int kind = JOB_GEMM;
@@ -22,6 +28,7 @@ struct Job {
     size_t counters = 0;         // split-K arrival counters the job needs
     GroupedArgs grouped{};       // JOB_GROUPED
     QuantArgs quant{};           // JOB_QUANTIZE
+    GemvQuantArgs gemvq{};       // JOB_GEMV_QUANT
     bool empty = false;          // nothing to launch (a grouped GEMM with no rows)
 };
 
@@ -35,6 +42,9 @@ int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_pa
                     void* out, int64_t M, int64_t N, int64_t K, Job* job);
 int prepare_quantize(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
                      void* packed_codes, void* packed_scales, Job* job);
+int prepare_gemm_quantized(const void* x, int x_type, int64_t ldx, const void* b_packed,
+                           const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
+                           int64_t K, Job* job);
 
 // The current device, checked to be a gfx950 GPU (status).
 int current_device(int* device);

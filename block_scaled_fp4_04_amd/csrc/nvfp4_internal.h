@@ -145,4 +145,23 @@ struct QuantArgs {
 };
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 
+// The dot-product GEMM with the quantisation of A folded in (M <= 4): A as
+// fp32 or bfloat16 rows, quantised per workgroup into LDS.
+struct GemvQuantArgs {
+    const void* x;    // M x K values (fp32, or bfloat16 if bf16), row stride ldx elements
+    bool bf16;
+    int64_t ldx;
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    uint16_t* out;
+    float alpha;
+    int M, N, K;
+    int Np, P;        // B's padded rows, 64-element panels
+};
+// Rows of A (rounded up to 1, 2 or 4) x Kp held in LDS at most: 32 KB of
+// codes and 4 KB of scales.
+constexpr int kGemvQuantElems = 65536;
+inline int gemv_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
+hipError_t launch_gemv_quant(const GemvQuantArgs& a, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -20,6 +20,7 @@
 // contiguous, as long as A and B lanes agree and each 8-element group stays
 // inside one 16-element scale block.
 #include "nvfp4_device.h"
+#include "nvfp4_quant_device.h"
 
 namespace nvfp4 {
 namespace {
@@ -1117,6 +1118,50 @@ __device__ __forceinline__ float wave_sum_lane63(float x) {
     return x;
 }
 
+// The dot products of one batch: lane `lane` holds half-panels base + lane,
+// base + lane + 64, ... of B (codes bw, scale words bsc) and of the MR rows
+// of A (aw, asc); a half-panel past hp_total is weighted by zero.
+template <int MR, int HPL>
+__device__ __forceinline__ void gemv_batch(const uint4 (&bw)[HPL], const uint32_t (&bsc)[HPL],
+                                           const uint4 (&aw)[HPL][MR],
+                                           const uint32_t (&asc)[HPL][MR], int base, int lane,
+                                           int hp_total, float (&acc)[MR]) {
+#pragma unroll
+    for (int i = 0; i < HPL; ++i) {
+        const bool live = base + lane + 64 * i < hp_total;
+        const h2 sb = e4m3x2_lo(bsc[i]);       // B scales of the half-panel's two blocks
+        h2 sa[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) sa[m] = e4m3x2_lo(asc[i][m]);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            float bs[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) bs[m] = 0.0f;
+#pragma unroll
+            for (int wd = 0; wd < 2; ++wd) {
+                const uint32_t w = word_of(bw[i], 2 * blk + wd);
+                const h2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+                const h2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+                const h2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+                const h2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const uint32_t v = word_of(aw[i][m], 2 * blk + wd);
+                    bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0), b0, bs[m], false);
+                    bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1), b1, bs[m], false);
+                    bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2), b2, bs[m], false);
+                    bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3), b3, bs[m], false);
+                }
+            }
+            const float sbf = live ? (float)sb[blk] : 0.0f;
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                acc[m] = __builtin_fmaf(bs[m], live ? (float)sa[m][blk] * sbf : 0.0f, acc[m]);
+        }
+    }
+}
+
 // Four waves (rows of B) per workgroup: 4 consecutive rows share every
 // 128-byte line of a packed panel (32 bytes each), so each workgroup reads
 // whole lines.  Workgroups are dealt to the 8 XCDs in turn; the workgroup
@@ -1175,40 +1220,154 @@ __global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(
                 asc[i][m] = *reinterpret_cast<const uint16_t*>(a_scales + arow * 4 + half * 2);
             }
         }
+        gemv_batch<MR, HPL>(bw, bsc, aw, asc, base, lane, hp_total, acc);
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = wave_sum_lane63(acc[m]);
+    if (lane == 63 && n < N) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            if (m < M) out[(int64_t)m * N + n] = to_bf16(alpha * acc[m]);
+    }
+}
+
+// The dot-product kernel with the quantisation of A folded in: A arrives as
+// fp32 or bfloat16 rows (T: float or uint16_t), and the workgroup quantises
+// them itself, with the quantiser's rule and functions, so that the result
+// is bit for bit that of nvfp4_quantize followed by the dot-product kernel
+// -- one launch instead of two for a decode step's GEMM.
+//   * Every wave first issues the loads of its row of B (as above); while
+//     they are in flight, the workgroup's lanes quantise the MR rows of A
+//     (two lanes per 16-element block, the block's amax combined over the
+//     pair by one DPP exchange) into LDS in the packed form the dot products
+//     read: codes [panel][row][32 bytes], scales [panel][row][4 bytes], rows
+//     M..MR-1 and the blocks past K as zeros;
+//   * after one barrier each lane reads its half-panels of A from LDS and
+//     the dot products run exactly as in gemv_kernel.
+// Every workgroup quantises all of A (it needs all of it), so WAVES rows of
+// B per workgroup trade the quantisation work per lane against the number
+// of workgroups streaming B.
+// Rows of B per workgroup.
+constexpr int kGemvQuantWaves = 8;
+
+template <int MR, int HPL, int WAVES, typename T>
+__global__ void __launch_bounds__(64 * WAVES) gemv_quant_kernel(
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
+    const T* __restrict__ x, int64_t ldx, int Np, int P, int total, int K,
+    uint16_t* __restrict__ out, float alpha, int M, int N) {
+    __shared__ __attribute__((aligned(16))) uint8_t qa_codes[kGemvQuantElems / 2];
+    __shared__ __attribute__((aligned(16))) uint8_t qa_scales[kGemvQuantElems / 16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int q8 = total >> 3, r8 = total & 7;
+    const int xcd = blockIdx.x & 7;
+    const int bid = xcd * q8 + min(xcd, r8) + (int)(blockIdx.x >> 3);
+    const int n = bid * WAVES + (tid >> 6);   // B row (< Np: the grid is Np / WAVES)
+    const int hp_total = P * 2;
+
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+
+    uint4 bw[HPL];
+    uint32_t bsc[HPL];
+    auto load_b = [&](int base) {
 #pragma unroll
         for (int i = 0; i < HPL; ++i) {
-            const bool live = base + lane + 64 * i < hp_total;
-            const h2 sb = e4m3x2_lo(bsc[i]);       // B scales of the half-panel's two blocks
-            h2 sa[MR];
+            const int hp = min(base + lane + 64 * i, hp_total - 1);
+            const int64_t brow = (int64_t)(hp >> 1) * Np + n;
+            bw[i] = *reinterpret_cast<const uint4*>(b_codes + brow * 32 + (hp & 1) * 16);
+            bsc[i] = *reinterpret_cast<const uint16_t*>(b_scales + brow * 4 + (hp & 1) * 2);
+        }
+    };
+    auto batch = [&](int base) {
+        uint4 aw[HPL][MR];
+        uint32_t asc[HPL][MR];
 #pragma unroll
-            for (int m = 0; m < MR; ++m) sa[m] = e4m3x2_lo(asc[i][m]);
+        for (int i = 0; i < HPL; ++i) {
+            const int hp = min(base + lane + 64 * i, hp_total - 1);
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                float bs[MR];
-#pragma unroll
-                for (int m = 0; m < MR; ++m) bs[m] = 0.0f;
-#pragma unroll
-                for (int wd = 0; wd < 2; ++wd) {
-                    const uint32_t w = word_of(bw[i], 2 * blk + wd);
-                    const h2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-                    const h2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-                    const h2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-                    const h2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
-#pragma unroll
-                    for (int m = 0; m < MR; ++m) {
-                        const uint32_t v = word_of(aw[i][m], 2 * blk + wd);
-                        bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0), b0, bs[m], false);
-                        bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1), b1, bs[m], false);
-                        bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2), b2, bs[m], false);
-                        bs[m] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3), b3, bs[m], false);
-                    }
-                }
-                const float sbf = live ? (float)sb[blk] : 0.0f;
-#pragma unroll
-                for (int m = 0; m < MR; ++m)
-                    acc[m] = __builtin_fmaf(bs[m], live ? (float)sa[m][blk] * sbf : 0.0f, acc[m]);
+            for (int m = 0; m < MR; ++m) {
+                const int slot = (hp >> 1) * MR + m;
+                aw[i][m] = *reinterpret_cast<const uint4*>(qa_codes + slot * 32 + (hp & 1) * 16);
+                asc[i][m] = *reinterpret_cast<const uint16_t*>(qa_scales + slot * 4 + (hp & 1) * 2);
             }
         }
+        gemv_batch<MR, HPL>(bw, bsc, aw, asc, base, lane, hp_total, acc);
+    };
+
+    // Quantise A: half-block j = (row m, 16-element block b of Kp, half h);
+    // the two halves of a block are adjacent lanes, and the work is a whole
+    // number of pairs, so both lanes of a pair take the same rounds.  Loads
+    // are clamped into the input (row to M - 1, elements to end by K); what
+    // they bring in for padding rows or past K is written as zero.  The
+    // loads of the first QR rounds go out before B's (the wait for them
+    // then does not include B's, which arrive in order behind them).
+    const int items = MR * P * 8;
+    auto load_x = [&](int j, float (&v)[8]) {
+        const int m = j / (P * 8), b = (j >> 1) % (P * 4), h = j & 1;
+        const T* src = x + (int64_t)min(m, M - 1) * ldx + min(b * 16 + h * 8, K - 8);
+        if constexpr (sizeof(T) == 2) {
+            const uint4 q = *reinterpret_cast<const uint4*>(src);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+                v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+            }
+        } else {
+            const uint4 q0 = reinterpret_cast<const uint4*>(src)[0];
+            const uint4 q1 = reinterpret_cast<const uint4*>(src)[1];
+            const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(float, w[i]);
+        }
+    };
+    auto quantise = [&](int j, const float (&v)[8]) {
+        const int m = j / (P * 8), b = (j >> 1) % (P * 4), h = j & 1;
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+        const float o = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, false));
+        amax = __builtin_fmaxf(amax, o);
+        const uint32_t sb = e4m3_nearest(amax / 6.0f);
+        const float sv = e4m3_value(sb);
+        const bool has = m < M && b * 16 < K;
+        const uint32_t w = has ? e2m1_word(v, e2m1_search(sv), sv > 0.0f ? 7u : 0u) : 0u;
+        const int slot = (b >> 2) * MR + m;
+        *reinterpret_cast<uint32_t*>(qa_codes + slot * 32 + (b & 3) * 8 + h * 4) = w;
+        if (h == 0) qa_scales[slot * 4 + (b & 3)] = has ? (uint8_t)sb : (uint8_t)0;
+    };
+    constexpr int QR = 4;
+    constexpr int STRIDE = 64 * WAVES;
+    float xv[QR][8];
+#pragma unroll
+    for (int r = 0; r < QR; ++r) load_x(min(tid + r * STRIDE, items - 1), xv[r]);  // (clamped: unused past items)
+    __builtin_amdgcn_sched_barrier(0);  // (keeps these loads ahead of B's)
+    load_b(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // (every loaded value is taken here, after B's loads were issued: with
+    // the values used only inside the branches below, the compiler would
+    // move each load into its branch, behind B's)
+#pragma unroll
+    for (int r = 0; r < QR; ++r)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(xv[r][i]));
+#pragma unroll
+    for (int r = 0; r < QR; ++r)
+        if (tid + r * STRIDE < items) quantise(tid + r * STRIDE, xv[r]);
+    for (int j = tid + QR * STRIDE; j < items; j += STRIDE) {
+        float v[8];
+        load_x(j, v);
+        quantise(j, v);
+    }
+    __syncthreads();
+
+    batch(0);
+    for (int base = 64 * HPL; base < hp_total; base += 64 * HPL) {
+        load_b(base);
+        batch(base);
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[m] = wave_sum_lane63(acc[m]);
@@ -1381,6 +1540,33 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t stream) {
         NVFP4_GEMV_CASE(4, 1) NVFP4_GEMV_CASE(4, 2) NVFP4_GEMV_CASE(4, 3) NVFP4_GEMV_CASE(4, 4)
 #undef NVFP4_GEMV_CASE
         default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_quant(const GemvQuantArgs& a, hipStream_t stream) {
+    constexpr int W = kGemvQuantWaves;
+    const dim3 grid((unsigned)(a.Np / W)), block(64 * W);   // Np % 16 == 0
+    const int hpl = std::min(4, (2 * a.P + 63) / 64);
+    const int mr = gemv_rows(a.M);
+    switch ((mr * 8 + hpl) * 2 + (a.bf16 ? 1 : 0)) {
+#define NVFP4_GEMVQ_CASE(MR, HPL)                                                                  \
+        case (MR * 8 + HPL) * 2:                                                                   \
+            hipLaunchKernelGGL((gemv_quant_kernel<MR, HPL, W, float>), grid, block, 0, stream,     \
+                               a.b_codes, a.b_scales, static_cast<const float*>(a.x), a.ldx, a.Np, \
+                               a.P, (int)grid.x, a.K, a.out, a.alpha, a.M, a.N);                   \
+            break;                                                                                 \
+        case (MR * 8 + HPL) * 2 + 1:                                                               \
+            hipLaunchKernelGGL((gemv_quant_kernel<MR, HPL, W, uint16_t>), grid, block, 0, stream,  \
+                               a.b_codes, a.b_scales, static_cast<const uint16_t*>(a.x), a.ldx,    \
+                               a.Np, a.P, (int)grid.x, a.K, a.out, a.alpha, a.M, a.N);             \
+            break;
+        NVFP4_GEMVQ_CASE(1, 1) NVFP4_GEMVQ_CASE(1, 2) NVFP4_GEMVQ_CASE(1, 3) NVFP4_GEMVQ_CASE(1, 4)
+        NVFP4_GEMVQ_CASE(2, 1) NVFP4_GEMVQ_CASE(2, 2) NVFP4_GEMVQ_CASE(2, 3) NVFP4_GEMVQ_CASE(2, 4)
+        NVFP4_GEMVQ_CASE(4, 1) NVFP4_GEMVQ_CASE(4, 2) NVFP4_GEMVQ_CASE(4, 3) NVFP4_GEMVQ_CASE(4, 4)
+#undef NVFP4_GEMVQ_CASE
+        default:
+            return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

@@ -115,6 +115,17 @@ int nvfp4_sequence_add_quantize(nvfp4_sequence_t seq, const float* x, int64_t ro
     return add_job(seq, st, job);
 }
 
+int nvfp4_sequence_add_gemm_quantized(nvfp4_sequence_t seq, const void* x, int x_type,
+                                      int64_t ldx, const void* b_packed, const void* b_scales,
+                                      float alpha, void* out, int64_t M, int64_t N, int64_t K) {
+    if (!seq) return NVFP4_ERR_INVALID_VALUE;
+    if (seq->finalized) return NVFP4_ERR_STATE;
+    Job job;
+    const int st = prepare_gemm_quantized(x, x_type, ldx, b_packed, b_scales, alpha, out, M, N, K,
+                                          &job);
+    return add_job(seq, st, job);
+}
+
 int nvfp4_sequence_add_quantize_bf16(nvfp4_sequence_t seq, const void* x, int64_t rows, int64_t K,
                                      int64_t ld, void* packed_codes, void* packed_scales) {
     if (!seq) return NVFP4_ERR_INVALID_VALUE;

@@ -208,6 +208,34 @@ int nvfp4_quantize(const float* x, int64_t rows, int64_t K, int64_t ld, void* pa
 int nvfp4_quantize_bf16(const void* x, int64_t rows, int64_t K, int64_t ld, void* packed_codes,
                         void* packed_scales, void* stream);
 
+/* Element types of activation rows given to nvfp4_gemm_quantized. */
+enum { NVFP4_INPUT_F32 = 0, NVFP4_INPUT_BF16 = 1 };
+
+/* Decode-step GEMM from unquantised activations, in one launch:
+ *   C = nvfp4_gemm(quantize(X), B)
+ * bit for bit, where quantize is the rule of nvfp4_quantize (fp32 rows) or
+ * nvfp4_quantize_bf16 (bfloat16 rows).  At one to four rows the
+ * quantisation launch costs as much as the GEMM's own work, and the pages'
+ * decode regime is exactly such batches ("Peeling the Kernel Onion",
+ * sections "The Critical Connection to Real Inference" and "Knowledge
+ * Created and Its Impact": per-call overhead dominates small GEMMs).  Each
+ * workgroup of the dot-product kernel quantises X into LDS itself while
+ * its rows of B arrive.
+ *   x        : DEVICE, M x K values of type x_type (NVFP4_INPUT_F32 or
+ *              NVFP4_INPUT_BF16), row stride ldx elements (ldx >= K; ldx % 4
+ *              == 0 for fp32, % 8 for bfloat16)
+ *   b_packed, b_scales : DEVICE, B (N x K) packed by nvfp4_pack
+ *   out      : DEVICE, M x N bfloat16, row-major, overwritten
+ *   M        : 1..4 (NVFP4_ERR_UNSUPPORTED above); the rows rounded up to 1,
+ *              2 or 4 times K rounded up to 128 must be at most 65536
+ *              (NVFP4_ERR_UNSUPPORTED otherwise: the quantised rows live in
+ *              LDS)
+ * Same alignment, status and stream rules as nvfp4_gemm; no workspace, no
+ * allocation; the quantised A is not written out. */
+int nvfp4_gemm_quantized(const void* x, int x_type, int64_t ldx, const void* b_packed,
+                         const void* b_scales, float alpha, void* out, int64_t M, int64_t N,
+                         int64_t K, void* stream);
+
 /* Grouped GEMM for mixture-of-experts layers: `groups` weight operands B_g
  * (each N x K) share one launch; group g owns rows
  * row_offsets[g] .. row_offsets[g+1]-1 of A and of C:
@@ -310,8 +338,8 @@ const char* nvfp4_build_id(void);
  *   nvfp4_sequence_create   : an empty sequence (host object, caller-owned)
  *   nvfp4_sequence_add_*    : append one call; arguments and checks as for
  *                             nvfp4_gemm / nvfp4_grouped_gemm / nvfp4_quantize
- *                             / nvfp4_quantize_bf16 (minus the stream); the
- *                             plan is fixed here.
+ *                             / nvfp4_quantize_bf16 / nvfp4_gemm_quantized
+ *                             (minus the stream); the plan is fixed here.
  *                             Buffers are used by address at every launch:
  *                             they must stay allocated for the sequence's
  *                             lifetime, and their contents are read when the
@@ -348,6 +376,9 @@ int nvfp4_sequence_add_quantize(nvfp4_sequence_t seq, const float* x, int64_t ro
 int nvfp4_sequence_add_quantize_bf16(nvfp4_sequence_t seq, const void* x, int64_t rows,
                                      int64_t K, int64_t ld, void* packed_codes,
                                      void* packed_scales);
+int nvfp4_sequence_add_gemm_quantized(nvfp4_sequence_t seq, const void* x, int x_type,
+                                      int64_t ldx, const void* b_packed, const void* b_scales,
+                                      float alpha, void* out, int64_t M, int64_t N, int64_t K);
 int nvfp4_sequence_finalize(nvfp4_sequence_t seq);
 int nvfp4_sequence_launch(nvfp4_sequence_t seq, void* stream);
 int nvfp4_sequence_destroy(nvfp4_sequence_t seq);

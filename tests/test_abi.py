@@ -180,6 +180,28 @@ def test_quantize_bf16_rejects_bad_arguments_before_launch():
     assert q(0x3000, 4, 64, 64, 0x1000, 0x2004, None) == nv.ERR_MISALIGNED
 
 
+def test_gemm_quantized_rejects_bad_arguments_before_launch():
+    """nvfp4_gemm_quantized: the GEMM's rules plus the activation rows' own
+    (element type, row stride, at most 4 rows, rows x Kp within LDS)."""
+    f = nv.lib().nvfp4_gemm_quantized
+
+    def call(x=0x1000, t=nv.INPUT_F32, ld=64, b=0x3000, sb=0x4000, out=0x5000, M=1, N=8, K=64):
+        return f(x, t, ld, b, sb, 1.0, out, M, N, K, None)
+    assert call(x=None) == nv.ERR_INVALID_VALUE
+    assert call(out=None) == nv.ERR_INVALID_VALUE
+    assert call(t=2) == nv.ERR_INVALID_VALUE
+    assert call(M=0) == nv.ERR_INVALID_VALUE
+    assert call(K=24, ld=24) == nv.ERR_INVALID_VALUE            # K % 16
+    assert call(ld=32) == nv.ERR_INVALID_VALUE                  # ld < K
+    assert call(ld=66) == nv.ERR_INVALID_VALUE                  # fp32 rows: ld % 4
+    assert call(t=nv.INPUT_BF16, ld=68) == nv.ERR_INVALID_VALUE  # bfloat16 rows: ld % 8
+    assert call(x=0x1008) == nv.ERR_MISALIGNED
+    assert call(b=0x3004) == nv.ERR_MISALIGNED
+    assert call(M=5) == nv.ERR_UNSUPPORTED                      # decode rows only
+    assert call(M=1, K=65664, ld=65664) == nv.ERR_UNSUPPORTED   # 1 x 65664 > 65536 in LDS
+    assert call(M=3, K=16512, ld=16512) == nv.ERR_UNSUPPORTED   # rounded to 4 rows
+
+
 def test_python_gemm_rejects_k_mismatch():
     a = nv.PackedOperand(None, None, 4, 128)
     b = nv.PackedOperand(None, None, 4, 256)
@@ -251,12 +273,16 @@ def test_sequence_state_and_validation():
         assert q(h, 0x3000, 4, 64, 32, 0x1000, 0x2000) == nv.ERR_INVALID_VALUE
         qb = lib.nvfp4_sequence_add_quantize_bf16
         assert qb(h, 0x3000, 4, 64, 68, 0x1000, 0x2000) == nv.ERR_INVALID_VALUE   # ld % 8
+        gq = lib.nvfp4_sequence_add_gemm_quantized
+        assert gq(h, 0x3000, nv.INPUT_F32, 64, 0x1000, 0x2000, 1.0, 0x5000, 5, 8, 64) \
+            == nv.ERR_UNSUPPORTED
         # nothing recorded: nothing to finalize; not finalized: no launch
         assert lib.nvfp4_sequence_finalize(h) == nv.ERR_INVALID_VALUE
         assert lib.nvfp4_sequence_launch(h, None) == nv.ERR_STATE
         assert add(h, 0x1000, 0x2000, 0x3000, 0x4000, 1.0, 0x5000, 4, 4, 64) == nv.OK
         assert q(h, 0x3000, 4, 64, 64, 0x1000, 0x2000) == nv.OK
         assert qb(h, 0x3000, 4, 64, 72, 0x1000, 0x2000) == nv.OK
+        assert gq(h, 0x3000, nv.INPUT_BF16, 72, 0x1000, 0x2000, 1.0, 0x5000, 2, 8, 64) == nv.OK
         assert g(h, 0x1000, 0x2000, 0x3000, 0x4000, 0x6000, 2, 1.0, 0x5000, 0, 4, 64) == nv.OK
     finally:
         assert lib.nvfp4_sequence_destroy(h) == nv.OK

@@ -34,6 +34,7 @@ hipError_t launch_gemv(const GemmArgs&, hipStream_t) { return hipErrorInvalidVal
 hipError_t launch_grouped(const GroupedArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_grouped_tile(const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_quantize(const QuantArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_gemv_quant(const GemvQuantArgs&, hipStream_t) { return hipErrorInvalidValue; }
 size_t tile_partial_floats(int, const GemmArgs&) { return 0; }
 size_t tile_counters(int, const GemmArgs&) { return 0; }
 size_t skinny_flagged_words(const GemmArgs&) { return 0; }
