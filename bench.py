@@ -68,7 +68,7 @@ COPY_BYTES = 256 << 20   # size of the copy used to scale the HBM counters
 CSRC = os.path.join(ROOT, "block_scaled_fp4_04_amd", "csrc")
 # the sources whose code the counters of a workload depend on
 KERNEL_SOURCES = {
-    "gemm": ["nvfp4_internal.h", "nvfp4_device.h", "nvfp4_kernels.hip"],
+    "gemm": ["nvfp4_internal.h", "nvfp4_device.h", "nvfp4_quant_device.h", "nvfp4_kernels.hip"],
     "grouped": ["nvfp4_internal.h", "nvfp4_device.h", "nvfp4_grouped.hip"],
 }
 

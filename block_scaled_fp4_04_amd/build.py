@@ -19,7 +19,7 @@ SOURCES = [os.path.join(CSRC, "nvfp4_api.cpp"), os.path.join(CSRC, "nvfp4_plan.c
 # what the kernels and their launches are built from
 KERNEL_FILES = [os.path.join(CSRC, f) for f in ("nvfp4_kernels.hip", "nvfp4_grouped.hip",
                                                 "nvfp4_quantize.hip", "nvfp4_internal.h",
-                                                "nvfp4_device.h")]
+                                                "nvfp4_device.h", "nvfp4_quant_device.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
