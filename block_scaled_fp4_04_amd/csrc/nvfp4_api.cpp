@@ -381,7 +381,7 @@ const char* nvfp4_status_string(int status) {
     }
 }
 
-int nvfp4_version(void) { return 10300; }
+int nvfp4_version(void) { return 10400; }
 
 int nvfp4_packed_size(int64_t rows, int64_t K, size_t* code_bytes, size_t* scale_bytes) {
     if (!code_bytes || !scale_bytes || !valid_rows_k(rows, K)) return NVFP4_ERR_INVALID_VALUE;
