@@ -196,13 +196,58 @@ def _operand_sets(nv, torch, cfg, ops, cold):
              torch.empty_like(out)) for _ in range(n)]
 
 
+WARM_MS = 50.0          # device time a captured graph replays before its timed replay
+MAX_WARM_REPLAYS = 2000
+
+
+def timed_replay(torch, gr, stream, calls, warm_ms=WARM_MS):
+    """Per-call device time of the captured graph `gr` (holding `calls`
+    calls), measured on a warm GPU with the host ahead of the device.
+
+    One replay sizes the warm-up; after a synchronisation, replays making
+    about `warm_ms` of device time (two at least) and then the timed replay,
+    between two HIP events on `stream`, are enqueued back to back, and the
+    device is synchronised again.  Two effects are kept out of the figure:
+    * the first replays after a capture or an idle gap run slow (the grouped
+      GEMM's graph of 50 calls: 56, 52, 50 us per call in replays 2-4, about
+      43 us from the tenth on; an empty kernel's first replay after 1 s idle:
+      7.4 us per call against 1.76);
+    * the host can take longer to enqueue a graph than the device takes to
+      run it (50 decode-sized calls: 40-70 us to enqueue as a rule, up to
+      600 us right after a long backlog drained), so a timed replay enqueued
+      onto an idle device would time the host.
+    Returns (ms per call of the timed replay, warm replays, wall seconds from
+    the first warm replay to the end of the timed one)."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        gr.replay()
+        stop.record(stream)
+    stop.synchronize()
+    first = max(start.elapsed_time(stop), 1e-3)
+    more = int(min(MAX_WARM_REPLAYS - 1, max(1, -(-(warm_ms - first) // first))))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(more):
+            gr.replay()
+        start.record(stream)
+        gr.replay()
+        stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / calls, 1 + more, wall
+
+
 def time_workload(nv, torch, cfg, steps, warmup, cold=False, ops=None):
     """Per-call time of nvfp4_gemm on resident operands.
 
     'graph': the `steps` calls are captured once into a HIP graph (no memset
-    or allocation inside: the split-K workspace exists after the warm-up) and
-    the graph is replayed between two events, so the figure is the device
-    time per call without host launch overhead.  'eager': the same calls
+    or allocation inside: the split-K workspace exists after the warm-up),
+    warmed by replays and replayed once more between two events
+    (timed_replay), so the figure is the device time per call without host
+    launch overhead.  'eager': the same calls
     issued one by one from Python between two events (host overhead
     included when the host is slower than the device)."""
     if ops is None:
@@ -237,24 +282,16 @@ def time_workload(nv, torch, cfg, steps, warmup, cold=False, ops=None):
         for i in range(steps):
             x, y, o = sets[i % len(sets)]
             nv.gemm(x, y, cfg.alpha, out=o, stream=cap)
-    with torch.cuda.stream(stream):
-        g.replay()                       # warm replay
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        g.replay()
-        stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    graph_ms = start.elapsed_time(stop) / steps
+    graph_ms, warm_replays, wall = timed_replay(torch, g, stream, steps)
     plan = nv.plan(cfg.M, cfg.N, cfg.K)
     # the timed replay's own output (warm: every call wrote the one output
     # buffer), copied out after the timing for the parity check
     out_bits = None if cold else sets[0][2].view(torch.int16).cpu().numpy().astype(np.uint16)
+    copies = len(sets)
     del g, sets
     return {"graph_ms": graph_ms, "eager_ms": eager_ms, "wall_s": wall, "plan": plan, "ops": ops,
-            "out_bits": out_bits}
+            "out_bits": out_bits, "warm_replays": warm_replays, "calls_per_replay": steps,
+            "operand_copies": copies}
 
 
 def grouped_roofline(g, seconds_per_call):
@@ -296,17 +333,11 @@ def time_grouped(nv, torch, g, steps, warmup, ops=None, cold=False):
         for i in range(steps):
             x, y, o = sets[i % len(sets)]
             nv.grouped_gemm(x, y, off, g.alpha, out=o, stream=cap)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        gr.replay()
-        start.record(stream)
-        gr.replay()
-        stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
+    ms, warm_replays, _ = timed_replay(torch, gr, stream, steps)
+    copies = len(sets)
     del gr, sets
-    return {"graph_ms": ms, "ops": ops}
+    return {"graph_ms": ms, "ops": ops, "warm_replays": warm_replays, "calls_per_replay": steps,
+            "operand_copies": copies}
 
 
 def grouped_line(nv, torch, steps, warmup):
@@ -322,6 +353,8 @@ def grouped_line(nv, torch, steps, warmup):
                     "roofline": dict(grouped_roofline(g, ms * 1e-3), traffic=stored_traffic(g)),
                     "cold": {"ms": cms, "tflops": synth.flops(g.M, g.N, g.K) / (cms * 1e-3) / 1e12,
                              "roofline": grouped_roofline(g, cms * 1e-3),
+                             "operand_copies": c["operand_copies"],
+                             "calls_per_replay": c["calls_per_replay"],
                              "note": "operand copies rotated beyond the last-level cache"},
                     "path": "grouped",
                     "pages_tflops_other_gpu": None}
@@ -356,15 +389,7 @@ def quantize_line(nv, torch, rows, K, steps, warmup, bf16=False):
         cap = torch.cuda.current_stream()
         for _ in range(steps):
             nv.quantize(x, out=out, stream=cap)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        gr.replay()
-        start.record(stream)
-        gr.replay()
-        stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
+    ms, _, _ = timed_replay(torch, gr, stream, steps)
     b = quantize_bytes(rows, K, 2 if bf16 else 4)
     ach = b / (ms * 1e-3) / 1e9
     del gr
@@ -425,13 +450,22 @@ def decode_sequence_line(nv, torch, steps, warmup):
     seq_f.finalize()
 
     def timed(fn):
-        with torch.cuda.stream(stream):
-            for _ in range(max(1, warmup)):
-                fn()
-        stream.synchronize()
+        # warm-up as in timed_replay: `warmup` steps, then as many more as
+        # make about WARM_MS of device time, with the timed steps enqueued
+        # right behind them (a warm GPU, and the host ahead of the device
+        # when the timed region starts)
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
+            start.record(stream)
+            for _ in range(max(1, warmup)):
+                fn()
+            stop.record(stream)
+        stop.synchronize()
+        per = max(start.elapsed_time(stop) / max(1, warmup), 1e-3)
+        with torch.cuda.stream(stream):
+            for _ in range(int(min(MAX_WARM_REPLAYS, max(1, WARM_MS // per)))):
+                fn()
             start.record(stream)
             for _ in range(steps):
                 fn()
@@ -484,16 +518,9 @@ def fused_projection_line(nv, torch, steps, warmup):
                 cap = torch.cuda.current_stream()
                 for _ in range(steps):
                     fn(cap)
-            start = torch.cuda.Event(enable_timing=True)
-            stop = torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(stream):
-                gr.replay()
-                start.record(stream)
-                gr.replay()
-                stop.record(stream)
-            torch.cuda.synchronize()
+            ms, _, _ = timed_replay(torch, gr, stream, steps)
             del gr
-            return start.elapsed_time(stop) * 1000.0 / steps
+            return ms * 1000.0
 
         two = per_call(lambda s: (nv.quantize(x, out=a, stream=s), nv.gemm(a, b, 0.5, out=o2, stream=s)))
         one = per_call(lambda s: nv.gemm_quantized(x, b, 0.5, out=o1, stream=s))
@@ -520,16 +547,11 @@ def floors_line(nv, torch, steps):
         cap = torch.cuda.current_stream()
         for _ in range(steps):
             nv.probe_empty(blocks, threads, stream=cap)
+    empty_ms, _, _ = timed_replay(torch, g, stream, steps)
+    empty_us = empty_ms * 1000.0
+    del g
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        g.replay()
-        start.record(stream)
-        g.replay()
-        stop.record(stream)
-    torch.cuda.synchronize()
-    empty_us = start.elapsed_time(stop) * 1000.0 / steps
-    del g
     lat = {}
     out = torch.zeros(1, dtype=torch.int32, device="cuda")
     # HBM first, on a buffer no load has touched (4x the last-level cache);
@@ -586,16 +608,9 @@ def measured_peaks(nv, torch, steps):
         with torch.cuda.graph(g, stream=stream):
             for _ in range(reps):
                 fn()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            g.replay()
-            start.record(stream)
-            g.replay()
-            stop.record(stream)
-        torch.cuda.synchronize()
+        ms, _, _ = timed_replay(torch, g, stream, reps)
         del g
-        return start.elapsed_time(stop) / reps
+        return ms
 
     blocks, iters = 1024, 2000
     mout = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
@@ -761,17 +776,22 @@ def main():
                    "split_k": plan["split_k"], "tile": [plan["tile_m"], plan["tile_n"]],
                    "operands": "E2M1 codes + E4M3 per-16 scales (packed), bf16 out, "
                                "fp16 MFMA with fp32 accumulation",
-                   "timing": "HIP graph of the timed calls replayed between HIP events",
+                   "timing": "HIP graph of the timed calls, replayed for about "
+                             f"{WARM_MS:g} ms of device time and then once more between HIP "
+                             "events, enqueued behind the warm replays",
                    "parallelism": "none (1 GPU)"},
         "roofline": dict(roofline_for(cfg, ms * 1e-3), traffic=stored_traffic(cfg)),
         "eager_ms_per_step": r["eager_ms"],
-        "wall_s_timed_region": r["wall_s"],
+        "warm_replays": r["warm_replays"],
+        "wall_s_warm_and_timed_replays": r["wall_s"],
     }
     if args.cold or not args.only_headline:
         c = time_workload(nv, torch, cfg, args.steps, args.warmup, cold=True, ops=ops)
         line["cold"] = {"ms_per_step": c["graph_ms"],
                         "tflops": synth.flops(cfg.M, cfg.N, cfg.K) / (c["graph_ms"] * 1e-3) / 1e12,
                         "roofline": roofline_for(cfg, c["graph_ms"] * 1e-3),
+                        "operand_copies": c["operand_copies"],
+                        "calls_per_replay": c["calls_per_replay"],
                         "note": "operand copies rotated beyond the last-level cache"}
     if not args.only_headline:
         per = {}
@@ -810,6 +830,8 @@ def main():
                     "ms": cc["graph_ms"],
                     "tflops": synth.flops(c.M, c.N, c.K) / (cc["graph_ms"] * 1e-3) / 1e12,
                     "roofline": roofline_for(c, cc["graph_ms"] * 1e-3),
+                    "operand_copies": cc["operand_copies"],
+                    "calls_per_replay": cc["calls_per_replay"],
                     "note": "operand copies rotated beyond the last-level cache"}
         line["per_shape"] = per
         torch.cuda.empty_cache()

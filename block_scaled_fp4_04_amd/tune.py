@@ -6,8 +6,11 @@ For each shape it times the library's own plan and a set of candidate plans
 (kernel path, output tile, split-K) through nvfp4_gemm_with_plan, and keeps
 the fastest; the library's plan is kept unless another is at least 2% faster
 (the run-to-run spread of these timings is about 1%).  Timing: the calls are
-captured in a HIP graph and replayed, so the figure is device time per call
-without launch gaps; the best of three replays is kept.
+captured in a HIP graph, replayed for about WARM_MS of device time and then
+three more times between HIP events, all enqueued back to back so that the
+device never waits for the host (enqueueing a graph of short calls can take
+longer than running it) and runs at the clock it keeps under load; the best
+of the three timed replays is kept.
 
 Operands are seeded N(0, 1) values quantised on the GPU by nvfp4_quantize
 (the power-limited clock of the MFMA-bound shapes depends on the data, so
@@ -34,6 +37,7 @@ M_SWEEP = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
 EXTRA_SHAPES = [(1, 2048, 6144)]
 KEEP_MARGIN = 0.02
 SKINNY_MAX_SPLIT = 16  # the skinny kernel's last arrival fetches one split per wave (16 waves)
+WARM_MS = 10.0         # device time of the warm replays before a plan's timed replays
 
 
 def shapes(quick: bool) -> list[tuple[int, int, int]]:
@@ -83,7 +87,8 @@ def make_operand(rows: int, K: int, seed: int, device):
 
 
 def time_plan(a, b, out, plan, stream, reps: int) -> float:
-    """Device microseconds per call of one plan (best of three replays)."""
+    """Device microseconds per call of one plan (best of three timed
+    replays behind about WARM_MS of warm replays)."""
     import torch
     path, tile, split = plan
     with torch.cuda.stream(stream):
@@ -94,17 +99,24 @@ def time_plan(a, b, out, plan, stream, reps: int) -> float:
     with torch.cuda.graph(g, stream=stream):
         for _ in range(reps):
             nv.gemm(a, b, 1.0, out=out, path=path, tile=tile, split_k=split, stream=stream)
-    best = float("inf")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(4)]
     with torch.cuda.stream(stream):
+        ev[0][0].record(stream)
         g.replay()
-        for _ in range(3):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+        ev[0][1].record(stream)
+    ev[0][1].synchronize()
+    first = max(ev[0][0].elapsed_time(ev[0][1]), 1e-3)
+    warm = int(min(500, max(1, WARM_MS // first)))
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            g.replay()
+        for e0, e1 in ev[1:]:
             e0.record(stream)
             g.replay()
             e1.record(stream)
-            e1.synchronize()
-            best = min(best, e0.elapsed_time(e1) * 1000.0 / reps)
+    stream.synchronize()
+    best = min(e0.elapsed_time(e1) for e0, e1 in ev[1:]) * 1000.0 / reps
     del g
     return best
 
@@ -167,8 +179,9 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
     doc = {"format": "nvfp4-plan-table", "version": 1, "arch": "gfx950",
            "build": nv.build_id(),
-           "how": "device time per call in HIP graph replay, best of 3; operands N(0,1) "
-                  "quantised; library plan kept unless another is 2% faster",
+           "how": "device time per call in HIP graph replay, best of 3 behind "
+                  f"{WARM_MS:g} ms of warm replays; operands N(0,1) quantised; library "
+                  "plan kept unless another is 2% faster",
            "entries": entries}
     tmp = args.out + ".tmp"
     with open(tmp, "w") as f:
