@@ -44,7 +44,10 @@ def parse():
                     help="skip the per-shape lines for the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grouped-only", action="store_true",
-                    help="time only the grouped (all experts in one launch) workload")
+                    help="time only one grouped (all experts in one launch) workload")
+    ap.add_argument("--grouped-workload", default=synth.GROUPED_CONFIGS[0].name,
+                    choices=[c.name for c in synth.GROUPED_CONFIGS],
+                    help="the grouped workload of --grouped-only (and of its --traffic-summary)")
     ap.add_argument("--quantize-only", action="store_true",
                     help="time only the fp32 -> NVFP4 quantisation shapes")
     ap.add_argument("--decode-only", action="store_true",
@@ -295,10 +298,17 @@ def time_workload(nv, torch, cfg, steps, warmup, cold=False, ops=None):
 
 
 def grouped_roofline(g, seconds_per_call):
+    """As roofline_for, with the grouped GEMM's algorithmic bytes (A, the
+    weights of every expert, the output)."""
     b = synth.grouped_algorithmic_bytes(g.M, g.N, g.K, g.experts)
-    ach = b / seconds_per_call / 1e9
-    return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
-            "frac": ach / HBM_GBPS, "traffic": None, "algorithmic_bytes_per_launch": b}
+    f = synth.flops(g.M, g.N, g.K)
+    if f / b < MFMA_F16_TFLOPS * 1e12 / (HBM_GBPS * 1e9):
+        ach = b / seconds_per_call / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
+                "frac": ach / HBM_GBPS, "traffic": None, "algorithmic_bytes_per_launch": b}
+    ach = f / seconds_per_call / 1e12
+    return {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / MFMA_F16_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": f}
 
 
 def time_grouped(nv, torch, g, steps, warmup, ops=None, cold=False):
@@ -340,8 +350,10 @@ def time_grouped(nv, torch, g, steps, warmup, ops=None, cold=False):
             "operand_copies": copies}
 
 
-def grouped_line(nv, torch, steps, warmup):
-    g = synth.GROUPED_CONFIGS[0]
+def grouped_line(nv, torch, steps, warmup, g=None):
+    """One grouped workload (the decode batch by default), warm and cold;
+    the library picks the kernel from the rows per expert."""
+    g = synth.GROUPED_CONFIGS[0] if g is None else g
     r = time_grouped(nv, torch, g, steps, warmup)
     ms = r["graph_ms"]
     c = time_grouped(nv, torch, g, steps, warmup, ops=r["ops"], cold=True)
@@ -356,7 +368,7 @@ def grouped_line(nv, torch, steps, warmup):
                              "operand_copies": c["operand_copies"],
                              "calls_per_replay": c["calls_per_replay"],
                              "note": "operand copies rotated beyond the last-level cache"},
-                    "path": "grouped",
+                    "path": "grouped (kernel chosen from the rows per expert)",
                     "pages_tflops_other_gpu": None}
 
 
@@ -714,7 +726,7 @@ def main():
     args = parse()
     if args.traffic_summary:
         if args.grouped_only:
-            g = synth.GROUPED_CONFIGS[0]
+            g = synth.grouped_config(args.grouped_workload)
             traffic_summary(g, *args.traffic_summary,
                             alg_bytes=synth.grouped_algorithmic_bytes(g.M, g.N, g.K, g.experts))
         else:
@@ -748,7 +760,8 @@ def main():
         print(json.dumps({"workload": name, **d}), flush=True)
         return
     if args.grouped_only:
-        name, g = grouped_line(nv, torch, args.steps, args.warmup)
+        name, g = grouped_line(nv, torch, args.steps, args.warmup,
+                               synth.grouped_config(args.grouped_workload))
         print(json.dumps({"workload": name, **g}), flush=True)
         return
     if args.floors_only:
@@ -795,12 +808,13 @@ def main():
                         "note": "operand copies rotated beyond the last-level cache"}
     if not args.only_headline:
         per = {}
-        # the grouped workload first, then the single GEMMs by size; the
+        # the grouped workloads first, then the single GEMMs by size; the
         # allocator's cached blocks are released between workloads
         torch.cuda.empty_cache()
-        name, g = grouped_line(nv, torch, args.steps, args.warmup)
-        per[name] = g
-        torch.cuda.empty_cache()
+        for gc in synth.GROUPED_CONFIGS:
+            name, g = grouped_line(nv, torch, args.steps, args.warmup, gc)
+            per[name] = g
+            torch.cuda.empty_cache()
         name, d = decode_sequence_line(nv, torch, args.steps, args.warmup)
         per[name] = d
         name, d = fused_projection_line(nv, torch, args.steps, args.warmup)

@@ -59,7 +59,8 @@ PLAN_TABLE = 1
 EXPORTS = ["nvfp4_status_string", "nvfp4_version", "nvfp4_packed_size", "nvfp4_pack",
            "nvfp4_unpack", "nvfp4_init", "nvfp4_shutdown", "nvfp4_gemm",
            "nvfp4_gemm_with_plan", "nvfp4_plan", "nvfp4_plan_table_load",
-           "nvfp4_plan_table_clear", "nvfp4_build_id", "nvfp4_grouped_gemm", "nvfp4_quantize",
+           "nvfp4_plan_table_clear", "nvfp4_build_id", "nvfp4_grouped_gemm",
+           "nvfp4_grouped_gemm_with_plan", "nvfp4_quantize",
            "nvfp4_sequence_create", "nvfp4_sequence_add_gemm", "nvfp4_sequence_add_grouped_gemm",
            "nvfp4_sequence_add_quantize", "nvfp4_sequence_finalize", "nvfp4_sequence_launch",
            "nvfp4_quantize_bf16", "nvfp4_sequence_add_quantize_bf16", "nvfp4_gemm_quantized",
@@ -137,6 +138,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_grouped_gemm.restype = ctypes.c_int
         L.nvfp4_grouped_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float, _vp, _i64,
                                          _i64, _i64, _vp]
+        L.nvfp4_grouped_gemm_with_plan.restype = ctypes.c_int
+        L.nvfp4_grouped_gemm_with_plan.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, ctypes.c_float,
+                                                   _vp, _i64, _i64, _i64, ctypes.c_int, _vp]
         L.nvfp4_gemm_quantized.restype = ctypes.c_int
         L.nvfp4_gemm_quantized.argtypes = [_vp, ctypes.c_int, _i64, _vp, _vp, ctypes.c_float, _vp,
                                            _i64, _i64, _i64, _vp]
@@ -438,11 +442,12 @@ def groups_to_device(codes: np.ndarray, scales: np.ndarray, device="cuda") -> Pa
 
 
 def grouped_gemm(a: PackedOperand, b: PackedGroups, row_offsets, alpha: float = 1.0, out=None,
-                 stream=None):
-    """Grouped GEMM (nvfp4_grouped_gemm): rows row_offsets[g] ..
-    row_offsets[g+1]-1 of A and C belong to group g, whose weights are
-    b's g-th operand.  ``row_offsets`` is an int32 device tensor of G + 1
-    entries.  Returns C (M x N bfloat16)."""
+                 stream=None, path: int = PATH_AUTO):
+    """Grouped GEMM (nvfp4_grouped_gemm, or nvfp4_grouped_gemm_with_plan for
+    a forced ``path``: PATH_SKINNY, PATH_WSPLIT or PATH_TILE): rows
+    row_offsets[g] .. row_offsets[g+1]-1 of A and C belong to group g, whose
+    weights are b's g-th operand.  ``row_offsets`` is an int32 device tensor
+    of G + 1 entries.  Returns C (M x N bfloat16)."""
     import torch
     if a.K != b.K:
         raise ValueError(f"K dimension mismatch: A has K={a.K}, B has K={b.K}")
@@ -457,11 +462,14 @@ def grouped_gemm(a: PackedOperand, b: PackedGroups, row_offsets, alpha: float = 
         raise ValueError(f"out must be a contiguous bfloat16 tensor of shape ({M}, {N})")
     a.check("a")
     b.check("b")
-    st = lib().nvfp4_grouped_gemm(a.codes.data_ptr(), a.scales.data_ptr(), b.codes.data_ptr(),
-                                  b.scales.data_ptr(), row_offsets.data_ptr(), b.groups,
-                                  float(alpha), out.data_ptr(), M, N, K, _stream_handle(stream))
+    st = lib().nvfp4_grouped_gemm_with_plan(a.codes.data_ptr(), a.scales.data_ptr(),
+                                            b.codes.data_ptr(), b.scales.data_ptr(),
+                                            row_offsets.data_ptr(), b.groups, float(alpha),
+                                            out.data_ptr(), M, N, K, int(path),
+                                            _stream_handle(stream))
     if st:
-        raise Nvfp4Error(st, f"nvfp4_grouped_gemm(G={b.groups}, M={M}, N={N}, K={K})")
+        raise Nvfp4Error(st, f"nvfp4_grouped_gemm_with_plan(G={b.groups}, M={M}, N={N}, K={K}, "
+                             f"path={path})")
     return out
 
 

@@ -215,8 +215,11 @@ int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packe
 
 int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_packed,
                     const void* b_scales, const int32_t* row_offsets, int64_t groups, float alpha,
-                    void* out, int64_t M, int64_t N, int64_t K, Job* job) {
+                    void* out, int64_t M, int64_t N, int64_t K, int path, Job* job) {
     if (!a_packed || !a_scales || !b_packed || !b_scales || !row_offsets || !out)
+        return NVFP4_ERR_INVALID_VALUE;
+    if (path != NVFP4_PATH_AUTO && path != NVFP4_PATH_SKINNY && path != NVFP4_PATH_WSPLIT &&
+        path != NVFP4_PATH_TILE)
         return NVFP4_ERR_INVALID_VALUE;
     if (M < 0 || N < 1 || M > kMaxDim || N > kMaxDim || groups < 1 || !valid_rows_k(1, K))
         return NVFP4_ERR_INVALID_VALUE;
@@ -229,21 +232,41 @@ int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_pa
     job->empty = M == 0;  // no rows: nothing to compute or write
     const int64_t P = num_panels(K);
     const int64_t Mp = round_up(M, kRowPad);
-    // Groups of kGroupedTileRows rows or more on average run on the tile
-    // kernel with 256 x 256 tiles (one workgroup per row block of a group
-    // and column block), smaller ones on the grouped skinny kernel: measured
-    // with 256 experts, N = 256, K = 6144, the tile path takes 306 against
-    // 374 us at about 256 rows per expert and 462 against 700 at 512, while
-    // at 64-128 rows (and with N = 2048) the skinny kernel is as fast or
-    // faster.  The tile kernel addresses each packed operand with 32-bit
-    // offsets.
-    if (M > 0 && M / groups >= kGroupedTileRows && P * Mp * kPanelCodeBytes < ((int64_t)1 << 31) &&
-        P * Np * kPanelCodeBytes < ((int64_t)1 << 31)) {
+    // Three kernels, by the average rows per group (measured with 32-256
+    // experts of equal size, K = 6144): the grouped skinny kernel up to 32
+    // rows, which it covers in one pass over B (256 experts, N = 256: 48
+    // against 71 us for the mid-size kernel at 32 rows, 87 against 74 at 40);
+    // the grouped mid-size kernel from kGroupedWsplitRows (at 128 rows 156
+    // against 190 us for the skinny and 246 for the tile kernel, N = 256;
+    // 955 against 1386 and 1618 at N = 2048); the tile kernel with 256 x 256
+    // tiles from kGroupedTileRows (at 384 rows the mid-size kernel is still
+    // 3-5% faster at N = 256 and 2048, at 448-512 the tile kernel 6-14%).
+    // The tile and mid-size kernels address A and each group's B with 32-bit
+    // offsets; the mid-size kernel keeps a table of the groups in LDS.
+    const bool offsets32 = P * Mp * kPanelCodeBytes < ((int64_t)1 << 31) &&
+                           P * Np * kPanelCodeBytes < ((int64_t)1 << 31);
+    const int64_t avg = M / groups;
+    const int64_t tiles_n64 = (N + 63) / 64;
+    const bool wsplit_ok = offsets32 && groups <= kGroupedWsplitMaxGroups &&
+                           ((M + 63) / 64 + groups) * tiles_n64 <= INT32_MAX;
+    int use = path;
+    if (use == NVFP4_PATH_AUTO)
+        use = (M > 0 && avg >= kGroupedTileRows && offsets32) ? NVFP4_PATH_TILE
+              : (M > 0 && avg >= kGroupedWsplitRows && wsplit_ok) ? NVFP4_PATH_WSPLIT
+                                                                  : NVFP4_PATH_SKINNY;
+    if (use == NVFP4_PATH_WSPLIT) {
+        if (!wsplit_ok) return NVFP4_ERR_UNSUPPORTED;
+        job->kind = JOB_GROUPED_WSPLIT;
+    }
+    if (use == NVFP4_PATH_TILE) {
+        if (!offsets32) return NVFP4_ERR_UNSUPPORTED;
         const int cfg = TILE_256x256;
         const TileShape ts = tile_shape(cfg);
         const int64_t tiles_m = (M + ts.bm - 1) / ts.bm + groups;  // bound: each group adds at most one partial block
         const int64_t tiles_n = (N + ts.bn - 1) / ts.bn;
-        if (tiles_m * tiles_n <= INT32_MAX) {
+        if (tiles_m * tiles_n > INT32_MAX) {
+            if (path == NVFP4_PATH_TILE) return NVFP4_ERR_UNSUPPORTED;
+        } else {
             job->kind = JOB_GROUPED_TILE;
             job->plan.path = NVFP4_PATH_TILE;
             job->plan.cfg = cfg;
@@ -270,7 +293,7 @@ int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_pa
             return NVFP4_OK;
         }
     }
-    job->kind = JOB_GROUPED;
+    if (job->kind != JOB_GROUPED_WSPLIT) job->kind = JOB_GROUPED;
     GroupedArgs& a = job->grouped;
     a.a_codes = static_cast<const uint8_t*>(a_packed);
     a.a_scales = static_cast<const uint8_t*>(a_scales);
@@ -349,6 +372,7 @@ hipError_t launch_job(const Job& job, int device, const WorkspacePtrs& ws, hipSt
     if (job.kind == JOB_GEMV_QUANT) return launch_gemv_quant(job.gemvq, s);
     if (job.kind == JOB_GROUPED) return launch_grouped(job.grouped, s);
     if (job.kind == JOB_GROUPED_TILE) return launch_grouped_tile(job.gemm, s);
+    if (job.kind == JOB_GROUPED_WSPLIT) return launch_grouped_wsplit(job.grouped, s);
     if (job.kind == JOB_QUANTIZE) return launch_quantize(job.quant, s);
     GemmArgs a = job.gemm;
     a.partials = ws.partials;
@@ -381,7 +405,7 @@ const char* nvfp4_status_string(int status) {
     }
 }
 
-int nvfp4_version(void) { return 10400; }
+int nvfp4_version(void) { return 10500; }
 
 int nvfp4_packed_size(int64_t rows, int64_t K, size_t* code_bytes, size_t* scale_bytes) {
     if (!code_bytes || !scale_bytes || !valid_rows_k(rows, K)) return NVFP4_ERR_INVALID_VALUE;
@@ -522,9 +546,18 @@ int nvfp4_gemm_quantized(const void* x, int x_type, int64_t ldx, const void* b_p
 int nvfp4_grouped_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
                        const void* b_scales, const int32_t* row_offsets, int64_t groups,
                        float alpha, void* out, int64_t M, int64_t N, int64_t K, void* stream) {
+    return nvfp4_grouped_gemm_with_plan(a_packed, a_scales, b_packed, b_scales, row_offsets,
+                                        groups, alpha, out, M, N, K, NVFP4_PATH_AUTO, stream);
+}
+
+int nvfp4_grouped_gemm_with_plan(const void* a_packed, const void* a_scales,
+                                 const void* b_packed, const void* b_scales,
+                                 const int32_t* row_offsets, int64_t groups, float alpha,
+                                 void* out, int64_t M, int64_t N, int64_t K, int path,
+                                 void* stream) {
     Job job;
     const int st = prepare_grouped(a_packed, a_scales, b_packed, b_scales, row_offsets, groups,
-                                   alpha, out, M, N, K, &job);
+                                   alpha, out, M, N, K, path, &job);
     return st != NVFP4_OK ? st : run_job(job, stream);
 }
 

@@ -16,7 +16,8 @@ enum JobKind {
     JOB_GROUPED = 1,
     JOB_QUANTIZE = 2,
     JOB_GROUPED_TILE = 3,
-    JOB_GEMV_QUANT = 4
+    JOB_GEMV_QUANT = 4,
+    JOB_GROUPED_WSPLIT = 5
 };
 
 struct Job {
@@ -26,7 +27,7 @@ struct Job {
     size_t floats = 0;           // split-K partial floats the job needs (tile, wsplit)
     size_t flagged = 0;          // flagged 64-bit partial words the job needs (skinny)
     size_t counters = 0;         // split-K arrival counters the job needs
-    GroupedArgs grouped{};       // JOB_GROUPED
+    GroupedArgs grouped{};       // JOB_GROUPED, JOB_GROUPED_WSPLIT
     QuantArgs quant{};           // JOB_QUANTIZE
     GemvQuantArgs gemvq{};       // JOB_GEMV_QUANT
     bool empty = false;          // nothing to launch (a grouped GEMM with no rows)
@@ -39,7 +40,7 @@ int prepare_gemm(const void* a_packed, const void* a_scales, const void* b_packe
                  int path, int tile, int split_k, Job* job);
 int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_packed,
                     const void* b_scales, const int32_t* row_offsets, int64_t groups, float alpha,
-                    void* out, int64_t M, int64_t N, int64_t K, Job* job);
+                    void* out, int64_t M, int64_t N, int64_t K, int path, Job* job);
 int prepare_quantize(const void* x, bool bf16, int64_t rows, int64_t K, int64_t ld,
                      void* packed_codes, void* packed_scales, Job* job);
 int prepare_gemm_quantized(const void* x, int x_type, int64_t ldx, const void* b_packed,

@@ -99,7 +99,11 @@ constexpr int kGroupedWaves = 4;   // waves per workgroup (split K)
 constexpr int kGroupedChunks = 2;  // 16-row chunks of A per pass over B
 constexpr int kGroupedUnits = 1;   // 128-element K units of loads in flight per wave
 constexpr int kGroupedBlocks = 4;  // 16-row blocks of B per workgroup (share A's decode)
-constexpr int kGroupedTileRows = 256;  // groups this large on average use the tile kernel
+constexpr int kGroupedTileRows = 416;  // groups this large on average use the tile kernel
+constexpr int kGroupedWsplitRows = 33;   // groups this large (and below kGroupedTileRows) on
+                                         // average use the grouped mid-size kernel
+constexpr int kGroupedWsplitWaves = 8;   // waves per workgroup of that kernel (split K)
+constexpr int kGroupedWsplitMaxGroups = 4096;  // its LDS table of row blocks per group
 
 struct GroupedArgs {
     const uint8_t* a_codes;   // [P][Mp][32], all M rows
@@ -115,6 +119,7 @@ struct GroupedArgs {
     int G;                    // number of groups
 };
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t stream);
+hipError_t launch_grouped_wsplit(const GroupedArgs& a, hipStream_t stream);
 
 // Grouped GEMM with large groups on the tile kernel (256 x 256 tiles): one
 // workgroup per (row block of a group, column block) of an upper bound of

@@ -102,7 +102,7 @@ int nvfp4_sequence_add_grouped_gemm(nvfp4_sequence_t seq, const void* a_packed,
     if (seq->finalized) return NVFP4_ERR_STATE;
     Job job;
     const int st = prepare_grouped(a_packed, a_scales, b_packed, b_scales, row_offsets, groups,
-                                   alpha, out, M, N, K, &job);
+                                   alpha, out, M, N, K, NVFP4_PATH_AUTO, &job);
     return add_job(seq, st, job);
 }
 

@@ -258,16 +258,35 @@ int nvfp4_gemm_quantized(const void* x, int x_type, int64_t ldx, const void* b_p
  *                        group are overwritten, rows outside every group are
  *                        left untouched
  *   M                  : total rows (0 is allowed: nothing is launched)
- * Groups of about 16-250 rows (M / groups < 256) run on a skinny kernel
- * built for the memory-bound decode regime; larger groups (prefill) run on
- * the MFMA tile kernel with 256 x 256 tiles, one workgroup per row block of
- * a group and column block.  Either way the result is the same GEMM, up to
- * the order of the FP32 additions.
+ * The kernel follows the average group size M / groups: up to 32 rows (the
+ * decode regime, about 16 rows per expert) a skinny kernel built for the
+ * memory-bound case; from 33 to 415 rows a mid-size kernel with 64 x 64
+ * output tiles of every group taken in turn by a persistent grid (at most
+ * 4096 groups, else the skinny kernel); from 416 rows the MFMA tile kernel
+ * with 256 x 256 tiles, one workgroup per row block of a group and column
+ * block.  Either
+ * way the result is the same GEMM, up to the order of the FP32 additions.
  * Same alignment (row_offsets: 4 bytes), status and stream rules as
  * nvfp4_gemm; no workspace, no allocation. */
 int nvfp4_grouped_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
                        const void* b_scales, const int32_t* row_offsets, int64_t groups,
                        float alpha, void* out, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* nvfp4_grouped_gemm with a forced kernel, for tuning and tests:
+ *   path : NVFP4_PATH_AUTO (the choice above), NVFP4_PATH_SKINNY (the decode
+ *          kernel), NVFP4_PATH_WSPLIT (the mid-size kernel) or
+ *          NVFP4_PATH_TILE (256 x 256 tiles); anything else is
+ *          NVFP4_ERR_INVALID_VALUE
+ * NVFP4_ERR_UNSUPPORTED if the forced kernel cannot run the call: the
+ * mid-size kernel needs at most 4096 groups, and it and the tile kernel need
+ * the packed codes of A and of one group's B each below 2 GiB.  Otherwise
+ * the same contract as nvfp4_grouped_gemm; every path gives the same result
+ * up to the order of the FP32 additions. */
+int nvfp4_grouped_gemm_with_plan(const void* a_packed, const void* a_scales,
+                                 const void* b_packed, const void* b_scales,
+                                 const int32_t* row_offsets, int64_t groups, float alpha,
+                                 void* out, int64_t M, int64_t N, int64_t K, int path,
+                                 void* stream);
 
 /* Where a plan came from. */
 enum {

@@ -232,6 +232,9 @@ GROUPED_CONFIGS = [
     GroupedConfig("moe_up_grouped_e256", 512, 256, 8, 256, 6144, 1.0, 6,
                   "MoE up-projection eight-way share, all 256 experts in one launch, "
                   "512 tokens routed to 8 experts each (about 16 rows per expert)"),
+    GroupedConfig("moe_up_grouped_e256_t4096", 4096, 256, 8, 256, 6144, 1.0, 7,
+                  "the same layer for a prefill-sized batch: 4096 tokens routed to 8 of "
+                  "256 experts each (about 128 rows per expert)"),
 ]
 
 

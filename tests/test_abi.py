@@ -144,6 +144,31 @@ def test_grouped_gemm_rejects_bad_arguments_before_launch():
     assert _graw(off=0x6002) == nv.ERR_MISALIGNED
 
 
+def _gwp(path, G=4, M=4, N=4, K=64, b=0x3000):
+    return nv.lib().nvfp4_grouped_gemm_with_plan(0x1000, 0x2000, b, 0x4000, 0x6000, G, 1.0,
+                                                 0x5000, M, N, K, path, None)
+
+
+def test_grouped_gemm_with_plan_rejects_bad_paths_and_sizes_before_launch():
+    # only the three grouped kernels (or the library's choice) can be forced
+    for path in (-1, nv.PATH_GEMV, 5, 99):
+        assert _gwp(path) == nv.ERR_INVALID_VALUE, path
+    # the checks of nvfp4_grouped_gemm come first, for every path
+    for path in (nv.PATH_AUTO, nv.PATH_SKINNY, nv.PATH_WSPLIT, nv.PATH_TILE):
+        assert _gwp(path, G=0) == nv.ERR_INVALID_VALUE, path
+        assert _gwp(path, K=24) == nv.ERR_INVALID_VALUE, path
+        assert _gwp(path, b=0x3008) == nv.ERR_MISALIGNED, path
+    # the mid-size kernel's LDS table holds at most 4096 groups
+    assert _gwp(nv.PATH_WSPLIT, G=4097, M=4097 * 64) == nv.ERR_UNSUPPORTED
+    # the mid-size and tile kernels address A (and each group's B) with
+    # 32-bit offsets: 2 GiB of packed codes or more cannot be forced there,
+    # while the skinny kernel and the library's choice (which falls back to
+    # it) take them
+    big_m = (1 << 31) // (6144 // 2) + 16   # rows of K = 6144 past 2 GiB of codes
+    for path in (nv.PATH_WSPLIT, nv.PATH_TILE):
+        assert _gwp(path, G=4, M=big_m, N=256, K=6144) == nv.ERR_UNSUPPORTED, path
+
+
 def test_pack_groups_concatenates_per_group_packing():
     g = np.random.Generator(np.random.PCG64(3))
     codes = g.integers(0, 256, size=(3, 20, 80), dtype=np.uint8)

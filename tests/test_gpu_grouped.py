@@ -7,6 +7,7 @@ bit-exact fraction reported.
 """
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -51,14 +52,18 @@ def random_grouped(seed, sizes, N, K, alpha=1.0):
     return synth.GroupedOperands(ac, as_, bc, bs, offsets, alpha, M, N, K, G)
 
 
-def run_grouped(ops, offsets=None, out=None, label=""):
+PATHS = {"auto": nv.PATH_AUTO, "skinny": nv.PATH_SKINNY, "mid": nv.PATH_WSPLIT,
+         "tile": nv.PATH_TILE}
+
+
+def run_grouped(ops, offsets=None, out=None, label="", path="auto"):
     offs = ops.offsets if offsets is None else np.asarray(offsets, np.int32)
-    say(f"{label} G={ops.G} M={ops.M} N={ops.N} K={ops.K} alpha={ops.alpha} "
+    say(f"{label} path={path} G={ops.G} M={ops.M} N={ops.N} K={ops.K} alpha={ops.alpha} "
         f"offsets={offs.tolist() if offs.size <= 12 else '...'}")
     a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
     b = nv.groups_to_device(ops.b_codes, ops.b_scales, DEV)
     off = torch.from_numpy(offs).to(DEV)
-    c = nv.grouped_gemm(a, b, off, ops.alpha, out=out)
+    c = nv.grouped_gemm(a, b, off, ops.alpha, out=out, path=PATHS[path])
     torch.cuda.synchronize()
     return c.view(torch.int16).cpu().numpy().astype(np.uint16)
 
@@ -95,6 +100,34 @@ def test_grouped_moe_workload(o):
     check(o, ops, g, "moe grouped workload")
 
 
+def test_grouped_prefill_workload(o):
+    """4096 tokens routed to 8 of 256 experts (about 128 rows per expert,
+    the mid-size kernel): every element of 16 whole groups (the first, the
+    last, the smallest and largest non-empty ones and 12 more at random),
+    and every output finite."""
+    cfg = synth.grouped_config("moe_up_grouped_e256_t4096")
+    ops = synth.make_grouped_inputs(cfg)
+    g = run_grouped(ops, label="moe grouped prefill workload")
+    counts = np.diff(ops.offsets)
+    nonempty = np.flatnonzero(counts)
+    rng = np.random.Generator(np.random.PCG64(4096))
+    pick = {0, ops.G - 1, int(nonempty[np.argmin(counts[nonempty])]), int(np.argmax(counts))}
+    pick |= {int(x) for x in rng.choice(ops.G, size=12, replace=False)}
+    say(f"prefill workload: rows per expert {counts.min()}-{counts.max()}, checking groups "
+        f"{sorted(pick)}")
+    for e in sorted(pick):
+        r0, r1 = int(ops.offsets[e]), int(ops.offsets[e + 1])
+        if r0 == r1:
+            continue
+        bits, exact, mag = o.gemm(np.ascontiguousarray(ops.a_codes[r0:r1]),
+                                  np.ascontiguousarray(ops.a_scales[r0:r1]), ops.b_codes[e],
+                                  ops.b_scales[e], ops.alpha)
+        r = compare(g[r0:r1], bits, exact, mag, ops.alpha)
+        assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, (e, r)
+    vals = orc.bf16_bits_to_float(g)
+    assert np.all(np.isfinite(vals))
+
+
 def test_grouped_offsets_are_clamped_and_rows_outside_groups_untouched(o):
     """A table with entries outside [0, M] is clamped (group 0 empty, group 2
     ends at M); rows after the last group's end are not written."""
@@ -125,38 +158,90 @@ def test_grouped_no_rows():
     assert st == nv.OK
 
 
-# Groups of 256 rows or more on average run on the tile kernel (256 x 256
-# tiles: row blocks of each group, with a partial block at every group's
-# end); the first case stays on the grouped skinny kernel (about 100 rows
-# per group, several passes over B per workgroup).
+# Large groups on the tile kernel (256 x 256 tiles: row blocks of each
+# group, with a partial block at every group's end), forced, and each case
+# also on the library's choice (the mid-size kernel up to 415 rows on
+# average, the tile kernel from 416: the last case) and on the skinny kernel
+# (several passes over B per workgroup).
 @pytest.mark.parametrize("sizes,N,K", [
-    ([0, 70, 130, 1, 257, 64, 200], 200, 640),      # skinny path, empty and 1-row groups
-    ([300, 512, 0, 700, 259], 264, 1040),            # tile path, K not a multiple of 128
-    ([256] * 4 + [512], 256, 2048),                  # tile path, whole blocks only
-    ([1, 1000, 3, 300], 136, 384),                   # tile path, tiny and large groups
+    ([0, 70, 130, 1, 257, 64, 200], 200, 640),      # empty and 1-row groups
+    ([300, 512, 0, 700, 259], 264, 1040),            # K not a multiple of 128
+    ([256] * 4 + [512], 256, 2048),                  # whole 256-row blocks only
+    ([1, 1000, 3, 300], 136, 384),                   # tiny and large groups
+    ([420, 0, 900, 500], 72, 256),                   # 455 rows on average: tile by default
 ])
 def test_grouped_tile_path(o, sizes, N, K):
     ops = random_grouped(sum(sizes) * 3 + N + K, sizes, N, K, alpha=-0.625)
-    g = run_grouped(ops, label="grouped (tile path)")
-    check(o, ops, g, f"grouped tile path sizes={sizes} N={N} K={K}")
+    for path in ("tile", "auto", "skinny"):
+        g = run_grouped(ops, label=f"grouped ({path} path)", path=path)
+        check(o, ops, g, f"grouped {path} path sizes={sizes} N={N} K={K}")
 
 
-def test_grouped_tile_path_clamps_and_leaves_other_rows(o):
-    """Tile path with a malformed table (entries outside [0, M] are clamped)
-    and a table that ends before M (the rows after it keep their contents)."""
+# Groups of 33-415 rows on average run on the mid-size kernel: 64 x 64 tiles
+# of every group (row blocks from each group's first row, the last one cut
+# at the group's end), taken in turn by a persistent grid of at most one
+# workgroup per CU.
+@pytest.mark.parametrize("sizes,N,K", [
+    ([64] * 8, 256, 6144),                            # whole row blocks, full K
+    ([65, 63, 128, 129, 0, 191], 136, 1040),          # partial blocks, K not a multiple of 128
+    ([96] * 300, 128, 128),                           # 1200 tiles: about 5 per workgroup
+    ([0, 1, 2, 500, 3, 0, 64], 40, 256),              # one large group among tiny ones
+])
+def test_grouped_mid_path(o, sizes, N, K):
+    ops = random_grouped(sum(sizes) * 5 + N + K, sizes, N, K, alpha=1.375)
+    g = run_grouped(ops, label="grouped (mid-size path)", path="mid")
+    check(o, ops, g, f"grouped mid-size path sizes={sizes} N={N} K={K}")
+
+
+def test_grouped_mid_path_table_limit(o):
+    """4096 groups (the mid-size kernel's LDS table holds that many) of 0-5
+    rows, forced onto the mid-size kernel: every thread of the prefix sum
+    counts eight groups."""
+    g = np.random.Generator(np.random.PCG64(4096))
+    sizes = [int(s) for s in g.integers(0, 6, size=4096)]
+    ops = random_grouped(4097, sizes, 40, 64, alpha=0.5)
+    out = run_grouped(ops, label="grouped (mid-size path, 4096 groups)", path="mid")
+    check(o, ops, out, "mid-size path, 4096 groups")
+
+
+def test_grouped_paths_agree(o):
+    """The same call on each of the three kernels: every one matches the
+    oracle, and all give the same bits.  Scales are 0.5, 1 or 2 (E4M3 bytes
+    0x30, 0x38, 0x40), so every product is a multiple of 1/16 of magnitude at
+    most 144 and every sum over K = 768 is exact in FP32 (below 2^24 / 16),
+    whatever the order of the additions."""
+    sizes = [40, 0, 200, 64, 1, 300, 128]
+    ops = random_grouped(91, sizes, 160, 768, alpha=-2.0)
+    g = np.random.Generator(np.random.PCG64(92))
+    pick = np.array([0x30, 0x38, 0x40], np.uint8)
+    ops = dataclasses.replace(ops, a_scales=pick[g.integers(0, 3, size=ops.a_scales.shape)],
+                              b_scales=pick[g.integers(0, 3, size=ops.b_scales.shape)])
+    outs = {}
+    for path in ("skinny", "mid", "tile"):
+        outs[path] = run_grouped(ops, label=f"grouped ({path} path)", path=path)
+        check(o, ops, outs[path], f"grouped {path} path")
+    assert np.array_equal(outs["skinny"], outs["mid"])
+    assert np.array_equal(outs["skinny"], outs["tile"])
+
+
+@pytest.mark.parametrize("path", ["tile", "mid"])
+def test_grouped_tile_path_clamps_and_leaves_other_rows(o, path):
+    """Tile and mid-size paths with a malformed table (entries outside
+    [0, M] are clamped) and a table that ends before M (the rows after it
+    keep their contents)."""
     sizes = [400, 260, 300]
     ops = random_grouped(77, sizes, 136, 512, alpha=1.5)
     M, N = ops.M, ops.N
     bad = np.array([0, -9, 400, 10 ** 6], np.int32)           # acts as [0, 0, 400, M]
     eff = synth.GroupedOperands(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales,
                                 np.array([0, 0, 400, M], np.int32), ops.alpha, M, N, ops.K, 3)
-    g = run_grouped(ops, offsets=bad, label="tile path, clamped offsets")
-    check(o, eff, g, "tile path, clamped offsets")
+    g = run_grouped(ops, offsets=bad, label=f"{path} path, clamped offsets", path=path)
+    check(o, eff, g, f"{path} path, clamped offsets")
     short = np.array([0, 400, 660, M - 70], np.int32)
     out = torch.full((M, N), 3.0, dtype=torch.bfloat16, device=DEV)
-    g2 = run_grouped(ops, offsets=short, out=out, label="tile path, short table")
+    g2 = run_grouped(ops, offsets=short, out=out, label=f"{path} path, short table", path=path)
     eff2 = synth.GroupedOperands(ops.a_codes[:M - 70], ops.a_scales[:M - 70], ops.b_codes,
                                  ops.b_scales, short, ops.alpha, M - 70, N, ops.K, 3)
-    check(o, eff2, g2[:M - 70], "tile path, short table")
+    check(o, eff2, g2[:M - 70], f"{path} path, short table")
     three = int(torch.tensor([3.0], dtype=torch.bfloat16).view(torch.int16).item()) & 0xFFFF
     assert np.all(g2[M - 70:] == three)

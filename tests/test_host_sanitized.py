@@ -32,6 +32,7 @@ hipError_t launch_wsplit(int, const GemmArgs&, hipStream_t) { return hipErrorInv
 hipError_t launch_skinny(const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_gemv(const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_grouped(const GroupedArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_grouped_wsplit(const GroupedArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_grouped_tile(const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_quantize(const QuantArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_gemv_quant(const GemvQuantArgs&, hipStream_t) { return hipErrorInvalidValue; }
