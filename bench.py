@@ -345,14 +345,18 @@ def time_grouped(nv, torch, g, steps, warmup, ops=None, cold=False):
             nv.grouped_gemm(x, y, off, g.alpha, out=o, stream=cap)
     ms, warm_replays, _ = timed_replay(torch, gr, stream, steps)
     copies = len(sets)
+    # the timed replay's own output (warm), for the parity check after the timing
+    out_bits = None if cold else sets[0][2].view(torch.int16).cpu().numpy().astype(np.uint16)
     del gr, sets
     return {"graph_ms": ms, "ops": ops, "warm_replays": warm_replays, "calls_per_replay": steps,
-            "operand_copies": copies}
+            "operand_copies": copies, "out_bits": out_bits}
 
 
 def grouped_line(nv, torch, steps, warmup, g=None):
     """One grouped workload (the decode batch by default), warm and cold;
-    the library picks the kernel from the rows per expert."""
+    the library picks the kernel from the rows per expert.  Returns the
+    workload's name, its line, and (config, operands, the warm run's output
+    bits) for the parity check."""
     g = synth.GROUPED_CONFIGS[0] if g is None else g
     r = time_grouped(nv, torch, g, steps, warmup)
     ms = r["graph_ms"]
@@ -369,7 +373,7 @@ def grouped_line(nv, torch, steps, warmup, g=None):
                              "calls_per_replay": c["calls_per_replay"],
                              "note": "operand copies rotated beyond the last-level cache"},
                     "path": "grouped (kernel chosen from the rows per expert)",
-                    "pages_tflops_other_gpu": None}
+                    "pages_tflops_other_gpu": None}, (g, r["ops"], r["out_bits"])
 
 
 QUANT_SHAPES = [(16, 6144), (16384, 8192)]   # decode activations of one expert; saturation-shape A
@@ -702,6 +706,44 @@ def oracle_leg(o, cfg, ops, gpu_bits):
                        "by the number of multiply-adds"})
 
 
+def grouped_oracle_leg(o, g, ops, gpu_bits):
+    """Parity of a timed grouped run's output against the oracle (each
+    expert's rows an ordinary GEMM with that expert's weights), and the
+    oracle's time: every expert up to 2 * 10^10 multiply-adds; above that 16
+    whole experts (the first, the last, the smallest and the largest
+    non-empty ones, 12 more drawn with a fixed seed), the oracle's time for
+    the whole layer extrapolated by multiply-adds."""
+    from oracle import parity
+    counts = np.diff(ops.offsets)
+    nonempty = [int(e) for e in np.flatnonzero(counts)]
+    if g.M * g.N * g.K <= 2 * 10 ** 10:
+        experts, what = nonempty, "every expert"
+    else:
+        rng = np.random.Generator(np.random.PCG64(g.M))
+        pick = {nonempty[0], nonempty[-1], min(nonempty, key=lambda e: counts[e]),
+                max(nonempty, key=lambda e: counts[e])}
+        rest = [e for e in nonempty if e not in pick]
+        pick |= {int(e) for e in rng.choice(rest, size=min(12, len(rest)), replace=False)}
+        experts = sorted(pick)
+        what = f"{len(experts)} whole experts {experts}"
+    reports, macs = [], 0
+    t0 = time.perf_counter()
+    for e in experts:
+        r0, r1 = int(ops.offsets[e]), int(ops.offsets[e + 1])
+        bits, exact, mag = o.gemm(np.ascontiguousarray(ops.a_codes[r0:r1]),
+                                  np.ascontiguousarray(ops.a_scales[r0:r1]), ops.b_codes[e],
+                                  ops.b_scales[e], g.alpha)
+        reports.append(parity.compare(gpu_bits[r0:r1], bits, exact, mag, g.alpha))
+        macs += (r1 - r0) * g.N * g.K
+    el = time.perf_counter() - t0
+    r = parity.merge(reports)
+    return ({k: r[k] for k in ("n", "over", "max_err_over_tol", "bit_exact_frac")} |
+            {"elements": what},
+            {"oracle_s": el, "tflops": 2 * macs / el / 1e12, "threads": o.threads,
+             "full_layer_s_extrapolated": el * (g.M * g.N * g.K) / macs,
+             "sample": f"{r['n']} output elements ({what})"})
+
+
 def cpu_baseline(cfg, ops, budget_s):
     from oracle import oracle as orc
     o = orc.load()
@@ -760,8 +802,8 @@ def main():
         print(json.dumps({"workload": name, **d}), flush=True)
         return
     if args.grouped_only:
-        name, g = grouped_line(nv, torch, args.steps, args.warmup,
-                               synth.grouped_config(args.grouped_workload))
+        name, g, _ = grouped_line(nv, torch, args.steps, args.warmup,
+                                  synth.grouped_config(args.grouped_workload))
         print(json.dumps({"workload": name, **g}), flush=True)
         return
     if args.floors_only:
@@ -775,6 +817,7 @@ def main():
     r = time_workload(nv, torch, cfg, args.steps, args.warmup)
     ms, plan, ops = r["graph_ms"], r["plan"], r["ops"]
     outputs = {cfg.name: (cfg, ops, r["out_bits"])}   # checked against the oracle at the end
+    grouped_outputs = {}
     tflops = synth.flops(cfg.M, cfg.N, cfg.K) / (ms * 1e-3) / 1e12
     line = {
         "metric": "NVFP4 GEMM TFLOPS (2MNK/s) per shape + % of HBM/MFMA roofline, 1 MI355X",
@@ -812,7 +855,7 @@ def main():
         # allocator's cached blocks are released between workloads
         torch.cuda.empty_cache()
         for gc in synth.GROUPED_CONFIGS:
-            name, g = grouped_line(nv, torch, args.steps, args.warmup, gc)
+            name, g, grouped_outputs[name] = grouped_line(nv, torch, args.steps, args.warmup, gc)
             per[name] = g
             torch.cuda.empty_cache()
         name, d = decode_sequence_line(nv, torch, args.steps, args.warmup)
@@ -868,6 +911,10 @@ def main():
                 line["parity"] = par
             else:
                 line["per_shape"][name]["parity"] = par
+        for name, (g, g_ops, bits) in grouped_outputs.items():
+            par, stats = grouped_oracle_leg(o, g, g_ops, bits)
+            cb["per_config"][name] = stats
+            line["per_shape"][name]["parity"] = par
         line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 

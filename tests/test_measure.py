@@ -23,3 +23,50 @@ def test_config_bytes():
     for i, b in want.items():
         c = synth.config(i)
         assert synth.algorithmic_bytes(c.M, c.N, c.K) == b
+
+
+def _grouped(seed, tokens, experts, N, K):
+    ops = synth.grouped_operands(seed, tokens, experts, 4, N, K)
+    cfg = synth.GroupedConfig("t", tokens, experts, 4, N, K, 1.0, seed, "test")
+    return cfg, ops
+
+
+def test_grouped_oracle_leg_checks_every_expert_or_a_sample():
+    """The benchmark's grouped parity leg: on the oracle's own bits every
+    checked element is exact; a one-element error in a checked expert is
+    counted; above the size limit only 16 whole sampled experts are checked
+    (the first, the last, the smallest, the largest and 12 drawn), and their
+    rows are what is reported."""
+    import ast
+    import types
+
+    import numpy as np
+
+    import bench
+    from oracle import oracle as orc
+    o = orc.load()
+    cfg, ops = _grouped(3, 40, 8, 24, 128)
+    ref, _, _ = o.grouped_gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.offsets,
+                               cfg.alpha)
+    par, stats = bench.grouped_oracle_leg(o, cfg, ops, ref)
+    assert par["over"] == 0 and par["bit_exact_frac"] == 1.0 and par["n"] == cfg.M * cfg.N
+    assert par["elements"] == "every expert"
+    bad = ref.copy()
+    bad[int(ops.offsets[-1]) - 1, 5] ^= 0x4000           # flip an exponent bit in the last row
+    par, _ = bench.grouped_oracle_leg(o, cfg, ops, bad)
+    assert par["over"] == 1, par
+    # past 2 * 10^10 multiply-adds (a stand-in config with a huge K): sampled
+    cfg2, ops2 = _grouped(4, 160, 32, 16, 64)
+    ref2, _, _ = o.grouped_gemm(ops2.a_codes, ops2.a_scales, ops2.b_codes, ops2.b_scales,
+                                ops2.offsets, 1.0)
+    big = types.SimpleNamespace(M=cfg2.M, N=cfg2.N, K=10 ** 10, alpha=1.0)
+    par, stats = bench.grouped_oracle_leg(o, big, ops2, ref2)
+    counts = np.diff(ops2.offsets)
+    assert par["elements"].startswith("16 whole experts "), par["elements"]
+    picked = ast.literal_eval(par["elements"][len("16 whole experts "):])
+    nonempty = np.flatnonzero(counts)
+    assert len(set(picked)) == 16 and all(counts[e] > 0 for e in picked)
+    for e in (nonempty[0], nonempty[-1], int(np.argmax(counts))):
+        assert int(e) in picked
+    assert par["n"] == sum(int(counts[e]) for e in picked) * cfg2.N
+    assert par["over"] == 0 and par["bit_exact_frac"] == 1.0
