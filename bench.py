@@ -709,14 +709,15 @@ def oracle_leg(o, cfg, ops, gpu_bits):
 def grouped_oracle_leg(o, g, ops, gpu_bits):
     """Parity of a timed grouped run's output against the oracle (each
     expert's rows an ordinary GEMM with that expert's weights), and the
-    oracle's time: every expert up to 2 * 10^10 multiply-adds; above that 16
+    oracle's time: every expert up to 10^11 multiply-adds (a few seconds on
+    16 host threads); above that 16
     whole experts (the first, the last, the smallest and the largest
     non-empty ones, 12 more drawn with a fixed seed), the oracle's time for
     the whole layer extrapolated by multiply-adds."""
     from oracle import parity
     counts = np.diff(ops.offsets)
     nonempty = [int(e) for e in np.flatnonzero(counts)]
-    if g.M * g.N * g.K <= 2 * 10 ** 10:
+    if g.M * g.N * g.K <= 10 ** 11:
         experts, what = nonempty, "every expert"
     else:
         rng = np.random.Generator(np.random.PCG64(g.M))

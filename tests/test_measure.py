@@ -55,7 +55,7 @@ def test_grouped_oracle_leg_checks_every_expert_or_a_sample():
     bad[int(ops.offsets[-1]) - 1, 5] ^= 0x4000           # flip an exponent bit in the last row
     par, _ = bench.grouped_oracle_leg(o, cfg, ops, bad)
     assert par["over"] == 1, par
-    # past 2 * 10^10 multiply-adds (a stand-in config with a huge K): sampled
+    # past 10^11 multiply-adds (a stand-in config with a huge K): sampled
     cfg2, ops2 = _grouped(4, 160, 32, 16, 64)
     ref2, _, _ = o.grouped_gemm(ops2.a_codes, ops2.a_scales, ops2.b_codes, ops2.b_scales,
                                 ops2.offsets, 1.0)
