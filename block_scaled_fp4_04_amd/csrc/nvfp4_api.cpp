@@ -234,13 +234,13 @@ int prepare_grouped(const void* a_packed, const void* a_scales, const void* b_pa
     const int64_t Mp = round_up(M, kRowPad);
     // Three kernels, by the average rows per group (measured with 32-256
     // experts of equal size, K = 6144): the grouped skinny kernel up to 32
-    // rows, which it covers in one pass over B (256 experts, N = 256: 48
-    // against 71 us for the mid-size kernel at 32 rows, 87 against 74 at 40);
-    // the grouped mid-size kernel from kGroupedWsplitRows (at 128 rows 156
-    // against 190 us for the skinny and 246 for the tile kernel, N = 256;
-    // 955 against 1386 and 1618 at N = 2048); the tile kernel with 256 x 256
-    // tiles from kGroupedTileRows (at 384 rows the mid-size kernel is still
-    // 3-5% faster at N = 256 and 2048, at 448-512 the tile kernel 6-14%).
+    // rows, which it covers in one pass over B (256 experts, N = 256: 49
+    // against 59 us for the mid-size kernel at 32 rows, 88 against 63 at
+    // 40); the grouped mid-size kernel from kGroupedWsplitRows (at 128 rows
+    // 121 against 190 us for the skinny and 246 for the tile kernel, N =
+    // 256); the tile kernel with 256 x 256 tiles from kGroupedTileRows (at
+    // 448 rows the mid-size kernel is still 6-7% faster at N = 256, 2048
+    // and 6144, at 480-512 the tile kernel 0-4%).
     // The tile and mid-size kernels address A and each group's B with 32-bit
     // offsets; the mid-size kernel keeps a table of the groups in LDS.
     const bool offsets32 = P * Mp * kPanelCodeBytes < ((int64_t)1 << 31) &&

@@ -229,7 +229,15 @@ __global__ void __launch_bounds__(WAVES * 64) grouped_wsplit_kernel(GroupedArgs 
         t_step = gridDim.x >> 3;
         t_end = (int)((int64_t)total * (x + 1) / 8);
     }
-    for (int t = t_begin; t < t_end; t += t_step) {
+    // A tile's rows, group, and the lane offsets and weight descriptors of
+    // its loads.
+    struct Src {
+        int m0, n0, r1;
+        uint32_t a_code[MI], a_sc[MI], b_code[NI], b_sc[NI];
+        __amdgpu_buffer_rsrc_t rbc, rbs;
+    };
+    auto src_of = [&](int t) {
+        Src s;
         const int vm = t / tiles_n, tn = t - vm * tiles_n;
         int lo = 0, hi = a.G;  // the group of row block vm: cum[g] <= vm < cum[g + 1]
         while (hi - lo > 1) {
@@ -238,104 +246,127 @@ __global__ void __launch_bounds__(WAVES * 64) grouped_wsplit_kernel(GroupedArgs 
             else hi = mid;
         }
         const int g = lo;
-        int r0, r1;
-        rows_of(g, r0, r1);
-        const int m0 = r0 + (vm - cum[g]) * BM, n0 = tn * BN;
-
-        // Lane offsets inside a panel, rows clamped to the padded operands
-        // (rows past the group's end belong to the next group or to the
-        // padding: they are computed but not stored).
-        uint32_t a_code[MI], a_sc[MI], b_code[NI], b_sc[NI];
+        int r0;
+        rows_of(g, r0, s.r1);
+        s.m0 = r0 + (vm - cum[g]) * BM;
+        s.n0 = tn * BN;
+        // rows clamped to the padded operands (rows past the group's end
+        // belong to the next group or to the padding: computed, not stored)
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const uint32_t r = (uint32_t)min(m0 + i * 32 + q, a.Mp - 1);
-            a_code[i] = r * 32u + (uint32_t)h * 16u;
-            a_sc[i] = r * 4u + (uint32_t)h * 2u;
+            const uint32_t r = (uint32_t)min(s.m0 + i * 32 + q, a.Mp - 1);
+            s.a_code[i] = r * 32u + (uint32_t)h * 16u;
+            s.a_sc[i] = r * 4u + (uint32_t)h * 2u;
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const uint32_t r = (uint32_t)min(n0 + j * 32 + q, a.Np - 1);
-            b_code[j] = r * 32u + (uint32_t)h * 16u;
-            b_sc[j] = r * 4u + (uint32_t)h * 2u;
+            const uint32_t r = (uint32_t)min(s.n0 + j * 32 + q, a.Np - 1);
+            s.b_code[j] = r * 32u + (uint32_t)h * 16u;
+            s.b_sc[j] = r * 4u + (uint32_t)h * 2u;
         }
-        const __amdgpu_buffer_rsrc_t rbc =
-            make_rsrc(a.b_codes + (int64_t)g * P * a.Np * 32, (uint32_t)P * a.Np * 32u);
-        const __amdgpu_buffer_rsrc_t rbs =
-            make_rsrc(a.b_scales + (int64_t)g * P * a.Np * 4, (uint32_t)P * a.Np * 4u);
-
-        // k-th panel of this wave; past its last panel it re-reads that one
-        // and compute() gives it zero scales (unconditional loads: exact
-        // wait counts, as in the single-GEMM kernel)
-        auto load = [&](int k, Regs& r) {
-            const uint32_t pnl = (uint32_t)(wave + min(k, count - 1) * WAVES);
-            const uint32_t sa_off = pnl * (uint32_t)a.Mp, sb_off = pnl * (uint32_t)a.Np;
+        s.rbc = make_rsrc(a.b_codes + (int64_t)g * P * a.Np * 32, (uint32_t)P * a.Np * 32u);
+        s.rbs = make_rsrc(a.b_scales + (int64_t)g * P * a.Np * 4, (uint32_t)P * a.Np * 4u);
+        return s;
+    };
+    // k-th panel of this wave in tile s; past its last panel it re-reads
+    // that one and compute() gives it zero scales (unconditional loads:
+    // exact wait counts, as in the single-GEMM kernel)
+    auto load = [&](const Src& s, int k, Regs& r) {
+        const uint32_t pnl = (uint32_t)(wave + min(k, count - 1) * WAVES);
+        const uint32_t sa_off = pnl * (uint32_t)a.Mp, sb_off = pnl * (uint32_t)a.Np;
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                r.ca[i] = load16(rac, a_code[i], sa_off * 32u);
-                r.sa[i] = __builtin_amdgcn_raw_buffer_load_b16(ras, a_sc[i], sa_off * 4u, 0);
-            }
+        for (int i = 0; i < MI; ++i) {
+            r.ca[i] = load16(rac, s.a_code[i], sa_off * 32u);
+            r.sa[i] = __builtin_amdgcn_raw_buffer_load_b16(ras, s.a_sc[i], sa_off * 4u, 0);
+        }
 #pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                r.cb[j] = load16(rbc, b_code[j], sb_off * 32u);
-                r.sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rbs, b_sc[j], sb_off * 4u, 0);
-            }
-        };
+        for (int j = 0; j < NI; ++j) {
+            r.cb[j] = load16(s.rbc, s.b_code[j], sb_off * 32u);
+            r.sb[j] = __builtin_amdgcn_raw_buffer_load_b16(s.rbs, s.b_sc[j], sb_off * 4u, 0);
+        }
+    };
 
-        f16v acc[MI][NI];
+    f16v acc[MI][NI];
+    auto compute = [&](const Regs& r, bool live) {  // live: a panel of the wave (uniform)
+        h2 sa[MI], sb[NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) sa[i] = e4m3x2_lo(live ? r.sa[i] : 0u);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) sb[j] = e4m3x2_lo(live ? r.sb[j] : 0u);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            h8 av[MI], bv[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) av[i] = decode8(word_of(r.ca[i], s), scale_of(sa[i], s));
+#pragma unroll
+            for (int j = 0; j < NI; ++j) bv[j] = decode8(word_of(r.cb[j], s), scale_of(sb[j], s));
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // A wave whose panels fill whole rounds of the ring loads the next
+    // tile's first panels in its last round, instead of reading its last
+    // panel again, so that they arrive while this tile is reduced and
+    // stored; other waves start each tile with fresh loads.
+    const bool ahead = count > 0 && count % DEPTH == 0;  // (wave-uniform)
+    const int k_last = count > 0 ? (count - 1) / DEPTH * DEPTH : 0;  // first panel of the last round
+    if (t_begin >= t_end) return;
+    Regs ring[DEPTH];
+    int t = t_begin;
+    Src cur = src_of(t);
+    bool loaded = false;  // ring holds the current tile's first panels
+    for (;;) {
+        const int t_next = t + t_step;
+        const bool more = t_next < t_end;
+        const Src nxt = src_of(more ? t_next : t);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-        auto compute = [&](const Regs& r, bool live) {  // live: a panel of the wave (uniform)
-            h2 sa[MI], sb[NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) sa[i] = e4m3x2_lo(live ? r.sa[i] : 0u);
-#pragma unroll
-            for (int j = 0; j < NI; ++j) sb[j] = e4m3x2_lo(live ? r.sb[j] : 0u);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                h8 av[MI], bv[NI];
-#pragma unroll
-                for (int i = 0; i < MI; ++i) av[i] = decode8(word_of(r.ca[i], s), scale_of(sa[i], s));
-#pragma unroll
-                for (int j = 0; j < NI; ++j) bv[j] = decode8(word_of(r.cb[j], s), scale_of(sb[j], s));
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int j = 0; j < NI; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-            }
-        };
-
         if (count > 0) {
-            Regs ring[DEPTH];
+            if (!loaded) {
 #pragma unroll
-            for (int d = 0; d < DEPTH; ++d) load(d, ring[d]);
-            // (the first panels are taken as they arrive, so that the
-            // compiler does not merge these loads with the loop's own)
-#pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    asm volatile("" : "+v"(ring[d].ca[i].x), "+v"(ring[d].ca[i].y), "+v"(ring[d].ca[i].z),
-                                      "+v"(ring[d].ca[i].w), "+v"(ring[d].sa[i]));
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    asm volatile("" : "+v"(ring[d].cb[j].x), "+v"(ring[d].cb[j].y), "+v"(ring[d].cb[j].z),
-                                      "+v"(ring[d].cb[j].w), "+v"(ring[d].sb[j]));
-            }
-            for (int k = 0; k < count; k += DEPTH) {
+                for (int d = 0; d < DEPTH; ++d) load(cur, d, ring[d]);
+                // (the first panels are taken as they arrive, so that the
+                // compiler does not merge these loads with the loop's own)
 #pragma unroll
                 for (int d = 0; d < DEPTH; ++d) {
-                    compute(ring[d], k + d < count);
-                    load(k + d + DEPTH, ring[d]);
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        asm volatile("" : "+v"(ring[d].ca[i].x), "+v"(ring[d].ca[i].y), "+v"(ring[d].ca[i].z),
+                                          "+v"(ring[d].ca[i].w), "+v"(ring[d].sa[i]));
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        asm volatile("" : "+v"(ring[d].cb[j].x), "+v"(ring[d].cb[j].y), "+v"(ring[d].cb[j].z),
+                                          "+v"(ring[d].cb[j].w), "+v"(ring[d].sb[j]));
+                }
+            }
+            for (int k = 0; k < k_last; k += DEPTH) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) {
+                    compute(ring[d], true);
+                    load(cur, k + d + DEPTH, ring[d]);
                     __builtin_amdgcn_sched_barrier(0);  // each slot's loads right after its MFMAs
                 }
             }
+            // the last round: its loads fetch the next tile's first panels
+            // (or, without a next tile or whole rounds, re-read the last one)
+            const bool go = ahead && more;  // (wave-uniform)
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                compute(ring[d], k_last + d < count);
+                load(go ? nxt : cur, go ? d : k_last + d + DEPTH, ring[d]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            loaded = go;
         }
+        const int m0 = cur.m0, n0 = cur.n0, r1 = cur.r1;
 
         // Add the wave tiles in wave order.
 #pragma unroll
@@ -365,6 +396,9 @@ __global__ void __launch_bounds__(WAVES * 64) grouped_wsplit_kernel(GroupedArgs 
             if (row < r1 && col < a.N) a.out[(int64_t)row * a.N + col] = to_bf16(a.alpha * sum[u]);
         }
         __syncthreads();  // every wave is done reading red before the next tile writes it
+        if (!more) break;
+        t = t_next;
+        cur = nxt;
     }
 }
 

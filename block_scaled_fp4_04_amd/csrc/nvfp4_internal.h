@@ -99,7 +99,7 @@ constexpr int kGroupedWaves = 4;   // waves per workgroup (split K)
 constexpr int kGroupedChunks = 2;  // 16-row chunks of A per pass over B
 constexpr int kGroupedUnits = 1;   // 128-element K units of loads in flight per wave
 constexpr int kGroupedBlocks = 4;  // 16-row blocks of B per workgroup (share A's decode)
-constexpr int kGroupedTileRows = 416;  // groups this large on average use the tile kernel
+constexpr int kGroupedTileRows = 464;  // groups this large on average use the tile kernel
 constexpr int kGroupedWsplitRows = 33;   // groups this large (and below kGroupedTileRows) on
                                          // average use the grouped mid-size kernel
 constexpr int kGroupedWsplitWaves = 8;   // waves per workgroup of that kernel (split K)

@@ -260,9 +260,9 @@ int nvfp4_gemm_quantized(const void* x, int x_type, int64_t ldx, const void* b_p
  *   M                  : total rows (0 is allowed: nothing is launched)
  * The kernel follows the average group size M / groups: up to 32 rows (the
  * decode regime, about 16 rows per expert) a skinny kernel built for the
- * memory-bound case; from 33 to 415 rows a mid-size kernel with 64 x 64
+ * memory-bound case; from 33 to 463 rows a mid-size kernel with 64 x 64
  * output tiles of every group taken in turn by a persistent grid (at most
- * 4096 groups, else the skinny kernel); from 416 rows the MFMA tile kernel
+ * 4096 groups, else the skinny kernel); from 464 rows the MFMA tile kernel
  * with 256 x 256 tiles, one workgroup per row block of a group and column
  * block.  Either
  * way the result is the same GEMM, up to the order of the FP32 additions.

@@ -160,15 +160,15 @@ def test_grouped_no_rows():
 
 # Large groups on the tile kernel (256 x 256 tiles: row blocks of each
 # group, with a partial block at every group's end), forced, and each case
-# also on the library's choice (the mid-size kernel up to 415 rows on
-# average, the tile kernel from 416: the last case) and on the skinny kernel
+# also on the library's choice (the mid-size kernel up to 463 rows on
+# average, the tile kernel from 464: the last case) and on the skinny kernel
 # (several passes over B per workgroup).
 @pytest.mark.parametrize("sizes,N,K", [
     ([0, 70, 130, 1, 257, 64, 200], 200, 640),      # empty and 1-row groups
     ([300, 512, 0, 700, 259], 264, 1040),            # K not a multiple of 128
     ([256] * 4 + [512], 256, 2048),                  # whole 256-row blocks only
     ([1, 1000, 3, 300], 136, 384),                   # tiny and large groups
-    ([420, 0, 900, 500], 72, 256),                   # 455 rows on average: tile by default
+    ([520, 0, 900, 500], 72, 256),                   # 480 rows on average: tile by default
 ])
 def test_grouped_tile_path(o, sizes, N, K):
     ops = random_grouped(sum(sizes) * 3 + N + K, sizes, N, K, alpha=-0.625)
@@ -177,7 +177,7 @@ def test_grouped_tile_path(o, sizes, N, K):
         check(o, ops, g, f"grouped {path} path sizes={sizes} N={N} K={K}")
 
 
-# Groups of 33-415 rows on average run on the mid-size kernel: 64 x 64 tiles
+# Groups of 33-463 rows on average run on the mid-size kernel: 64 x 64 tiles
 # of every group (row blocks from each group's first row, the last one cut
 # at the group's end), taken in turn by a persistent grid of at most one
 # workgroup per CU.

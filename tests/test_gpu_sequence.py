@@ -38,8 +38,10 @@ class Step:
     """One decode step: quantise the fp32 activations of 16 tokens and of 1
     token, an MoE up-projection share (16 x 256 x 6144, skinny), an
     attention projection (1 x 768 x 6144, dot products), a 48-row GEMM whose
-    plan splits K across workgroups (workspace), and a grouped GEMM of the
-    16 tokens routed to 2 of 8 experts."""
+    plan splits K across workgroups (workspace), a grouped GEMM of the 16
+    tokens routed to 2 of 8 experts (the decode kernel), and one of 256
+    tokens routed to 2 of 8 experts (about 64 rows per expert: the mid-size
+    kernel)."""
 
     def __init__(self, seed):
         g = torch.Generator(device=DEV).manual_seed(seed)
@@ -55,14 +57,21 @@ class Step:
         self.offsets = torch.from_numpy(gops.offsets).to(DEV)
         self.tok = gops.M                       # 32 routed rows
         self.xg = torch.randn((self.tok, K), generator=g, device=DEV)
+        gops2 = synth.grouped_operands(seed + 1, 256, 8, 2, 96, K, alpha=-0.5)
+        self.experts2 = nv.groups_to_device(gops2.b_codes, gops2.b_scales, DEV)
+        self.offsets2 = torch.from_numpy(gops2.offsets).to(DEV)
+        self.tok2 = gops2.M                     # 512 routed rows
+        self.xg2 = torch.randn((self.tok2, K), generator=g, device=DEV)
         mk = lambda r: nv.PackedOperand(*(torch.empty(n, dtype=torch.uint8, device=DEV)
                                           for n in nv.packed_size(r, K)), r, K)
         self.a16, self.a1, self.a48, self.ag = mk(16), mk(1), mk(48), mk(self.tok)
+        self.ag2 = mk(self.tok2)
         self.out = {
             "up": torch.empty((16, 256), dtype=torch.bfloat16, device=DEV),
             "attn": torch.empty((1, 768), dtype=torch.bfloat16, device=DEV),
             "mid": torch.empty((48, 200), dtype=torch.bfloat16, device=DEV),
             "moe": torch.empty((self.tok, 64), dtype=torch.bfloat16, device=DEV),
+            "moe_mid": torch.empty((self.tok2, 96), dtype=torch.bfloat16, device=DEV),
         }
 
     def eager(self, stream=None):
@@ -75,6 +84,9 @@ class Step:
         nv.gemm(self.a48, self.w_mid, -1.25, out=self.out["mid"], stream=stream)
         nv.grouped_gemm(self.ag, self.experts, self.offsets, 0.75, out=self.out["moe"],
                         stream=stream)
+        nv.quantize(self.xg2, out=self.ag2, stream=stream)
+        nv.grouped_gemm(self.ag2, self.experts2, self.offsets2, -0.5, out=self.out["moe_mid"],
+                        stream=stream)
 
     def record(self) -> nv.Sequence:
         s = nv.Sequence()
@@ -86,6 +98,8 @@ class Step:
         s.add_gemm(self.a1, self.w_attn, self.out["attn"], 0.5)
         s.add_gemm(self.a48, self.w_mid, self.out["mid"], -1.25)
         s.add_grouped_gemm(self.ag, self.experts, self.offsets, self.out["moe"], 0.75)
+        s.add_quantize(self.xg2, self.ag2)
+        s.add_grouped_gemm(self.ag2, self.experts2, self.offsets2, self.out["moe_mid"], -0.5)
         return s
 
     def results(self):
@@ -105,12 +119,12 @@ def test_sequence_replays_match_eager_calls():
     assert plans["mid"]["split_k"] > 1          # the sequence's own workspace is used
     seq = step.record()
     seq.finalize()
-    assert seq.calls == 8
+    assert seq.calls == 10
     stream = torch.cuda.Stream()
     for replay in range(4):
         # new activations, written by the program's own eager work
         with torch.no_grad():
-            for x in (step.x16, step.x1, step.x48, step.xg):
+            for x in (step.x16, step.x1, step.x48, step.xg, step.xg2):
                 x.normal_()
                 x.mul_(1.0 + replay)
         torch.cuda.synchronize()
