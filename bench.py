@@ -170,19 +170,24 @@ def path_name(nv, path: int) -> str:
             nv.PATH_GEMV: "gemv"}.get(path, str(path))
 
 
+def _roofline(b, f, seconds_per_call):
+    """The binding roofline (HBM below the ridge AI = 2.5 PF / 8 TB/s, else
+    the fp16 MFMA peak), with the other resource's rate beside it."""
+    gbps = b / seconds_per_call / 1e9
+    tflops = f / seconds_per_call / 1e12
+    hbm = {"achieved": gbps, "peak": HBM_GBPS, "unit": "GB/s", "frac": gbps / HBM_GBPS}
+    mfma = {"achieved": tflops, "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / MFMA_F16_TFLOPS}
+    if f / b < MFMA_F16_TFLOPS * 1e12 / (HBM_GBPS * 1e9):
+        return {"bound": "hbm", **hbm, "traffic": None, "algorithmic_bytes_per_launch": b,
+                "algorithmic_flops_per_launch": f, "other": dict(resource="mfma", **mfma)}
+    return {"bound": "mfma", **mfma, "traffic": None, "algorithmic_flops_per_launch": f,
+            "algorithmic_bytes_per_launch": b, "other": dict(resource="hbm", **hbm)}
+
+
 def roofline_for(cfg, seconds_per_call):
-    b = synth.algorithmic_bytes(cfg.M, cfg.N, cfg.K)
-    f = synth.flops(cfg.M, cfg.N, cfg.K)
-    ai = f / b
-    ridge = MFMA_F16_TFLOPS * 1e12 / (HBM_GBPS * 1e9)
-    if ai < ridge:
-        ach = b / seconds_per_call / 1e9
-        return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
-                "frac": ach / HBM_GBPS, "traffic": None,
-                "algorithmic_bytes_per_launch": b}
-    ach = f / seconds_per_call / 1e12
-    return {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
-            "frac": ach / MFMA_F16_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": f}
+    return _roofline(synth.algorithmic_bytes(cfg.M, cfg.N, cfg.K),
+                     synth.flops(cfg.M, cfg.N, cfg.K), seconds_per_call)
 
 
 def _operand_sets(nv, torch, cfg, ops, cold):
@@ -300,15 +305,8 @@ def time_workload(nv, torch, cfg, steps, warmup, cold=False, ops=None):
 def grouped_roofline(g, seconds_per_call):
     """As roofline_for, with the grouped GEMM's algorithmic bytes (A, the
     weights of every expert, the output)."""
-    b = synth.grouped_algorithmic_bytes(g.M, g.N, g.K, g.experts)
-    f = synth.flops(g.M, g.N, g.K)
-    if f / b < MFMA_F16_TFLOPS * 1e12 / (HBM_GBPS * 1e9):
-        ach = b / seconds_per_call / 1e9
-        return {"bound": "hbm", "achieved": ach, "peak": HBM_GBPS, "unit": "GB/s",
-                "frac": ach / HBM_GBPS, "traffic": None, "algorithmic_bytes_per_launch": b}
-    ach = f / seconds_per_call / 1e12
-    return {"bound": "mfma", "achieved": ach, "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
-            "frac": ach / MFMA_F16_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": f}
+    return _roofline(synth.grouped_algorithmic_bytes(g.M, g.N, g.K, g.experts),
+                     synth.flops(g.M, g.N, g.K), seconds_per_call)
 
 
 def time_grouped(nv, torch, g, steps, warmup, ops=None, cold=False):
@@ -648,11 +646,12 @@ def measured_peaks(nv, torch, steps):
 
 
 def add_measured_fracs(node, peaks):
-    """Every roofline object in the line also gets its fraction of the
-    measured peak of its bound."""
+    """Every roofline object in the line (and the other resource beside it)
+    also gets its fraction of the measured peak of that resource."""
     if isinstance(node, dict):
-        if "bound" in node and "achieved" in node:
-            p = peaks["hbm_read_gbps"] if node["bound"] == "hbm" else peaks["mfma_f16_tflops"]
+        kind = node.get("bound", node.get("resource"))
+        if kind in ("hbm", "mfma") and "achieved" in node:
+            p = peaks["hbm_read_gbps"] if kind == "hbm" else peaks["mfma_f16_tflops"]
             node["peak_measured"] = p
             node["frac_of_measured"] = node["achieved"] / p
         for v in node.values():
@@ -743,6 +742,17 @@ def grouped_oracle_leg(o, g, ops, gpu_bits):
             {"oracle_s": el, "tflops": 2 * macs / el / 1e12, "threads": o.threads,
              "full_layer_s_extrapolated": el * (g.M * g.N * g.K) / macs,
              "sample": f"{r['n']} output elements ({what})"})
+
+
+def host_pack_ms(nv, ops, reps=3):
+    """Host time of packing A's canonical arrays (nvfp4_pack, one thread),
+    best of `reps`; B is packed once, as weights, and not timed."""
+    best = float("inf")
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        nv.pack(ops.a_codes, ops.a_scales)
+        best = min(best, time.perf_counter() - t0)
+    return best * 1e3
 
 
 def cpu_baseline(cfg, ops, budget_s):
@@ -896,6 +906,10 @@ def main():
         line["floors"] = floors_line(nv, torch, args.steps)
         line["floors"]["measured_peaks"] = peaks
         add_measured_fracs(line, peaks)
+    # after the GPU timing: the host time of packing each workload's A
+    for name, (c, c_ops, _) in outputs.items():
+        pack_ms = host_pack_ms(nv, c_ops)
+        (line if c.index == cfg.index else line["per_shape"][name])["a_host_pack_ms"] = pack_ms
     if not args.no_cpu_baseline:
         # after every GPU timing: the oracle on all host threads, for the
         # headline's baseline figure and, per workload, for the parity of the

@@ -70,3 +70,21 @@ def test_grouped_oracle_leg_checks_every_expert_or_a_sample():
         assert int(e) in picked
     assert par["n"] == sum(int(counts[e]) for e in picked) * cfg2.N
     assert par["over"] == 0 and par["bit_exact_frac"] == 1.0
+
+
+def test_roofline_binds_by_arithmetic_intensity_and_reports_the_other_resource():
+    """Below the ridge (2.5 PF / 8 TB/s = 312.5 FLOP/B) the HBM roofline
+    binds, above it the fp16 MFMA peak; the other resource's rate is beside
+    it.  The decode projection (AI 3.5) and the saturation shape (AI 5,761)."""
+    import bench
+    for i, bound, other in ((2, "hbm", "mfma"), (5, "mfma", "hbm")):
+        c = synth.config(i)
+        r = bench.roofline_for(c, 1e-3)
+        b, f = synth.algorithmic_bytes(c.M, c.N, c.K), synth.flops(c.M, c.N, c.K)
+        assert r["bound"] == bound and r["other"]["resource"] == other
+        gbps, tflops = b / 1e-3 / 1e9, f / 1e-3 / 1e12
+        hbm = r if bound == "hbm" else r["other"]
+        mfma = r if bound == "mfma" else r["other"]
+        assert abs(hbm["achieved"] - gbps) < 1e-9 * gbps and hbm["unit"] == "GB/s"
+        assert abs(mfma["achieved"] - tflops) < 1e-9 * tflops and mfma["unit"] == "TFLOP/s"
+        assert abs(hbm["frac"] - gbps / 8000.0) < 1e-12 and abs(mfma["frac"] - tflops / 2500.0) < 1e-12
