@@ -246,14 +246,27 @@ def unpack(packed_codes: np.ndarray, packed_scales: np.ndarray, rows: int, K: in
     return codes, scales
 
 
+def tile_code(path: int, tile_m: int, tile_n: int) -> int:
+    """The ``tile`` argument of nvfp4_gemm_with_plan that names a path's
+    tile: the edge for PATH_TILE, rows x columns / 64 for PATH_WSPLIT
+    (16, 32, 64, 128 for 32 x 32, 64 x 32, 64 x 64, 128 x 64), else 0."""
+    if path == PATH_TILE:
+        return tile_m
+    if path == PATH_WSPLIT:
+        return tile_m * tile_n // 64
+    return 0
+
+
 def plan(M: int, N: int, K: int) -> dict:
     """The plan nvfp4_gemm uses for the shape (path, tile, split-K, and
-    whether it came from the tuned table)."""
+    whether it came from the tuned table); ``tile`` is its tile as
+    nvfp4_gemm_with_plan takes it."""
     p = _PlanT()
     st = lib().nvfp4_plan(M, N, K, ctypes.byref(p))
     if st:
         raise Nvfp4Error(st, "nvfp4_plan")
     return {"path": p.path, "split_k": p.split_k, "tile_m": p.tile_m, "tile_n": p.tile_n,
+            "tile": tile_code(p.path, p.tile_m, p.tile_n),
             "tail_tiles": p.tail_tiles, "tail_split": p.tail_split, "source": p.source}
 
 

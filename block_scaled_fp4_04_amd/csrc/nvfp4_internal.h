@@ -77,10 +77,16 @@ size_t tile_counters(int cfg, const GemmArgs& a);
 size_t skinny_flagged_words(const GemmArgs& a);
 size_t skinny_counters(const GemmArgs& a);
 
-// Mid-size kernel configurations (waves split K inside a workgroup).
-enum WsplitConfig { WSPLIT_64x64 = 0, WSPLIT_128x64 = 1 };
+// Mid-size kernel configurations (waves split K inside a workgroup), by
+// output tile: rows of A x rows of B.
+enum WsplitConfig { WSPLIT_64x64 = 0, WSPLIT_128x64 = 1, WSPLIT_64x32 = 2, WSPLIT_32x32 = 3 };
 inline TileShape wsplit_shape(int cfg) {
-    return cfg == WSPLIT_64x64 ? TileShape{64, 64} : TileShape{128, 64};
+    switch (cfg) {
+        case WSPLIT_64x64: return TileShape{64, 64};
+        case WSPLIT_64x32: return TileShape{64, 32};
+        case WSPLIT_32x32: return TileShape{32, 32};
+        default: return TileShape{128, 64};
+    }
 }
 size_t wsplit_partial_floats(int cfg, const GemmArgs& a);
 

@@ -866,6 +866,12 @@ __global__ void __launch_bounds__(WAVES * 64, (MB == 1 && UNITS <= 3) ? 2 * WAVE
 // -- a wave's reads of one block are 1 KB contiguous -- with DEPTH panels of
 // loads in flight; the panel's offset is the loads' scalar offset.  At the end the wave tiles are added in LDS in wave order, then
 // (split_k > 1) across workgroups by the last arrival in split order.
+// Tiles: 128 x 64 (four waves), 64 x 64, 64 x 32 and 32 x 32 (eight waves).
+// The smaller tiles cost more decode work per multiply-add but give enough
+// workgroups to fill the CUs without splitting K across workgroups, whose
+// hand-off costs more than that work at these sizes; they also hold fewer
+// registers (about 120 and 90 per lane against 177), so two or three of
+// their workgroups share a CU.
 // ---------------------------------------------------------------------------
 // (Plain arguments, operands and geometry first, so that those can be
 // preloaded into scalar registers before the waves start.)
@@ -1513,6 +1519,14 @@ hipError_t launch_wsplit(int cfg, const GemmArgs& a, hipStream_t stream) {
         case WSPLIT_64x64:
             if (split) NVFP4_WSPLIT(64, 64, 8, true, 512);
             else NVFP4_WSPLIT(64, 64, 8, false, 512);
+            break;
+        case WSPLIT_64x32:
+            if (split) NVFP4_WSPLIT(64, 32, 8, true, 512);
+            else NVFP4_WSPLIT(64, 32, 8, false, 512);
+            break;
+        case WSPLIT_32x32:
+            if (split) NVFP4_WSPLIT(32, 32, 8, true, 512);
+            else NVFP4_WSPLIT(32, 32, 8, false, 512);
             break;
         default:  // WSPLIT_128x64
             if (split) NVFP4_WSPLIT(128, 64, 4, true, 256);

@@ -71,7 +71,7 @@ bool tile_allowed(int path, int tile) {
         case NVFP4_PATH_SKINNY:
         case NVFP4_PATH_GEMV: return tile == 0;
         case NVFP4_PATH_TILE: return tile == 0 || tile == 64 || tile == 128 || tile == 256;
-        case NVFP4_PATH_WSPLIT: return tile == 0 || tile == 64 || tile == 128;
+        case NVFP4_PATH_WSPLIT: return tile == 0 || tile == 16 || tile == 32 || tile == 64 || tile == 128;
         default: return false;
     }
 }
@@ -340,8 +340,39 @@ void plan_skinny(int64_t M, int64_t N, int steps, int split_req, Plan* p) {
     p->tiles_n = (int)groups;
 }
 
+// Estimated device time (us, beyond the per-call floor) of the mid-size
+// kernel with configuration `cfg` and `s` K slices.  Measured on an MI355X
+// at M = 1..4096, N = 256..8192, K = 2048..16384 (graph replays): a tile
+// costs about kWsplitPanelUs per 64-element K panel, the same for 1 to 256
+// tiles; more tiles than CUs take further rounds; a split-K hand-off between
+// workgroups (a ticket and the round trip of the partial tiles through
+// memory) costs about 2 + s / 4 us.
+constexpr double kWsplitPanelUs[4] = {0.115, 0.2, 0.071, 0.038};  // by WsplitConfig
+double wsplit_estimate(int cfg, int64_t M, int64_t N, int steps, int s) {
+    const TileShape t = wsplit_shape(cfg);
+    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const int64_t rounds = (tiles * s + kCUs - 1) / kCUs;
+    return kWsplitPanelUs[cfg] * (2.0 * steps) * (double)rounds / s + (s > 1 ? 2.0 + 0.25 * s : 0.0);
+}
+
+// tile: 0 (choose), 16 (32 x 32), 32 (64 x 32), 64 (64 x 64) or 128 (128 x 64).
 void plan_wsplit(int64_t M, int64_t N, int steps, int tile, int split_req, Plan* p) {
-    const int cfg = tile == 128 ? WSPLIT_128x64 : WSPLIT_64x64;
+    int cfg = tile == 128 ? WSPLIT_128x64 : tile == 64 ? WSPLIT_64x64
+            : tile == 32 ? WSPLIT_64x32 : WSPLIT_32x32;
+    if (tile == 0) {
+        // From the largest tile down, a smaller tile only where it is
+        // estimated at least 10% faster without splitting K.
+        double best = 0.0;
+        bool first = true;
+        for (int c : {WSPLIT_128x64, WSPLIT_64x64, WSPLIT_64x32, WSPLIT_32x32}) {
+            const double e = wsplit_estimate(c, M, N, steps, 1);
+            if (first || e < 0.9 * best) {
+                cfg = c;
+                best = e;
+                first = false;
+            }
+        }
+    }
     const TileShape s = wsplit_shape(cfg);
     p->cfg = cfg;
     p->tiles_m = (int)((M + s.bm - 1) / s.bm);
@@ -349,13 +380,18 @@ void plan_wsplit(int64_t M, int64_t N, int steps, int tile, int split_req, Plan*
     const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
     int sk = split_req;
     if (sk <= 0) {
-        // A workgroup occupies a whole CU, so split K across workgroups only
-        // while every workgroup still has a CU of its own, and at most 3
-        // ways (more slices cost more in the cross-workgroup reduction than
-        // they save: measured at M = 32..2048, K = 6144), keeping at least
-        // one panel per wave.
+        // Split K across workgroups only while every slice keeps a CU of its
+        // own and at least one panel per wave, and only where that is
+        // estimated at least 10% faster (long K on few tiles).
         sk = 1;
-        while (sk < 3 && tiles * (sk + 1) <= kCUs && (int64_t)(sk + 1) * 8 <= 2 * steps) ++sk;
+        double best = wsplit_estimate(cfg, M, N, steps, 1);
+        for (int k = 2; k <= 8 && tiles * k <= kCUs && (int64_t)k * 8 <= 2 * steps; ++k) {
+            const double e = wsplit_estimate(cfg, M, N, steps, k);
+            if (e < 0.9 * best) {
+                sk = k;
+                best = e;
+            }
+        }
     }
     if (sk > steps) sk = steps;
     p->split_k = sk < 1 ? 1 : sk;
@@ -423,19 +459,20 @@ int make_plan(int64_t M, int64_t N, int64_t K, int path, int tile, int split_req
         // 6144 .. 8192 (device time per call):
         //  * the dot-product kernel wins only while the whole output is at
         //    most 2048 elements of one or two rows; beyond that the skinny
-        //    kernel's 16-row MFMA blocks are faster, up to 64 rows while
-        //    N <= 2048 (one workgroup per CU and 16 columns: more columns
-        //    than that make more than one round);
+        //    kernel's 16-row MFMA blocks are faster, up to 16 rows while
+        //    N <= 4096 and 32 rows while N <= 1024 (16 x 2048 x 6144: 4.4 us
+        //    against 5.8 us on 32 x 32 tiles of the mid-size kernel; 16 x
+        //    6144 x 6144: 6.7 against 5.9 us; 64 x 768: 6.6 against 5.8 us);
         //  * the LDS-fed tile kernel wins once its tiles give about 3/4 of
         //    a workgroup per CU: 256 x 256 tiles, else 128 x 128 tiles
         //    (with two K slices below two tiles per CU);
-        //  * below that the kernel whose waves split K wins, with 128-row
-        //    tiles once those alone give 3/4 of a workgroup per CU.
+        //  * below that the kernel whose waves split K wins, with the tile
+        //    and K split its cost estimate picks (plan_wsplit).
         const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
         if (M <= 2 && M * N <= 2048) {
             path = NVFP4_PATH_GEMV;
-        } else if (M <= 16 || (M <= 64 && N <= 2048)) {
+        } else if ((M <= 16 && N <= 4096) || (M <= 32 && N <= 1024)) {
             path = NVFP4_PATH_SKINNY;
         } else if (t256 >= (3 * kCUs) / 4) {
             path = NVFP4_PATH_TILE;
@@ -447,8 +484,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int path, int tile, int split_req
             split_req = split_req ? split_req : (t128 >= 2 * kCUs ? 1 : 2);
         } else {
             path = NVFP4_PATH_WSPLIT;
-            const int64_t w128 = ((M + 127) / 128) * ((N + 63) / 64);
-            tile = w128 >= (3 * kCUs) / 4 ? 128 : 64;
+            tile = 0;
         }
     }
     p->path = path;

@@ -60,9 +60,9 @@ def candidates(M: int, N: int, K: int) -> list[tuple[int, int, int]]:
             # at least four 128-element K steps per workgroup
             if s <= min(SKINNY_MAX_SPLIT, max(1, steps // 4)) and groups * s <= 4096:
                 out.append((nv.PATH_SKINNY, 0, s))
-    if M > 4:
-        for tile in (64, 128):
-            tiles = cdiv(M, tile) * cdiv(N, 64)
+    if M > 4 or N > 4096:
+        for tile, (bm, bn) in ((16, (32, 32)), (32, (64, 32)), (64, (64, 64)), (128, (128, 64))):
+            tiles = cdiv(M, bm) * cdiv(N, bn)
             for s in (1, 2, 3, 4, 6, 8):
                 if s * 8 <= 2 * steps and tiles * s <= 2048 and (s == 1 or tiles * s <= 1024):
                     out.append((nv.PATH_WSPLIT, tile, s))
@@ -128,8 +128,7 @@ def tune_shape(M, N, K, device, stream, log) -> dict:
     out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
     nv.clear_plan_table()
     h = nv.plan(M, N, K)
-    heur = (h["path"], h["tile_m"] if h["path"] in (nv.PATH_TILE, nv.PATH_WSPLIT) else 0,
-            h["split_k"])
+    heur = (h["path"], h["tile"], h["split_k"])
     # calls per graph: about 2 ms of work, at least 5
     t1 = time_plan(a, b, out, heur, stream, 5)
     reps = int(min(200, max(5, 2000.0 / max(t1, 1e-3))))

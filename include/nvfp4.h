@@ -162,10 +162,12 @@ int nvfp4_gemm(const void* a_packed, const void* a_scales, const void* b_packed,
 /* nvfp4_gemm with a forced launch plan, for tuning and tests:
  *   path    : NVFP4_PATH_* (NVFP4_PATH_AUTO = library's choice, then tile
  *             must be 0)
- *   tile    : 0 = library's choice; else the workgroup's output tile edge:
- *             256, 128 or 64 for NVFP4_PATH_TILE (square tiles), 64 or 128
- *             rows (of 64 columns) for NVFP4_PATH_WSPLIT; must be 0 for the
- *             skinny and gemv paths (fixed tiles)
+ *   tile    : 0 = library's choice; else the workgroup's output tile:
+ *             its edge for NVFP4_PATH_TILE (256, 128 or 64: square tiles);
+ *             rows x columns / 64 for NVFP4_PATH_WSPLIT (16 = 32 x 32,
+ *             32 = 64 x 32, 64 = 64 x 64, 128 = 128 x 64; rows of C x
+ *             columns of C); must be 0 for the skinny and gemv paths (fixed
+ *             tiles)
  *   split_k : 0 = library's choice, else the number of K slices, clamped to
  *             the number of 128-element K steps
  * Same contract as nvfp4_gemm.  A bad path or tile is NVFP4_ERR_INVALID_VALUE;

@@ -102,8 +102,8 @@ def test_gemm_rejects_bad_arguments_before_launch():
     assert _wp(4, 4, 64, 0, split_k=-1) == nv.ERR_INVALID_VALUE
     # tiles the path does not have
     for path, tile in [(nv.PATH_AUTO, 128), (nv.PATH_TILE, 96), (nv.PATH_TILE, 32),
-                       (nv.PATH_WSPLIT, 256), (nv.PATH_SKINNY, 16), (nv.PATH_GEMV, 4),
-                       (nv.PATH_TILE, -1)]:
+                       (nv.PATH_WSPLIT, 256), (nv.PATH_WSPLIT, 48), (nv.PATH_WSPLIT, 8),
+                       (nv.PATH_SKINNY, 16), (nv.PATH_GEMV, 4), (nv.PATH_TILE, -1)]:
         assert _wp(4, 32, 64, path, tile) == nv.ERR_INVALID_VALUE, (path, tile)
 
 
@@ -115,8 +115,9 @@ def test_gemm_refuses_operands_past_32bit_offsets():
     refusals are asserted here: an accepted call would launch on a GPU host;
     the GPU parity tests run operands one row-block under the limit.)"""
     K = 131072
-    for path, tile in ((nv.PATH_TILE, 256), (nv.PATH_TILE, 128), (nv.PATH_WSPLIT, 64),
-                       (nv.PATH_WSPLIT, 128), (nv.PATH_AUTO, 0)):
+    for path, tile in ((nv.PATH_TILE, 256), (nv.PATH_TILE, 128), (nv.PATH_WSPLIT, 16),
+                       (nv.PATH_WSPLIT, 32), (nv.PATH_WSPLIT, 64), (nv.PATH_WSPLIT, 128),
+                       (nv.PATH_AUTO, 0)):
         assert _wp(32768, 256, K, path, tile) == nv.ERR_UNSUPPORTED, (path, tile)
         assert _wp(256, 32768, K, path, tile) == nv.ERR_UNSUPPORTED, (path, tile)
 
@@ -238,12 +239,11 @@ def test_plan(no_table):
     """The library's own rules (no tuned table loaded)."""
     def key(M, N, K):
         p = nv.plan(M, N, K)
-        return nv.PATH_NAMES[p["path"]], p["tile_m"], p["split_k"]
+        return nv.PATH_NAMES[p["path"]], p["tile"], p["split_k"]
     # dot products only for at most 2048 outputs of one or two rows
     assert key(1, 768, 6144)[0] == "gemv"
     assert key(1, 2048, 6144)[0] == "gemv"
     assert key(2, 768, 6144)[0] == "gemv"
-    assert key(1, 6144, 6144)[0] == "skinny"
     assert key(2, 2048, 6144)[0] == "skinny"
     assert key(4, 256, 6144)[0] == "skinny"
     assert key(16, 256, 6144)[0] == "skinny"
@@ -254,23 +254,35 @@ def test_plan(no_table):
     assert key(4096, 2048, 6144) == ("tile", 128, 1)          # 512 tiles
     assert key(1024, 6144, 6144) == ("tile", 128, 2)          # 384 tiles
     assert key(2048, 2048, 6144) == ("tile", 128, 2)          # 256 tiles
-    # else waves split K; 128-row tiles once they alone fill 3/4 of the CUs
+    # else waves split K, on the tile and split of the cost estimate (tile
+    # codes: 128 = 128 x 64, 64 = 64 x 64, 32 = 64 x 32, 16 = 32 x 32); each
+    # expectation is the fastest plan measured for the shape
     assert key(1024, 2048, 6144) == ("wsplit", 128, 1)        # 256 tiles of 128 x 64
-    assert key(512, 2048, 6144) == ("wsplit", 64, 1)
-    assert key(512, 768, 6144) == ("wsplit", 64, 2)
-    # skinny up to 64 rows while N <= 2048: with 2-4 row blocks and up to 64
-    # column groups K splits 3 ways (two blocks) or 4 ways, else two K slices
-    # from 33 rows on
-    assert key(32, 256, 6144) == ("skinny", 16, 3)
-    assert key(64, 768, 6144) == ("skinny", 16, 4)
-    assert key(32, 2048, 6144) == ("skinny", 16, 1)
-    assert key(64, 2048, 6144) == ("skinny", 16, 2)
-    assert key(16, 256, 6144) == ("skinny", 16, 1)
-    assert key(64, 6144, 6144)[0] == "wsplit"
-    assert key(65, 256, 6144) == ("wsplit", 64, 3)            # at most 3 slices
-    for M, N, K in [(512, 768, 6144), (512, 2048, 6144), (300, 5000, 64), (128, 64, 4096)]:
+    assert key(2048, 768, 6144) == ("wsplit", 128, 1)
+    assert key(512, 2048, 6144) == ("wsplit", 64, 1)          # 256 tiles of 64 x 64
+    assert key(1024, 768, 6144) == ("wsplit", 64, 1)
+    assert key(512, 768, 6144) == ("wsplit", 32, 1)           # 192 tiles of 64 x 32
+    assert key(256, 2048, 6144) == ("wsplit", 32, 1)
+    assert key(64, 6144, 6144) == ("wsplit", 32, 1)
+    assert key(256, 768, 6144) == ("wsplit", 16, 1)           # 192 tiles of 32 x 32
+    assert key(512, 256, 6144) == ("wsplit", 16, 1)
+    assert key(128, 256, 6144) == ("wsplit", 16, 1)           # 32 tiles, still unsplit
+    assert key(200, 300, 2048) == ("wsplit", 16, 1)
+    # K split only for long K on few tiles (64 x 256 x 16384: 16 tiles)
+    assert key(64, 256, 16384)[:2] == ("wsplit", 16) and 4 <= key(64, 256, 16384)[2] <= 8
+    # skinny up to 16 rows while N <= 4096 and 32 rows while N <= 1024, with
+    # 2-4 row blocks and up to 64 column groups K splits 3 or 4 ways
+    assert key(16, 256, 6144) == ("skinny", 0, 1)
+    assert key(16, 2048, 6144)[0] == "skinny"
+    assert key(32, 256, 6144) == ("skinny", 0, 3)
+    assert key(32, 768, 6144)[0] == "skinny"
+    # past those, 32 x 32 tiles of the mid-size kernel
+    for M, N in [(1, 6144), (16, 6144), (32, 2048), (48, 768), (64, 768), (64, 2048)]:
+        assert key(M, N, 6144) == ("wsplit", 16, 1), (M, N)
+    for M, N, K in [(512, 768, 6144), (512, 2048, 6144), (300, 5000, 64), (128, 64, 4096),
+                    (64, 256, 16384), (40, 100, 65536)]:
         p = nv.plan(M, N, K)
-        assert p["path"] == nv.PATH_WSPLIT and 1 <= p["split_k"] <= 3
+        assert p["path"] == nv.PATH_WSPLIT and 1 <= p["split_k"] <= 8
         # split K only while every workgroup keeps a CU to itself
         tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
         assert p["split_k"] == 1 or tiles * p["split_k"] <= 256

@@ -231,7 +231,8 @@ def test_operand_just_under_32bit_offsets(o, big):
     ns = np.random.Generator(np.random.PCG64(10)).integers(0, N, 2048)
     outs = {}
     for path, tile in ((nv.PATH_AUTO, 0), (nv.PATH_TILE, 256), (nv.PATH_TILE, 128),
-                       (nv.PATH_WSPLIT, 64), (nv.PATH_WSPLIT, 128)):
+                       (nv.PATH_WSPLIT, 16), (nv.PATH_WSPLIT, 32), (nv.PATH_WSPLIT, 64),
+                       (nv.PATH_WSPLIT, 128)):
         say(f"{big}: path {path} tile {tile}")
         g = nv.gemm(a, b, ops.alpha, path=path, tile=tile)
         torch.cuda.synchronize()

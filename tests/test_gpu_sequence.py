@@ -37,21 +37,22 @@ def bits(t):
 class Step:
     """One decode step: quantise the fp32 activations of 16 tokens and of 1
     token, an MoE up-projection share (16 x 256 x 6144, skinny), an
-    attention projection (1 x 768 x 6144, dot products), a 48-row GEMM whose
-    plan splits K across workgroups (workspace), a grouped GEMM of the 16
+    attention projection (1 x 768 x 6144, dot products), a 48 x 200 x 16384
+    GEMM whose plan splits K across workgroups (long K on few tiles: the
+    workspace is used), a grouped GEMM of the 16
     tokens routed to 2 of 8 experts (the decode kernel), and one of 256
     tokens routed to 2 of 8 experts (about 64 rows per expert: the mid-size
     kernel)."""
 
     def __init__(self, seed):
         g = torch.Generator(device=DEV).manual_seed(seed)
-        K = 6144
+        K, KM = 6144, 16384
         self.x16 = torch.randn((16, K), generator=g, device=DEV)
         self.x1 = torch.randn((1, K), generator=g, device=DEV)
-        self.x48 = torch.randn((48, K), generator=g, device=DEV)
+        self.x48 = torch.randn((48, KM), generator=g, device=DEV)
         self.w_up = nv.quantize(torch.randn((256, K), generator=g, device=DEV))
         self.w_attn = nv.quantize(torch.randn((768, K), generator=g, device=DEV) * 0.02)
-        self.w_mid = nv.quantize(torch.randn((200, K), generator=g, device=DEV))
+        self.w_mid = nv.quantize(torch.randn((200, KM), generator=g, device=DEV))
         gops = synth.grouped_operands(seed, 16, 8, 2, 64, K, alpha=0.75)
         self.experts = nv.groups_to_device(gops.b_codes, gops.b_scales, DEV)
         self.offsets = torch.from_numpy(gops.offsets).to(DEV)
@@ -62,9 +63,9 @@ class Step:
         self.offsets2 = torch.from_numpy(gops2.offsets).to(DEV)
         self.tok2 = gops2.M                     # 512 routed rows
         self.xg2 = torch.randn((self.tok2, K), generator=g, device=DEV)
-        mk = lambda r: nv.PackedOperand(*(torch.empty(n, dtype=torch.uint8, device=DEV)
-                                          for n in nv.packed_size(r, K)), r, K)
-        self.a16, self.a1, self.a48, self.ag = mk(16), mk(1), mk(48), mk(self.tok)
+        mk = lambda r, k=K: nv.PackedOperand(*(torch.empty(n, dtype=torch.uint8, device=DEV)
+                                               for n in nv.packed_size(r, k)), r, k)
+        self.a16, self.a1, self.a48, self.ag = mk(16), mk(1), mk(48, KM), mk(self.tok)
         self.ag2 = mk(self.tok2)
         self.out = {
             "up": torch.empty((16, 256), dtype=torch.bfloat16, device=DEV),
@@ -114,7 +115,7 @@ class Step:
 def test_sequence_replays_match_eager_calls():
     step = Step(31)
     plans = {k: nv.plan(*shape) for k, shape in
-             [("up", (16, 256, 6144)), ("attn", (1, 768, 6144)), ("mid", (48, 200, 6144))]}
+             [("up", (16, 256, 6144)), ("attn", (1, 768, 6144)), ("mid", (48, 200, 16384))]}
     say(f"sequence plans {plans}")
     assert plans["mid"]["split_k"] > 1          # the sequence's own workspace is used
     seq = step.record()
@@ -179,7 +180,7 @@ def test_eager_call_under_capture_needs_its_workspace_first():
     nv.quantize(step.x48, out=step.a48)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
-    assert nv.plan(48, 200, 6144)["split_k"] > 1
+    assert nv.plan(48, 200, 16384)["split_k"] > 1
     g = torch.cuda.CUDAGraph()
     with pytest.raises(nv.Nvfp4Error) as e:
         with torch.cuda.graph(g, stream=s):

@@ -12,8 +12,8 @@ def test_scratch_bytes_follow_the_plan():
     # no split-K: nothing needed
     assert nv.noalloc_scratch_bytes(1, 768, 6144) == (0, True)
     # a split-K plan: its counters and FP32 partial tiles
-    need, fits = nv.noalloc_scratch_bytes(512, 768, 6144)
-    p = nv.plan(512, 768, 6144)
+    need, fits = nv.noalloc_scratch_bytes(64, 200, 16384)
+    p = nv.plan(64, 200, 16384)
     assert p["split_k"] > 1 and fits and need > 0
     # a tail round of 6144^3: more partial tiles than the array holds
     need, fits = nv.noalloc_scratch_bytes(6144, 6144, 6144)
