@@ -463,25 +463,23 @@ int make_plan(int64_t M, int64_t N, int64_t K, int path, int tile, int split_req
         //    N <= 4096 and 32 rows while N <= 1024 (16 x 2048 x 6144: 4.4 us
         //    against 5.8 us on 32 x 32 tiles of the mid-size kernel; 16 x
         //    6144 x 6144: 6.7 against 5.9 us; 64 x 768: 6.6 against 5.8 us);
-        //  * the LDS-fed tile kernel wins once its tiles give about 3/4 of
-        //    a workgroup per CU: 256 x 256 tiles, else 128 x 128 tiles
-        //    (with two K slices below two tiles per CU);
+        //  * the LDS-fed tile kernel wins once its 256 x 256 tiles give about
+        //    3/4 of a workgroup per CU, and with two K slices from half a
+        //    workgroup per CU (4096 x 2048 x 6144: 88 us against 95 us on
+        //    128 x 128 tiles);
         //  * below that the kernel whose waves split K wins, with the tile
-        //    and K split its cost estimate picks (plan_wsplit).
+        //    and K split its cost estimate picks (plan_wsplit): 6-16% faster
+        //    than 128 x 128 tiles of the tile kernel split two ways at 192-511
+        //    such tiles (2048 x 2048 x 6144: 49 against 55 us).
         const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-        const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
         if (M <= 2 && M * N <= 2048) {
             path = NVFP4_PATH_GEMV;
         } else if ((M <= 16 && N <= 4096) || (M <= 32 && N <= 1024)) {
             path = NVFP4_PATH_SKINNY;
-        } else if (t256 >= (3 * kCUs) / 4) {
+        } else if (t256 >= kCUs / 2) {
             path = NVFP4_PATH_TILE;
             tile = 256;
-            split_req = split_req ? split_req : 1;
-        } else if (t128 >= (3 * kCUs) / 4) {
-            path = NVFP4_PATH_TILE;
-            tile = 128;
-            split_req = split_req ? split_req : (t128 >= 2 * kCUs ? 1 : 2);
+            split_req = split_req ? split_req : (t256 >= (3 * kCUs) / 4 ? 1 : 2);
         } else {
             path = NVFP4_PATH_WSPLIT;
             tile = 0;

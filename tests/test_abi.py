@@ -247,13 +247,18 @@ def test_plan(no_table):
     assert key(2, 2048, 6144)[0] == "skinny"
     assert key(4, 256, 6144)[0] == "skinny"
     assert key(16, 256, 6144)[0] == "skinny"
-    # 256 x 256 tiles once they give 3/4 of a workgroup per CU
+    # 256 x 256 tiles once they give 3/4 of a workgroup per CU, split in
+    # two from half a workgroup per CU
     assert key(16384, 8192, 8192) == ("tile", 256, 1)
     assert key(2048, 6144, 6144) == ("tile", 256, 1)          # 192 tiles
-    # else 128 x 128 tiles, split in two below two tiles per CU
-    assert key(4096, 2048, 6144) == ("tile", 128, 1)          # 512 tiles
-    assert key(1024, 6144, 6144) == ("tile", 128, 2)          # 384 tiles
-    assert key(2048, 2048, 6144) == ("tile", 128, 2)          # 256 tiles
+    assert key(4096, 2048, 6144) == ("tile", 256, 2)          # 128 tiles
+    assert key(1024, 8192, 8192) == ("tile", 256, 2)
+    # below that the mid-size kernel, also where 128 x 128 tiles would number
+    # 192-511 (each expectation the fastest plan measured for the shape)
+    assert key(1024, 6144, 6144) == ("wsplit", 128, 1)
+    assert key(2048, 2048, 6144) == ("wsplit", 128, 1)
+    assert key(8192, 768, 6144) == ("wsplit", 128, 1)
+    assert key(16384, 256, 6144) == ("wsplit", 128, 1)
     # else waves split K, on the tile and split of the cost estimate (tile
     # codes: 128 = 128 x 64, 64 = 64 x 64, 32 = 64 x 32, 16 = 32 x 32); each
     # expectation is the fastest plan measured for the shape

@@ -176,12 +176,15 @@ EDGE_SHAPES = [(1, 1, 16), (1, 17, 32), (2, 33, 48), (15, 16, 80), (16, 255, 616
 
 @pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
 def test_edge_shapes(o, M, N, K):
+    """Every path on outputs smaller than one tile and ragged in both
+    dimensions, each tile of the mid-size kernel forced (32 x 32, 64 x 32,
+    64 x 64, 128 x 64)."""
     ops = synth.random_operands(1000 * M + N + K, M, N, K, alpha=0.75)
-    paths = [nv.PATH_AUTO, nv.PATH_TILE, nv.PATH_WSPLIT] + ([nv.PATH_SKINNY] if M <= 16 else []) \
-        + ([nv.PATH_GEMV] if M <= 4 else [])
-    for path in paths:
-        g = run_gpu(ops, path=path, label="edge")
-        check_full(o, ops, g, f"edge {M}x{N}x{K} path {path}")
+    plans = [(nv.PATH_AUTO, 0), (nv.PATH_TILE, 0)] + [(nv.PATH_WSPLIT, t) for t in (16, 32, 64, 128)] \
+        + ([(nv.PATH_SKINNY, 0)] if M <= 16 else []) + ([(nv.PATH_GEMV, 0)] if M <= 4 else [])
+    for path, tile in plans:
+        g = run_gpu(ops, path=path, tile=tile, label="edge")
+        check_full(o, ops, g, f"edge {M}x{N}x{K} path {path} tile {tile}")
 
 
 @pytest.mark.parametrize("M,N,K", [(4100, 4198, 128), (4352, 4096, 640)])
