@@ -301,7 +301,9 @@ enum {
 typedef struct nvfp4_plan_t {
     int32_t path;    /* NVFP4_PATH_TILE / _SKINNY / _WSPLIT / _GEMV */
     int32_t tile_m;  /* output rows of one workgroup's tile */
-    int32_t tile_n;  /* output columns of one workgroup's tile */
+    int32_t tile_n;  /* output columns of one workgroup's tile (the `tile`
+                        argument of nvfp4_gemm_with_plan is tile_m for the
+                        tile path, tile_m x tile_n / 64 for wsplit) */
     int32_t split_k; /* number of K slices (>= 1) */
     int32_t tail_tiles; /* tile path, split_k 1: the last tail_tiles tiles run in a */
     int32_t tail_split; /* second launch with K split tail_split ways (0 if none)  */
@@ -322,7 +324,8 @@ int nvfp4_plan(int64_t M, int64_t N, int64_t K, nvfp4_plan_t* plan);
  *     "entries": [ { "M": 4096, "N": 2048, "K": 6144, "path": "tile",
  *                    "tile": 128, "split_k": 1 }, ... ] }
  * "path" is "tile", "skinny", "wsplit" or "gemv"; "tile" and "split_k" follow
- * nvfp4_gemm_with_plan (tile 0 = the path's default; split_k >= 1); other
+ * nvfp4_gemm_with_plan (tile 0 = the library's choice for the path, e.g.
+ * "wsplit" tile 16 = 32 x 32, 32 = 64 x 32; split_k >= 1); other
  * keys are ignored.  Every entry is checked: sizes as for nvfp4_gemm, the
  * tile allowed for the path, skinny only for M <= 64 and gemv for M <= 4.
  * A later entry for the same (M, N, K) replaces an earlier one.

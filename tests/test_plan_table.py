@@ -46,8 +46,10 @@ def base(tmp_path, no_table):
         entry(512, 768, 6144, "wsplit", 128, 3),
         entry(16, 256, 6144, "skinny", 0, 2),
         entry(4, 768, 6144, "gemv"),
+        entry(256, 768, 8192, "wsplit", 16, 1),
+        entry(512, 768, 8192, "wsplit", 32, 2),
     ]), "base.json")
-    assert load(path)[:2] == (nv.OK, 5)
+    assert load(path)[:2] == (nv.OK, 7)
     yield path
 
 
@@ -67,6 +69,12 @@ def test_exact_and_nearby_shapes(base):
     assert (w["path"], w["tile_m"], w["tile_n"], w["split_k"]) == (nv.PATH_WSPLIT, 128, 64, 3)
     s = nv.plan(9, 256, 6144)
     assert (s["path"], s["split_k"], s["source"]) == (nv.PATH_SKINNY, 2, nv.PLAN_TABLE)
+    # the mid-size kernel's small tiles: codes 16 (32 x 32) and 32 (64 x 32)
+    w = nv.plan(256, 768, 8192)
+    assert (w["path"], w["tile_m"], w["tile_n"], w["tile"], w["source"]) == \
+        (nv.PATH_WSPLIT, 32, 32, 16, nv.PLAN_TABLE)
+    w = nv.plan(512, 768, 8192)
+    assert (w["tile_m"], w["tile_n"], w["tile"], w["split_k"]) == (64, 32, 32, 2)
     g = nv.plan(3, 768, 6144)
     assert (g["path"], g["source"]) == (nv.PATH_GEMV, nv.PLAN_TABLE)
 
@@ -132,6 +140,7 @@ BAD_TABLES = {
     "unknown path": [entry(64, 64, 128, "simd")],
     "tile the path lacks": [entry(64, 64, 128, "tile", 96)],
     "wsplit tile 256": [entry(64, 64, 128, "wsplit", 256)],
+    "wsplit tile 48": [entry(64, 64, 128, "wsplit", 48)],
     "skinny tile": [entry(8, 64, 128, "skinny", 16)],
     "skinny above 64 rows": [entry(65, 64, 128, "skinny")],
     "gemv above 4 rows": [entry(5, 64, 128, "gemv")],
