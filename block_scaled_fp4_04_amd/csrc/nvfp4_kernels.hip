@@ -363,10 +363,16 @@ __global__ void __launch_bounds__(256, 1) tile_kernel(GemmArgs a) {
                 for (int i = 0; i < MI; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                         bv[c][j], av[c][i], (first && s == 0) ? f16v{} : acc[i][j], 0, 0, 0);
+            // each MFMA followed by its share of the sub-step's VALU work: 8
+            // decode instructions per fragment, its scale convert and, in
+            // the last sub-step, its scale shift (with the decode alone
+            // counted, the last 16-24 instructions of a panel ran after its
+            // last MFMA: 256 x 256 tiles 0.5-1% slower; a share of six
+            // instead of five per MFMA was 2-3% slower)
 #pragma unroll
             for (int m = 0; m < MI * NI; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, (8 * (MI + NI) + MI * NI - 1) / (MI * NI), 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, (10 * (MI + NI) + MI * NI - 1) / (MI * NI), 0);
             }
         }
     };
