@@ -1290,6 +1290,11 @@ __global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(
                 asc[i][m] = *reinterpret_cast<const uint16_t*>(a_scales + arow * 4 + half * 2);
             }
         }
+        // The epilogue's arguments (past the preloaded ones) are fetched
+        // while the operand loads are in flight rather than after the dot
+        // products, where their scalar load sat on the kernel's last steps:
+        // 1-2 x 768 x 6144 2.79 -> 2.77 and 3.23 -> 3.15 us.
+        asm volatile("" ::"s"(alpha), "s"(M), "s"(N), "s"(out));
         gemv_batch<MR, HPL>(bw, bsc, aw, asc, base, lane, hp_total, acc);
     }
 #pragma unroll
