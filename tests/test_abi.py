@@ -370,3 +370,32 @@ def test_device_flags_and_poll_hook_on_the_host():
     assert L.nvfp4_debug_set_handoff_polls(0) == nv.OK
     assert L.nvfp4_debug_set_handoff_polls(0xFFFFFFFF) == nv.OK
     assert "flag" in nv.status_string(nv.ERR_DEVICE_FLAGS)
+
+
+def test_plan_rules_on_random_shapes(no_table):
+    """The library's own rules (no tuned table) on 3000 seeded random shapes:
+    every plan names a tile its path has, splits K only while every slice
+    keeps a CU of its own (skinny: at most 16 ways) with at least one
+    64-element panel per wave, and the skinny and gemv paths only take the
+    rows they can."""
+    rng = np.random.Generator(np.random.PCG64(2024))
+    wsplit_tiles = {(32, 32), (64, 32), (64, 64), (128, 64)}
+    for _ in range(3000):
+        M = int(rng.choice([rng.integers(1, 65), rng.integers(1, 4097), rng.integers(1, 20000)]))
+        N = int(rng.choice([rng.integers(1, 300), rng.integers(1, 9000)]))
+        K = 16 * int(rng.choice([rng.integers(1, 40), rng.integers(1, 1100)]))
+        p = nv.plan(M, N, K)
+        path, tm, tn, s = p["path"], p["tile_m"], p["tile_n"], p["split_k"]
+        panels = -(-K // 64)
+        assert 1 <= s <= max(1, -(-K // 128)), (M, N, K, p)
+        if path == nv.PATH_GEMV:
+            assert M <= 2 and M * N <= 2048 and s == 1, (M, N, K, p)
+        elif path == nv.PATH_SKINNY:
+            assert M <= 32 and s <= 16, (M, N, K, p)
+        elif path == nv.PATH_WSPLIT:
+            assert (tm, tn) in wsplit_tiles and p["tile"] == tm * tn // 64, (M, N, K, p)
+            tiles = -(-M // tm) * -(-N // tn)
+            assert s <= 8 and (s == 1 or (tiles * s <= 256 and 8 * s <= panels)), (M, N, K, p)
+        else:
+            assert path == nv.PATH_TILE and tm == tn == p["tile"] == 256, (M, N, K, p)
+            assert s in (1, 2), (M, N, K, p)
