@@ -188,3 +188,34 @@ def test_gemv_half_panels_per_lane(o, M, N, K):
     r = compare(g, bits, exact, mag, ops.alpha)
     say(f"  {r}")
     assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, r
+
+
+def test_library_plans_on_random_shapes(o):
+    """The library's own plan (table or rules) on 24 seeded random shapes,
+    ragged in M, N and K (K a multiple of 16), element by element against
+    the oracle: the rules reach the mid-size kernel's tiles, the skinny
+    kernel and the dot-product kernel at these sizes."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    seen = set()
+    for i in range(24):
+        if i % 3 < 2:
+            M = int(rng.choice([rng.integers(1, 5), rng.integers(5, 65), rng.integers(65, 521)]))
+            N = int(rng.integers(1, 521))
+        else:  # enough rows and columns for the larger tiles
+            M = int(rng.integers(200, 1100))
+            N = int(rng.integers(500, 2100))
+        K = 16 * int(rng.integers(1, 65))
+        p = nv.plan(M, N, K)
+        seen.add((p["path"], p["tile"]))
+        say(f"random shape {i}: {M}x{N}x{K} plan {nv.PATH_NAMES[p['path']]}/{p['tile']}/{p['split_k']}")
+        ops = synth.random_operands(5000 + i, M, N, K, alpha=0.625)
+        a = nv.to_device(ops.a_codes, ops.a_scales, DEV)
+        b = nv.to_device(ops.b_codes, ops.b_scales, DEV)
+        out = nv.gemm(a, b, ops.alpha)
+        torch.cuda.synchronize()
+        g = out.view(torch.int16).cpu().numpy().astype(np.uint16)
+        bits, exact, mag = o.gemm(ops.a_codes, ops.a_scales, ops.b_codes, ops.b_scales, ops.alpha)
+        r = compare(g, bits, exact, mag, ops.alpha)
+        say(f"  {r}")
+        assert r["over"] == 0 and r["bit_exact_frac"] >= 0.999, (M, N, K, p, r)
+    say(f"plans reached: {sorted(seen)}")
