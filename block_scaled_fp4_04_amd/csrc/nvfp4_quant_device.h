@@ -73,30 +73,21 @@ __device__ __forceinline__ E2m1Search e2m1_search(float s) {
                  "+v"(q.p6));
     return q;
 }
-// The code is the number of boundaries below A: each test is the borrow of
-// (bound - A) (both values below 2^31), added up through the carry chain:
-// two instructions per boundary.  One asm block per element, so that the
-// compiler keeps the chain as written.
+// The code is the number of boundaries below A (A and the boundaries are
+// fp32 bit patterns of non-negative values, so they order as integers, and
+// the boundaries increase -- but for a zero scale, whose codes are masked
+// off).  A three-level binary search finds it: A against the middle
+// boundary, then against the middle of the half that selects, then against
+// the one boundary left, the three bits summed (about 10 instructions per
+// element; counting all seven boundaries through a borrow chain took 14:
+// 16384 x 8192 bfloat16 rows 85 -> 80 us, fp32 rows 136 -> 134 us).
 __device__ __forceinline__ uint32_t e2m1_code(uint32_t A, const E2m1Search& q) {
-    uint32_t code, tmp;
-    asm("v_sub_co_u32_e32 %1, vcc, %2, %9\n\t"
-        "v_cndmask_b32_e64 %0, 0, 1, vcc\n\t"
-        "v_sub_co_u32_e32 %1, vcc, %3, %9\n\t"
-        "v_addc_co_u32_e32 %0, vcc, 0, %0, vcc\n\t"
-        "v_sub_co_u32_e32 %1, vcc, %4, %9\n\t"
-        "v_addc_co_u32_e32 %0, vcc, 0, %0, vcc\n\t"
-        "v_sub_co_u32_e32 %1, vcc, %5, %9\n\t"
-        "v_addc_co_u32_e32 %0, vcc, 0, %0, vcc\n\t"
-        "v_sub_co_u32_e32 %1, vcc, %6, %9\n\t"
-        "v_addc_co_u32_e32 %0, vcc, 0, %0, vcc\n\t"
-        "v_sub_co_u32_e32 %1, vcc, %7, %9\n\t"
-        "v_addc_co_u32_e32 %0, vcc, 0, %0, vcc\n\t"
-        "v_sub_co_u32_e32 %1, vcc, %8, %9\n\t"
-        "v_addc_co_u32_e32 %0, vcc, 0, %0, vcc"
-        : "=&v"(code), "=&v"(tmp)
-        : "v"(q.p0), "v"(q.p1m), "v"(q.p2), "v"(q.p3m), "v"(q.p4), "v"(q.p5m), "v"(q.p6), "v"(A)
-        : "vcc");
-    return code;
+    const bool s0 = A > q.p3m;
+    const uint32_t mid = s0 ? q.p5m : q.p1m;
+    const uint32_t lo = s0 ? q.p4 : q.p0, hi = s0 ? q.p6 : q.p2;
+    const bool s1 = A > mid;
+    const uint32_t last = s1 ? hi : lo;
+    return (s0 ? 4u : 0u) + (s1 ? 2u : 0u) + (A > last ? 1u : 0u);
 }
 
 // Code word (8 codes, element i in bits 4i+3:4i) of 8 values of one block
